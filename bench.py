@@ -1,0 +1,303 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark of the paged-KV hot path on one MI355X.
+
+A step is one pass of the whole path over one synthetic batch, with inputs
+already resident in HBM: copy-on-write block copies (prefix-shared workload
+only), the KV append of the step's new tokens, and paged decode attention
+(partition pass + merge).  Default workload: the Llama-3-8B-shaped GQA batch
+(256 sequences, 32 q / 8 KV heads, head_dim 128, bf16, 16-token blocks,
+lengths uniform in [1024, 8192] plus one appended token each).
+
+Prints ONE JSON line: seq-steps/s (value), KV-read GB/s and the fraction of
+the 8 TB/s HBM peak for the decode call (roofline), and the CPU oracle timed
+on the host cores over the same batch (cpu_baseline).
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "decode seq-steps/s + achieved KV-read GB/s (% of MI355X HBM peak), 1 GPU"
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "decode_gqa_llama3_8b_counters.json")
+KERNEL_SOURCES = ["paged_kv_cache_313_amd/csrc/pa_decode_kernels.hip",
+                  "paged_kv_cache_313_amd/csrc/pa_common.hpp"]
+
+WORKLOADS = {
+    1: "tiny MHA decode: 4 seqs, 8 heads, D64, fp32, bs16, lens {5,17,33,64}",
+    2: "OPT-13B-shaped MHA decode: 64 seqs, 40 heads, D128, fp16, bs16, lognormal lens (median 512, [16,2048])",
+    3: "Llama-3-8B-shaped GQA decode: 256 seqs, 32q/8kv heads, D128, bf16, bs16, lens U[1024,8192] + 1 appended token",
+    4: "prefix-shared sampling: 64 prompts x 8 samples, GQA 32/8, D128, bf16, bs16, 1032-token shared prompt, 448 CoW copies, 256-token suffix append, decode over 1288",
+    5: "long-context split decode: 16 seqs, GQA 32/8, D128, bf16, lens U[32768,131072], 512-token partitions",
+}
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=3, choices=sorted(WORKLOADS))
+    ap.add_argument("--block-size", type=int, default=16, help="block size of the long-context workload")
+    ap.add_argument("--partition", type=int, default=None, help="partition size (default: library choice)")
+    ap.add_argument("--table-layout", default="shuffled", choices=["shuffled", "identity"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=8.0, help="minimum wall time of the oracle timing")
+    return ap.parse_args()
+
+
+def make_batch(args):
+    from workloads import synth as W
+    kw = {}
+    if args.config in (2, 3, 5):
+        kw["table_layout"] = args.table_layout
+    if args.config == 5:
+        return W.config5(block_size=args.block_size, **kw)
+    return W.CONFIGS[args.config](**kw)
+
+
+# ----------------------------------------------------------------------------- CPU oracle leg
+_CPU_BATCH = None
+
+
+def _cpu_worker_init():
+    try:
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(1)
+    except Exception:
+        pass
+
+
+def _cpu_seq(s):
+    import numpy as np
+    import oracle.pa_oracle as O
+    b = _CPU_BATCH
+    G = b.num_q_heads // b.num_kv_heads
+    out = np.empty((b.num_q_heads, b.head_dim))
+    for g in range(b.num_kv_heads):
+        out[g * G:(g + 1) * G] = O.decode_group(b.query, b._k_after, b._v_after, b.block_tables,
+                                                b.context_lens, b.scale, b.block_size, b.dtype, s, g)
+    return s, out
+
+
+def cpu_baseline(b, min_seconds):
+    """The fp64 oracle, unchanged, over the whole batch: the step's CoW copies
+    and appends, then attention for every sequence, sequences dealt
+    longest-first to one worker process per host core (one BLAS thread each)."""
+    import multiprocessing as mp
+
+    import numpy as np
+    import oracle.pa_oracle as O
+    global _CPU_BATCH
+    cores = max(1, min(len(os.sched_getaffinity(0)), 16))
+    # pools after the step (oracle copies + appends); the timed loop redoes them
+    k, v = b.k_pool, b.v_pool
+    if b.block_mapping is not None and len(b.block_mapping):
+        k, v = k.copy(), v.copy()
+        O.block_copy(k, v, b.block_mapping)
+    if b.new_key is not None:
+        if k is b.k_pool:
+            k, v = k.copy(), v.copy()
+        O.kv_append(k, v, b.new_key, b.new_value, b.slot_mapping, b.block_size)
+    b._k_after, b._v_after = k, v
+    _CPU_BATCH = b
+    order = sorted(range(b.num_seqs), key=lambda s: -int(b.context_lens[s]))
+    ctx = mp.get_context("fork")
+    out = np.empty((b.num_seqs, b.num_q_heads, b.head_dim))
+    passes = 0
+    with ctx.Pool(cores, initializer=_cpu_worker_init) as pool:
+        t0 = time.perf_counter()
+        while True:
+            if b.new_key is not None:   # redo the step's appends in place (idempotent)
+                O.kv_append(k, v, b.new_key, b.new_value, b.slot_mapping, b.block_size)
+            for s, o in pool.imap_unordered(_cpu_seq, order, chunksize=1):
+                out[s] = o
+            passes += 1
+            el = time.perf_counter() - t0
+            if el >= min_seconds or passes >= 50:
+                break
+    value = b.num_seqs * passes / el
+    res = {"value": value, "unit": "seq-steps/s", "cores": cores, "kind": "oracle",
+           "sample": f"all {b.num_seqs} sequences of the workload (step's CoW copies + appends + fp64 attention), "
+                     f"{passes} passes in {el:.2f} s, {cores} worker processes x 1 BLAS thread",
+           "kv_gbps_equiv": b.kv_bytes() * passes / el / 1e9}
+    return res, out
+
+
+# ----------------------------------------------------------------------------- GPU leg
+def algorithmic_bytes(b, partition_size):
+    """Bytes the decode call must move: K/V of valid tokens, query, output,
+    block-table entries, lengths, and partial results of split sequences."""
+    import numpy as np
+    L = b.context_lens.astype(np.int64)
+    kv = b.kv_bytes()
+    qo = 2 * b.num_seqs * b.num_q_heads * b.head_dim * b.elt_bytes
+    tbl = int((-(-L // b.block_size)).sum()) * 4 + b.num_seqs * 4
+    part = 0
+    if partition_size and partition_size > 0:
+        nps = -(-L // partition_size)
+        nps = nps[nps > 1]
+        part = int(nps.sum()) * b.num_q_heads * (b.head_dim + 2) * 4 * 2
+    return kv + qo + tbl + part, kv
+
+
+def source_sha():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(config, partition):
+    try:
+        with open(COUNTERS_FILE) as f:
+            c = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if c.get("source_sha") != source_sha() or c.get("config") != config or c.get("partition") != partition:
+        return None
+    return c.get("hbm_bytes_per_launch")
+
+
+def main():
+    args = parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}): "
+              "the decode path has no multi-GPU leg in this build", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+
+    t_gen = time.perf_counter()
+    b = make_batch(args)
+    t_gen = time.perf_counter() - t_gen
+    print(f"[bench] workload {args.config} generated in {t_gen:.1f}s: {b.name}, S={b.num_seqs}, "
+          f"KV bytes {b.kv_bytes() / 1e9:.3f} GB", file=sys.stderr, flush=True)
+
+    cpu, cpu_out = None, None
+    if not args.no_cpu_baseline:
+        cpu, cpu_out = cpu_baseline(b, args.cpu_seconds)   # before any GPU call (forked workers)
+        print(f"[bench] cpu oracle: {cpu['value']:.1f} seq-steps/s on {cpu['cores']} cores",
+              file=sys.stderr, flush=True)
+
+    import torch
+
+    import oracle.pa_oracle as O
+    import paged_kv_cache_313_amd as P
+    from workloads import torch_io
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    d = torch_io.to_device(b, dev)
+    part = args.partition if args.partition is not None else P.choose_partition(
+        b.num_seqs, b.num_kv_heads, b.max_context_len, b.block_size)
+    need = P.decode_workspace_bytes(b.num_seqs, b.num_q_heads, b.head_dim, b.max_context_len, part)
+    ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    out = torch.empty_like(d.query)
+    stream = torch.cuda.current_stream(dev)
+    has_copy = b.block_mapping is not None and len(b.block_mapping) > 0
+    has_append = b.new_key is not None
+
+    ev = {"dec0": [], "dec1": [], "app0": [], "app1": [], "cp0": [], "cp1": []}
+
+    def step(record):
+        if has_copy:
+            if record:
+                e = torch.cuda.Event(enable_timing=True); e.record(stream); ev["cp0"].append(e)
+            P.block_copy(d.k_pool, d.v_pool, d.block_mapping, stream=stream)
+            if record:
+                e = torch.cuda.Event(enable_timing=True); e.record(stream); ev["cp1"].append(e)
+        if has_append:
+            if record:
+                e = torch.cuda.Event(enable_timing=True); e.record(stream); ev["app0"].append(e)
+            P.kv_append(d.new_key, d.new_value, d.k_pool, d.v_pool, d.slot_mapping, stream=stream)
+            if record:
+                e = torch.cuda.Event(enable_timing=True); e.record(stream); ev["app1"].append(e)
+        if record:
+            e = torch.cuda.Event(enable_timing=True); e.record(stream); ev["dec0"].append(e)
+        P.decode_attention(d.query, d.k_pool, d.v_pool, d.block_tables, d.context_lens, b.scale,
+                           b.max_context_len, part, out=out, workspace=ws, stream=stream)
+        if record:
+            e = torch.cuda.Event(enable_timing=True); e.record(stream); ev["dec1"].append(e)
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done ({args.warmup} steps), timing {args.steps} steps", file=sys.stderr, flush=True)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) / args.steps * 1e3
+
+    def mean_ms(a, z):
+        return float(np.mean([x.elapsed_time(y) for x, y in zip(ev[a], ev[z])])) if ev[a] else None
+
+    dec_ms = mean_ms("dec0", "dec1")
+    app_ms = mean_ms("app0", "app1")
+    cp_ms = mean_ms("cp0", "cp1")
+    alg_bytes, kv_bytes = algorithmic_bytes(b, part)
+    achieved = alg_bytes / (dec_ms * 1e-3) / 1e9
+
+    # parity of this run's output against the oracle run above (all sequences)
+    parity = None
+    if cpu_out is not None:
+        got = O.upcast(torch_io.torch_to_storage(out, b.dtype), b.dtype)
+        err = np.abs(got - cpu_out)
+        if b.dtype == "f32":
+            ok = bool(err.max() <= 1e-5)
+        else:
+            ok = bool((err <= 2e-2 + 1e-2 * np.abs(cpu_out)).all())
+        parity = {"max_abs_err": float(err.max()), "within_tolerance": ok,
+                  "checked": "all outputs vs the fp64 oracle"}
+
+    cfg = {"workload": WORKLOADS[args.config], "num_seqs": b.num_seqs, "num_q_heads": b.num_q_heads,
+           "num_kv_heads": b.num_kv_heads, "head_dim": b.head_dim, "block_size": b.block_size,
+           "num_blocks": b.num_blocks, "partition_size": part, "table_layout": args.table_layout,
+           "kv_bytes_per_step": kv_bytes, "tokens": int(b.context_lens.sum())}
+    line = {
+        "metric": METRIC,
+        "value": b.num_seqs / (ms_per_step * 1e-3),
+        "unit": "seq-steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": b.dtype,
+        "data": "synthetic (seeded N(0,1) q/K/V, shuffled physical blocks)",
+        "config": cfg,
+        "kv_read_gbps": kv_bytes / (dec_ms * 1e-3) / 1e9,
+        "pct_of_hbm_peak": 100.0 * achieved / HBM_PEAK_GBPS,
+        "decode_ms": dec_ms,
+        "append_ms": app_ms,
+        "block_copy_ms": cp_ms,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": traffic_from_profile(args.config, part),
+                     "kernel": "pa_decode_attention (decode_mfma_kernel + decode_merge_kernel)"
+                               if b.num_q_heads != b.num_kv_heads and b.dtype != "f32"
+                               else "pa_decode_attention (decode_valu_kernel + decode_merge_kernel)",
+                     "algorithmic_bytes_per_launch": alg_bytes},
+        "cpu_baseline": cpu,
+        "parity": parity,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,184 @@
+/*
+ * pa.h -- C ABI of libpagedkv: the data-parallel hot path of PagedAttention on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The KV cache of every sequence is cut into fixed-size blocks of
+ * `block_size` tokens that live anywhere in a shared physical pool; each
+ * sequence reaches its blocks through its own block table (vLLM/PagedAttention
+ * paged-KV analysis page, sections 2.2 and 2.3; vLLM entity page, "what it
+ * is").  Three operations run on the device:
+ *
+ *   pa_kv_append         write the newest tokens' K/V into their slots
+ *   pa_block_copy        copy-on-write duplication of shared blocks
+ *   pa_decode_attention  one query token per sequence attends over its paged
+ *                        context
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Pointers marked DEVICE are device (HBM) addresses; HOST means host memory.
+ *   The caller owns every buffer.  The library never allocates, frees or
+ *   synchronises; every call is enqueued on `stream` (a hipStream_t; NULL is
+ *   the null stream) and returns as soon as the launches are queued.  Inputs
+ *   must stay alive until the stream has passed the call.
+ * - Pools `k_pool` and `v_pool` are each laid out
+ *   [num_blocks][num_kv_heads][block_size][head_dim] (row-major, head_dim
+ *   fastest), so one (block, KV head) tile of block_size * head_dim elements is
+ *   contiguous.
+ * - Supported: dtype f32 / f16 / bf16 (the same for query, pools and output;
+ *   bf16 is the upper half of an IEEE float32), head_dim 64 or 128,
+ *   block_size 8, 16 or 32, num_q_heads a multiple of num_kv_heads with group
+ *   size Hq/Hkv in {1, 2, 4, 8, 16}.  Pool pointers and the key/value/query/out
+ *   pointers must be 16-byte aligned.
+ * - Argument checks are pure host checks made before any HIP call, so a
+ *   rejected call has no side effect.  A failed launch returns PA_ERR_HIP and
+ *   pa_last_hip_error() gives the hipError_t value.
+ * - Device-side contents are the caller's contract: table entries and slot
+ *   ids in range, slots unique within a call, CoW destinations distinct and
+ *   disjoint from all sources.  The kernels never access memory outside the
+ *   buffers described by the size arguments: out-of-range physical ids, slots
+ *   and lengths are clamped or skipped (results for such inputs are
+ *   unspecified, but memory stays safe).
+ * - All entry points are reentrant; the library holds no state other than the
+ *   thread-local last HIP error.
+ */
+#ifndef PAGEDKV_PA_H
+#define PAGEDKV_PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PA_OK = 0,
+  PA_ERR_NULL = 1,        /* a required pointer is NULL                        */
+  PA_ERR_SHAPE = 2,       /* a size is out of range or inconsistent            */
+  PA_ERR_BLOCK_SIZE = 3,  /* block_size not in {8, 16, 32}                     */
+  PA_ERR_DTYPE = 4,       /* dtype not one of pa_dtype                         */
+  PA_ERR_PARTITION = 5,   /* partition_size not 0 and not a multiple of 16 and of block_size */
+  PA_ERR_WORKSPACE = 6,   /* workspace missing or smaller than required        */
+  PA_ERR_HIP = 7,         /* a kernel launch failed; see pa_last_hip_error()   */
+  PA_ERR_ALIGN = 8        /* a data pointer is not 16-byte aligned             */
+} pa_status;
+
+typedef enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype;
+
+/*
+ * pa_kv_append -- paged KV append (slot-mapping scatter).
+ *
+ * Defined by the pages as the write of a newly generated token into the block
+ * that its sequence is filling (paged-KV analysis page, section 3.2, the
+ * copy-on-write paragraph; blocks are taken on demand, vLLM entity page,
+ * "what it is").  For every token i with slot = slot_mapping[i] >= 0:
+ *     b = slot / block_size, o = slot % block_size,
+ *     k_pool[b][h][o][:] = key[i][h][:]   and   v_pool[b][h][o][:] = value[i][h][:]
+ * for every KV head h.  Tokens with a negative slot are skipped, and so are
+ * slots >= num_blocks * block_size.  Byte copy: bits are preserved exactly.
+ *
+ *   key, value     DEVICE [num_tokens][num_kv_heads][head_dim] of dtype
+ *   k_pool, v_pool DEVICE pools (see above), written in place
+ *   slot_mapping   DEVICE int64 [num_tokens]
+ * num_tokens == 0 is a no-op returning PA_OK.
+ */
+pa_status pa_kv_append(const void* key, const void* value, void* k_pool, void* v_pool,
+                       const int64_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
+                       int32_t head_dim, int32_t block_size, int32_t num_blocks, pa_dtype dtype,
+                       void* stream);
+
+/*
+ * pa_decode_workspace_bytes -- size of the fp32 workspace that a split
+ * (partition_size > 0) decode needs: per (sequence, q head, partition) one
+ * running max, one running sum and head_dim partial outputs.  Returns 0 for
+ * partition_size == 0 and (size_t)-1 for invalid arguments.  HOST only.
+ */
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                 int32_t max_context_len, int32_t partition_size);
+
+/*
+ * pa_decode_choose_partition -- the partition size (0 = no split) that the
+ * library prefers for a decode batch of this shape on this GPU: enough
+ * independent work units to fill the 256 compute units without
+ * excessive partial-result traffic.  HOST only; never fails.
+ */
+int32_t pa_decode_choose_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len,
+                                   int32_t block_size);
+
+/*
+ * pa_decode_attention -- single-query decode attention over a paged KV cache.
+ *
+ * The pages give the operation per sequence: the query of every head reads the
+ * sequence's K/V block by block through its block table, the blocks being
+ * non-contiguous (paged-KV analysis page, section 3.1, simplified attention
+ * sketch).  The sketch is marked as simplified; the operation computed here is
+ * one softmax over the whole context, scaled, with the unfilled tail of the last
+ * block excluded:
+ *     for sequence s, q head h, KV head g = h / (num_q_heads / num_kv_heads),
+ *     L = context_lens[s], token t in [0, L) at block block_tables[s][t / bs],
+ *     slot t % bs:
+ *         s_t = scale * <query[s][h], k_t>,
+ *         out[s][h] = sum_t exp(s_t - max) v_t / sum_t exp(s_t - max).
+ * L == 0 gives a zero row.  Accumulation is fp32; the output is rounded once
+ * (round to nearest even) to dtype.
+ *
+ *   out            DEVICE [num_seqs][num_q_heads][head_dim] of dtype, written
+ *   query          DEVICE [num_seqs][num_q_heads][head_dim] of dtype
+ *   k_pool, v_pool DEVICE pools (see above), read only
+ *   block_tables   DEVICE int32 [num_seqs][max_blocks_per_seq]; entries past a
+ *                  sequence's last block are never read
+ *   context_lens   DEVICE int32 [num_seqs]; counts every token attended to,
+ *                  including one appended in the same step (append first)
+ *   max_context_len HOST upper bound of context_lens (sizes the grid);
+ *                  lengths above it, or above max_blocks_per_seq * block_size,
+ *                  are clamped
+ *   partition_size 0: one work unit per (sequence, KV head).  > 0: the context
+ *                  is cut into partitions of that many tokens (a multiple of 16
+ *                  and of block_size); each writes partial results to
+ *                  `workspace` and a second kernel merges them with the
+ *                  log-sum-exp rescale.  A sequence that fits one partition is
+ *                  written directly.
+ *   workspace      DEVICE, >= pa_decode_workspace_bytes(...) bytes when
+ *                  partition_size > 0 (may be NULL otherwise); scratch only,
+ *                  overwritten.
+ */
+pa_status pa_decode_attention(void* out, const void* query, const void* k_pool, const void* v_pool,
+                              const int32_t* block_tables, const int32_t* context_lens,
+                              int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                              int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                              int32_t num_blocks, int32_t max_context_len, float scale,
+                              int32_t partition_size, pa_dtype dtype, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
+/*
+ * pa_block_copy -- copy-on-write block duplication, all pairs in one launch.
+ *
+ * Shared blocks (parallel samples, beams, common prompts) are reference
+ * counted; a sequence about to write into a block that others still use gets
+ * a private copy first (vLLM entity page, "what it is"; paged-KV analysis
+ * page, sections 2.3 and 3.2).  For every pair p:
+ *     src = block_mapping[2p], dst = block_mapping[2p + 1],
+ *     k_pool[dst] = k_pool[src], v_pool[dst] = v_pool[src]   (all heads, all slots)
+ * Bits are preserved.  Pairs with an id outside [0, num_blocks) are skipped.
+ * Destinations must be distinct and must not be sources of the same call.
+ *
+ *   k_pool, v_pool DEVICE pools, written in place
+ *   block_mapping  DEVICE int32 [num_pairs][2]
+ * num_pairs == 0 is a no-op returning PA_OK.
+ */
+pa_status pa_block_copy(void* k_pool, void* v_pool, const int32_t* block_mapping, int32_t num_pairs,
+                        int32_t num_kv_heads, int32_t block_size, int32_t head_dim,
+                        int32_t num_blocks, pa_dtype dtype, void* stream);
+
+/* Static, human-readable name of a status code.  HOST only. */
+const char* pa_status_string(pa_status status);
+
+/* hipError_t (as int) of the last call on this thread that returned PA_ERR_HIP;
+ * 0 if none.  HOST only. */
+int pa_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_PA_H */

@@ -1,0 +1,179 @@
+// libpagedkv C ABI: host-side argument checks, launch geometry and status codes.
+// Every check happens before the first HIP call, so a rejected call has no
+// side effect and the checks work without a GPU.
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cstdint>
+
+#include "../../include/pa.h"
+#include "pa_common.hpp"
+#include "pa_launch.hpp"
+
+#define PA_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+bool dtype_ok(pa_dtype d) { return d == PA_F32 || d == PA_F16 || d == PA_BF16; }
+int elt_bytes(pa_dtype d) { return d == PA_F32 ? 4 : 2; }
+bool head_dim_ok(int32_t d) { return d == 64 || d == 128; }
+bool block_size_ok(int32_t b) { return b == 8 || b == 16 || b == 32; }
+bool group_ok(int32_t g) { return g == 1 || g == 2 || g == 4 || g == 8 || g == 16; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+pa::Elem elem_of(pa_dtype d) {
+  return d == PA_F32 ? pa::Elem::F32 : (d == PA_F16 ? pa::Elem::F16 : pa::Elem::BF16);
+}
+
+pa_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return PA_OK;
+  g_last_hip_error = (int)e;
+  return PA_ERR_HIP;
+}
+
+int64_t num_partitions(int32_t max_context_len, int32_t partition_size) {
+  if (partition_size <= 0 || max_context_len <= 0) return 1;
+  return ((int64_t)max_context_len + partition_size - 1) / partition_size;
+}
+
+}  // namespace
+
+PA_EXPORT const char* pa_status_string(pa_status s) {
+  switch (s) {
+    case PA_OK: return "PA_OK";
+    case PA_ERR_NULL: return "PA_ERR_NULL: a required pointer is NULL";
+    case PA_ERR_SHAPE: return "PA_ERR_SHAPE: a size is out of range or inconsistent";
+    case PA_ERR_BLOCK_SIZE: return "PA_ERR_BLOCK_SIZE: block_size must be 8, 16 or 32";
+    case PA_ERR_DTYPE: return "PA_ERR_DTYPE: dtype must be PA_F32, PA_F16 or PA_BF16";
+    case PA_ERR_PARTITION:
+      return "PA_ERR_PARTITION: partition_size must be 0 or a positive multiple of 16 and of block_size";
+    case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE: workspace missing or too small";
+    case PA_ERR_HIP: return "PA_ERR_HIP: a HIP launch failed (see pa_last_hip_error)";
+    case PA_ERR_ALIGN: return "PA_ERR_ALIGN: data pointers must be 16-byte aligned";
+  }
+  return "unknown pa_status";
+}
+
+PA_EXPORT int pa_last_hip_error(void) { return g_last_hip_error; }
+
+PA_EXPORT pa_status pa_kv_append(const void* key, const void* value, void* k_pool, void* v_pool,
+                                 const int64_t* slot_mapping, int32_t num_tokens,
+                                 int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                 int32_t num_blocks, pa_dtype dtype, void* stream) {
+  if (!dtype_ok(dtype)) return PA_ERR_DTYPE;
+  if (!block_size_ok(block_size)) return PA_ERR_BLOCK_SIZE;
+  if (num_tokens < 0 || num_kv_heads < 1 || !head_dim_ok(head_dim) || num_blocks < 1)
+    return PA_ERR_SHAPE;
+  if (num_tokens == 0) return PA_OK;
+  if (!key || !value || !k_pool || !v_pool || !slot_mapping) return PA_ERR_NULL;
+  if (!aligned16(key) || !aligned16(value) || !aligned16(k_pool) || !aligned16(v_pool))
+    return PA_ERR_ALIGN;
+  return hip_status(pa::launch_kv_append(key, value, k_pool, v_pool, slot_mapping, num_tokens,
+                                         num_kv_heads, head_dim * elt_bytes(dtype), block_size,
+                                         num_blocks, reinterpret_cast<hipStream_t>(stream)));
+}
+
+PA_EXPORT pa_status pa_block_copy(void* k_pool, void* v_pool, const int32_t* block_mapping,
+                                  int32_t num_pairs, int32_t num_kv_heads, int32_t block_size,
+                                  int32_t head_dim, int32_t num_blocks, pa_dtype dtype,
+                                  void* stream) {
+  if (!dtype_ok(dtype)) return PA_ERR_DTYPE;
+  if (!block_size_ok(block_size)) return PA_ERR_BLOCK_SIZE;
+  if (num_pairs < 0 || num_kv_heads < 1 || !head_dim_ok(head_dim) || num_blocks < 1)
+    return PA_ERR_SHAPE;
+  if (num_pairs == 0) return PA_OK;
+  if (num_pairs > INT32_MAX / 2) return PA_ERR_SHAPE;
+  if (!k_pool || !v_pool || !block_mapping) return PA_ERR_NULL;
+  if (!aligned16(k_pool) || !aligned16(v_pool)) return PA_ERR_ALIGN;
+  const int64_t block_bytes = (int64_t)num_kv_heads * block_size * head_dim * elt_bytes(dtype);
+  if (block_bytes / 16 > INT32_MAX) return PA_ERR_SHAPE;
+  return hip_status(pa::launch_block_copy(k_pool, v_pool, block_mapping, num_pairs, block_bytes,
+                                          num_blocks, reinterpret_cast<hipStream_t>(stream)));
+}
+
+PA_EXPORT size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                           int32_t max_context_len, int32_t partition_size) {
+  if (num_seqs < 0 || num_q_heads < 1 || head_dim < 1 || max_context_len < 0 || partition_size < 0)
+    return (size_t)-1;
+  const int64_t np = num_partitions(max_context_len, partition_size);
+  if (partition_size == 0 || np <= 1) return 0;
+  return (size_t)num_seqs * (size_t)num_q_heads * (size_t)np * ((size_t)head_dim + 2) * sizeof(float);
+}
+
+PA_EXPORT int32_t pa_decode_choose_partition(int32_t num_seqs, int32_t num_kv_heads,
+                                             int32_t max_context_len, int32_t block_size) {
+  (void)num_seqs;
+  (void)num_kv_heads;
+  (void)block_size;
+  // 512 tokens (a multiple of every supported block size and of the 16-token
+  // tile): long sequences split into many similar-sized units, which evens out
+  // ragged batches across the 256 CUs; short batches are not split at all.
+  return max_context_len > 512 ? 512 : 0;
+}
+
+PA_EXPORT pa_status pa_decode_attention(void* out, const void* query, const void* k_pool,
+                                        const void* v_pool, const int32_t* block_tables,
+                                        const int32_t* context_lens, int32_t num_seqs,
+                                        int32_t num_q_heads, int32_t num_kv_heads,
+                                        int32_t head_dim, int32_t block_size,
+                                        int32_t max_blocks_per_seq, int32_t num_blocks,
+                                        int32_t max_context_len, float scale,
+                                        int32_t partition_size, pa_dtype dtype, void* workspace,
+                                        size_t workspace_bytes, void* stream) {
+  if (!dtype_ok(dtype)) return PA_ERR_DTYPE;
+  if (!block_size_ok(block_size)) return PA_ERR_BLOCK_SIZE;
+  if (num_seqs < 0 || num_q_heads < 1 || num_kv_heads < 1 || !head_dim_ok(head_dim) ||
+      max_blocks_per_seq < 1 || num_blocks < 1 || max_context_len < 0)
+    return PA_ERR_SHAPE;
+  if (num_q_heads % num_kv_heads != 0 || !group_ok(num_q_heads / num_kv_heads)) return PA_ERR_SHAPE;
+  if (partition_size < 0 || (partition_size > 0 && (partition_size % 16 != 0 ||
+                                                     partition_size % block_size != 0)))
+    return PA_ERR_PARTITION;
+  if (num_seqs == 0) return PA_OK;
+  if (!out || !query || !k_pool || !v_pool || !block_tables || !context_lens) return PA_ERR_NULL;
+  if (!aligned16(out) || !aligned16(query) || !aligned16(k_pool) || !aligned16(v_pool))
+    return PA_ERR_ALIGN;
+
+  const int32_t group = num_q_heads / num_kv_heads;
+  const int64_t np = num_partitions(max_context_len, partition_size);
+  const bool split = np > 1;
+  const bool mfma = dtype != PA_F32 && group >= 2;
+  const int32_t heads_per_unit = mfma ? group : (group < 4 ? group : 4);
+  const int64_t chunks = mfma ? num_kv_heads : num_q_heads / heads_per_unit;
+  const int64_t units = (int64_t)num_seqs * chunks * np;
+  if (units > INT32_MAX) return PA_ERR_SHAPE;
+
+  pa::DecodeArgs a{};
+  a.out = out;
+  a.query = query;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_blocks = num_blocks;
+  a.max_context_len = max_context_len;
+  a.partition_size = split ? partition_size : (max_context_len > 16 ? max_context_len : 16);
+  a.num_parts = (int32_t)np;
+  a.split = split ? 1 : 0;
+  a.head_chunks = (int32_t)chunks;
+  a.scale_log2 = scale * pa::kLog2e;
+  if (split) {
+    const size_t need = pa_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_len,
+                                                  partition_size);
+    if (!workspace || workspace_bytes < need) return PA_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 3u) != 0) return PA_ERR_ALIGN;
+    const size_t rows = (size_t)num_seqs * num_q_heads * (size_t)np;
+    float* ws = static_cast<float*>(workspace);
+    a.ws_m = ws;
+    a.ws_l = ws + rows;
+    a.ws_o = ws + 2 * rows;
+  }
+  return hip_status(pa::launch_decode(a, elem_of(dtype), head_dim, block_size, group,
+                                      reinterpret_cast<hipStream_t>(stream)));
+}

@@ -1,0 +1,147 @@
+// Device-side helpers shared by the libpagedkv kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+constexpr int kWave = 64;
+constexpr int kNumXcd = 8;          // MI355X: 8 XCDs of 32 CUs, workgroups dealt round-robin
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kNegInf = -__builtin_inff();
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// storage tags: the element type as stored in HBM
+struct F32 { using elem = float;    static constexpr int bytes = 4; };
+struct F16 { using elem = uint16_t; static constexpr int bytes = 2; };
+struct BF16 { using elem = uint16_t; static constexpr int bytes = 2; };
+
+__device__ __forceinline__ u32x4 ld16(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+__device__ __forceinline__ void st16(void* p, u32x4 v) {
+  *reinterpret_cast<u32x4*>(p) = v;
+}
+
+// ---- unpack 16 loaded bytes to fp32 (exact) --------------------------------
+template <class T> struct Unpack;
+template <> struct Unpack<F32> {
+  static constexpr int n = 4;
+  __device__ __forceinline__ static void run(u32x4 v, float* o) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = __uint_as_float(v[i]);
+  }
+};
+template <> struct Unpack<BF16> {
+  static constexpr int n = 8;
+  __device__ __forceinline__ static void run(u32x4 v, float* o) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      o[2 * i] = __uint_as_float(v[i] << 16);
+      o[2 * i + 1] = __uint_as_float(v[i] & 0xffff0000u);
+    }
+  }
+};
+template <> struct Unpack<F16> {
+  static constexpr int n = 8;
+  __device__ __forceinline__ static void run(u32x4 v, float* o) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f16x2 h = __builtin_bit_cast(f16x2, v[i]);
+      o[2 * i] = (float)h[0];
+      o[2 * i + 1] = (float)h[1];
+    }
+  }
+};
+
+// ---- fp32 -> storage, round to nearest even --------------------------------
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;  // NaN stays NaN
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+__device__ __forceinline__ uint16_t f32_to_f16_rne(float f) {
+  _Float16 h = (_Float16)f;  // v_cvt_f16_f32 rounds to nearest even
+  return __builtin_bit_cast(uint16_t, h);
+}
+template <class T> __device__ __forceinline__ void store_elem(void* base, size_t idx, float v);
+template <> __device__ __forceinline__ void store_elem<F32>(void* base, size_t idx, float v) {
+  reinterpret_cast<float*>(base)[idx] = v;
+}
+template <> __device__ __forceinline__ void store_elem<BF16>(void* base, size_t idx, float v) {
+  reinterpret_cast<uint16_t*>(base)[idx] = f32_to_bf16_rne(v);
+}
+template <> __device__ __forceinline__ void store_elem<F16>(void* base, size_t idx, float v) {
+  reinterpret_cast<uint16_t*>(base)[idx] = f32_to_f16_rne(v);
+}
+
+// ---- cross-lane moves -------------------------------------------------------
+// butterfly exchange with lane ^ mask (ds_swizzle / bpermute through the LDS crossbar
+// for masks >= 16, DPP for the in-row masks)
+template <int MASK>
+__device__ __forceinline__ float xor_lane(float x) {
+  if constexpr (MASK == 1) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xf, 0xf, false));  // quad_perm [1,0,3,2]
+  } else if constexpr (MASK == 2) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xf, 0xf, false));  // quad_perm [2,3,0,1]
+  } else {
+    return __shfl_xor(x, MASK, kWave);
+  }
+}
+
+// broadcast lane `src` of each quad (DPP quad_perm) -- src in 0..3
+template <int SRC>
+__device__ __forceinline__ float quad_bcast(float x) {
+  constexpr int ctrl = SRC * 0x55;
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), ctrl, 0xf, 0xf, false));
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ---- work-unit mapping -----------------------------------------------------
+// Workgroup b runs on XCD b % 8.  Give each XCD a contiguous range of logical
+// units so neighbouring units (e.g. samples sharing a prompt's blocks) meet in
+// the same L2.  Bijective on [0, n).
+__device__ __forceinline__ uint32_t xcd_unit(uint32_t b, uint32_t n) {
+  const uint32_t q = n / kNumXcd, r = n % kNumXcd;
+  const uint32_t x = b % kNumXcd, k = b / kNumXcd;
+  return x * q + (x < r ? x : r) + k;
+}
+
+// Arguments of the decode kernels (by value, in the kernarg segment).
+struct DecodeArgs {
+  void* out;                  // [S, Hq, D] dtype
+  const void* query;          // [S, Hq, D] dtype
+  const void* k_pool;         // [NB, Hkv, BS, D]
+  const void* v_pool;
+  const int32_t* block_tables;  // [S, MB]
+  const int32_t* context_lens;  // [S]
+  float* ws_m;                // [S, Hq, NP] running max (log2 domain)
+  float* ws_l;                // [S, Hq, NP] running sum
+  float* ws_o;                // [S, Hq, NP, D] un-normalised partial outputs
+  int32_t num_seqs, num_q_heads, num_kv_heads;
+  int32_t max_blocks_per_seq, num_blocks, max_context_len;
+  int32_t partition_size;     // tokens per unit (>= max_context_len when not split)
+  int32_t num_parts;          // partitions in the grid (1 when not split)
+  int32_t split;              // 1 when partial results go through the workspace
+  int32_t head_chunks;        // q-head chunks per sequence (VALU path)
+  float scale_log2;           // scale * log2(e)
+};
+
+__device__ __forceinline__ int clamp_len(const DecodeArgs& a, int s, int block_size) {
+  int L = a.context_lens[s];
+  const int cap_tbl = a.max_blocks_per_seq * block_size;
+  L = L < 0 ? 0 : L;
+  L = L > cap_tbl ? cap_tbl : L;
+  L = L > a.max_context_len ? a.max_context_len : L;
+  return L;
+}
+
+}  // namespace pa

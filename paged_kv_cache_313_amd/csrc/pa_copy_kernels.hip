@@ -1,0 +1,98 @@
+// Paged KV append (slot-mapping scatter) and copy-on-write block copy.
+//
+// Both are byte copies in 16-byte vectors; bits are preserved exactly.
+//  - append: the newest token of a sequence is written into the slot of the
+//    block its sequence is filling (vLLM/PagedAttention paged-KV analysis page,
+//    section 3.2; vLLM entity page, "what it is": blocks are taken on demand).
+//  - block copy: a block shared by several sequences is duplicated before one
+//    of them writes into it (same page, sections 2.3 and 3.2).  All pairs go in
+//    one launch: many small per-block copies are what makes KV movement slow
+//    (vLLM entity page, key observations).
+#include "pa_common.hpp"
+#include "pa_launch.hpp"
+
+namespace pa {
+
+// One thread moves one 16-byte chunk of one (token, head) row of K and of V.
+// grid-stride over num_tokens * num_kv_heads * chunks_per_row.
+__global__ __launch_bounds__(256) void kv_append_kernel(
+    const u32x4* __restrict__ key, const u32x4* __restrict__ value, u32x4* __restrict__ k_pool,
+    u32x4* __restrict__ v_pool, const int64_t* __restrict__ slot_mapping, int64_t total_chunks,
+    int32_t num_kv_heads, int32_t chunks_per_row, int32_t block_size, int64_t num_slots) {
+  const int64_t per_token = (int64_t)num_kv_heads * chunks_per_row;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total_chunks;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t t = i / per_token;
+    const int32_t r = (int32_t)(i - t * per_token);
+    const int64_t slot = slot_mapping[t];
+    if (slot < 0 || slot >= num_slots) continue;
+    const int32_t h = r / chunks_per_row;
+    const int32_t c = r - h * chunks_per_row;
+    const int64_t b = slot / block_size;
+    const int32_t o = (int32_t)(slot - b * block_size);
+    const int64_t dst = ((b * num_kv_heads + h) * block_size + o) * chunks_per_row + c;
+    const u32x4 kv = key[i];
+    const u32x4 vv = value[i];
+    k_pool[dst] = kv;
+    v_pool[dst] = vv;
+  }
+}
+
+// One workgroup per (pair, K-or-V); each thread moves kChunksPerThread 16-byte
+// chunks per iteration, loads first then stores, to keep several in flight.
+constexpr int kCopyThreads = 256;
+constexpr int kChunksPerThread = 4;
+
+__global__ __launch_bounds__(kCopyThreads) void block_copy_kernel(
+    u32x4* __restrict__ k_pool, u32x4* __restrict__ v_pool, const int32_t* __restrict__ block_mapping,
+    int32_t chunks_per_block, int32_t num_blocks) {
+  const int32_t pair = blockIdx.x >> 1;
+  u32x4* pool = (blockIdx.x & 1) ? v_pool : k_pool;
+  const int32_t src = block_mapping[2 * pair];
+  const int32_t dst = block_mapping[2 * pair + 1];
+  if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return;
+  const u32x4* s = pool + (int64_t)src * chunks_per_block;
+  u32x4* d = pool + (int64_t)dst * chunks_per_block;
+  constexpr int step = kCopyThreads * kChunksPerThread;
+  for (int32_t base = 0; base < chunks_per_block; base += step) {
+    u32x4 tmp[kChunksPerThread];
+#pragma unroll
+    for (int j = 0; j < kChunksPerThread; ++j) {
+      const int32_t c = base + j * kCopyThreads + threadIdx.x;
+      if (c < chunks_per_block) tmp[j] = s[c];
+    }
+#pragma unroll
+    for (int j = 0; j < kChunksPerThread; ++j) {
+      const int32_t c = base + j * kCopyThreads + threadIdx.x;
+      if (c < chunks_per_block) d[c] = tmp[j];
+    }
+  }
+}
+
+hipError_t launch_kv_append(const void* key, const void* value, void* k_pool, void* v_pool,
+                            const int64_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
+                            int32_t row_bytes, int32_t block_size, int32_t num_blocks,
+                            hipStream_t stream) {
+  const int32_t chunks_per_row = row_bytes / 16;
+  const int64_t total = (int64_t)num_tokens * num_kv_heads * chunks_per_row;
+  const int64_t want = (total + 255) / 256;
+  const int32_t grid = (int32_t)(want < 65536 ? want : 65536);
+  hipLaunchKernelGGL(kv_append_kernel, dim3(grid), dim3(256), 0, stream,
+                     reinterpret_cast<const u32x4*>(key), reinterpret_cast<const u32x4*>(value),
+                     reinterpret_cast<u32x4*>(k_pool), reinterpret_cast<u32x4*>(v_pool), slot_mapping,
+                     total, num_kv_heads, chunks_per_row, block_size,
+                     (int64_t)num_blocks * block_size);
+  return hipGetLastError();
+}
+
+hipError_t launch_block_copy(void* k_pool, void* v_pool, const int32_t* block_mapping,
+                             int32_t num_pairs, int64_t block_bytes, int32_t num_blocks,
+                             hipStream_t stream) {
+  const int32_t chunks = (int32_t)(block_bytes / 16);
+  hipLaunchKernelGGL(block_copy_kernel, dim3(2 * num_pairs), dim3(kCopyThreads), 0, stream,
+                     reinterpret_cast<u32x4*>(k_pool), reinterpret_cast<u32x4*>(v_pool),
+                     block_mapping, chunks, num_blocks);
+  return hipGetLastError();
+}
+
+}  // namespace pa
