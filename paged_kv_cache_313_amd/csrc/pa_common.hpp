@@ -15,7 +15,6 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 // storage tags: the element type as stored in HBM
 struct F32 { using elem = float;    static constexpr int bytes = 4; };
@@ -51,11 +50,13 @@ template <> struct Unpack<BF16> {
 template <> struct Unpack<F16> {
   static constexpr int n = 8;
   __device__ __forceinline__ static void run(u32x4 v, float* o) {
+    // element by element from a scalar copy: clang mis-lowers a bit_cast
+    // whose operand is an element of an ext_vector (it reads element 0)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      f16x2 h = __builtin_bit_cast(f16x2, v[i]);
-      o[2 * i] = (float)h[0];
-      o[2 * i + 1] = (float)h[1];
+      const uint32_t x = v[i];
+      o[2 * i] = (float)__builtin_bit_cast(_Float16, (uint16_t)(x & 0xffffu));
+      o[2 * i + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(x >> 16));
     }
   }
 };
