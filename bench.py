@@ -52,7 +52,21 @@ def parse_args():
     ap.add_argument("--table-layout", default="shuffled", choices=["shuffled", "identity"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=8.0, help="minimum wall time of the oracle timing")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="only run a plain device-to-device copy of this many MiB (5 times), the "
+                         "reference kernel for scaling HBM byte counters, and exit")
     return ap.parse_args()
+
+
+def calibrate_copy(mib):
+    import torch
+    n = mib << 20
+    x = torch.ones(n, dtype=torch.uint8, device="cuda")
+    y = torch.empty_like(x)
+    for _ in range(5):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration_copy_bytes": n, "launches": 5}), flush=True)
 
 
 def make_batch(args):
@@ -134,20 +148,25 @@ def cpu_baseline(b, min_seconds):
 
 
 # ----------------------------------------------------------------------------- GPU leg
-def algorithmic_bytes(b, partition_size):
-    """Bytes the decode call must move: K/V of valid tokens, query, output,
-    block-table entries, lengths, and partial results of split sequences."""
+def algorithmic_bytes(b):
+    """Bytes the decode call must move: K/V of the valid tokens, query, output,
+    block-table entries and lengths.  Partial results of a split are the
+    implementation's overhead and are not counted."""
     import numpy as np
     L = b.context_lens.astype(np.int64)
     kv = b.kv_bytes()
     qo = 2 * b.num_seqs * b.num_q_heads * b.head_dim * b.elt_bytes
     tbl = int((-(-L // b.block_size)).sum()) * 4 + b.num_seqs * 4
-    part = 0
-    if partition_size and partition_size > 0:
-        nps = -(-L // partition_size)
-        nps = nps[nps > 1]
-        part = int(nps.sum()) * b.num_q_heads * (b.head_dim + 2) * 4 * 2
-    return kv + qo + tbl + part, kv
+    return kv + qo + tbl, kv
+
+
+def decode_kernel_name(b, part):
+    core = "MfmaCore" if b.num_q_heads != b.num_kv_heads and b.dtype != "f32" else "ValuCore"
+    if part == -1:
+        return f"pa_decode_attention: decode_balanced_kernel<{core}> + decode_merge_balanced_kernel"
+    if part and part > 0:
+        return f"pa_decode_attention: decode_unit_kernel<{core}> + decode_merge_parts_kernel"
+    return f"pa_decode_attention: decode_unit_kernel<{core}>"
 
 
 def source_sha():
@@ -176,6 +195,9 @@ def main():
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}): "
               "the decode path has no multi-GPU leg in this build", file=sys.stderr)
         sys.exit(2)
+    if args.calibrate_copy_mib:
+        calibrate_copy(args.calibrate_copy_mib)
+        return
 
     import numpy as np
 
@@ -202,7 +224,8 @@ def main():
     d = torch_io.to_device(b, dev)
     part = args.partition if args.partition is not None else P.choose_partition(
         b.num_seqs, b.num_kv_heads, b.max_context_len, b.block_size)
-    need = P.decode_workspace_bytes(b.num_seqs, b.num_q_heads, b.head_dim, b.max_context_len, part)
+    need = P.decode_workspace_bytes(b.num_seqs, b.num_q_heads, b.num_kv_heads, b.head_dim,
+                                    b.max_context_len, part)
     ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
     out = torch.empty_like(d.query)
     stream = torch.cuda.current_stream(dev)
@@ -248,7 +271,7 @@ def main():
     dec_ms = mean_ms("dec0", "dec1")
     app_ms = mean_ms("app0", "app1")
     cp_ms = mean_ms("cp0", "cp1")
-    alg_bytes, kv_bytes = algorithmic_bytes(b, part)
+    alg_bytes, kv_bytes = algorithmic_bytes(b)
     achieved = alg_bytes / (dec_ms * 1e-3) / 1e9
 
     # parity of this run's output against the oracle run above (all sequences)
@@ -289,9 +312,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": traffic_from_profile(args.config, part),
-                     "kernel": "pa_decode_attention (decode_mfma_kernel + decode_merge_kernel)"
-                               if b.num_q_heads != b.num_kv_heads and b.dtype != "f32"
-                               else "pa_decode_attention (decode_valu_kernel + decode_merge_kernel)",
+                     "kernel": decode_kernel_name(b, part),
                      "algorithmic_bytes_per_launch": alg_bytes},
         "cpu_baseline": cpu,
         "parity": parity,

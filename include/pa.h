@@ -57,13 +57,16 @@ typedef enum {
   PA_ERR_SHAPE = 2,       /* a size is out of range or inconsistent            */
   PA_ERR_BLOCK_SIZE = 3,  /* block_size not in {8, 16, 32}                     */
   PA_ERR_DTYPE = 4,       /* dtype not one of pa_dtype                         */
-  PA_ERR_PARTITION = 5,   /* partition_size not 0 and not a multiple of 16 and of block_size */
+  PA_ERR_PARTITION = 5,   /* partition_size invalid (see pa_decode_attention)       */
   PA_ERR_WORKSPACE = 6,   /* workspace missing or smaller than required        */
   PA_ERR_HIP = 7,         /* a kernel launch failed; see pa_last_hip_error()   */
   PA_ERR_ALIGN = 8        /* a data pointer is not 16-byte aligned             */
 } pa_status;
 
 typedef enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype;
+
+/* partition_size value selecting the balanced split of pa_decode_attention */
+#define PA_PARTITION_BALANCED (-1)
 
 /*
  * pa_kv_append -- paged KV append (slot-mapping scatter).
@@ -88,19 +91,20 @@ pa_status pa_kv_append(const void* key, const void* value, void* k_pool, void* v
                        void* stream);
 
 /*
- * pa_decode_workspace_bytes -- size of the fp32 workspace that a split
- * (partition_size > 0) decode needs: per (sequence, q head, partition) one
- * running max, one running sum and head_dim partial outputs.  Returns 0 for
- * partition_size == 0 and (size_t)-1 for invalid arguments.  HOST only.
+ * pa_decode_workspace_bytes -- size of the workspace that pa_decode_attention
+ * needs for this shape and partition_size (see there); 0 when none is needed
+ * (no split, or a single partition), (size_t)-1 for invalid arguments.  The
+ * balanced split's size depends only on num_seqs, the group size Hq/Hkv and
+ * head_dim.  HOST only; makes no HIP call.
  */
-size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
-                                 int32_t max_context_len, int32_t partition_size);
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t max_context_len, int32_t partition_size);
 
 /*
- * pa_decode_choose_partition -- the partition size (0 = no split) that the
- * library prefers for a decode batch of this shape on this GPU: enough
- * independent work units to fill the 256 compute units without
- * excessive partial-result traffic.  HOST only; never fails.
+ * pa_decode_choose_partition -- the partition_size the library prefers for a
+ * batch of this shape: PA_PARTITION_BALANCED for most batches, 0 (no split)
+ * for tiny contexts or more sequences than a balanced launch takes.  HOST
+ * only; never fails.
  */
 int32_t pa_decode_choose_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len,
                                    int32_t block_size);
@@ -132,15 +136,22 @@ int32_t pa_decode_choose_partition(int32_t num_seqs, int32_t num_kv_heads, int32
  *   max_context_len HOST upper bound of context_lens (sizes the grid);
  *                  lengths above it, or above max_blocks_per_seq * block_size,
  *                  are clamped
- *   partition_size 0: one work unit per (sequence, KV head).  > 0: the context
- *                  is cut into partitions of that many tokens (a multiple of 16
- *                  and of block_size); each writes partial results to
- *                  `workspace` and a second kernel merges them with the
- *                  log-sum-exp rescale.  A sequence that fits one partition is
- *                  written directly.
- *   workspace      DEVICE, >= pa_decode_workspace_bytes(...) bytes when
- *                  partition_size > 0 (may be NULL otherwise); scratch only,
- *                  overwritten.
+ *   partition_size how the context is cut into work units:
+ *                  0: one unit per (sequence, head group), no workspace;
+ *                  P > 0 (a multiple of 16 and of block_size): units of P
+ *                  tokens; each writes partial results (running max, running
+ *                  sum, un-normalised output) to `workspace` and a second
+ *                  kernel merges them with the log-sum-exp rescale (a
+ *                  sequence that fits one partition is written directly);
+ *                  PA_PARTITION_BALANCED: the grid holds the workgroups the
+ *                  GPU keeps resident and each takes an equal share of all
+ *                  tiles of the batch, so ragged batches finish together;
+ *                  pieces of a (sequence, head group) that several units
+ *                  share are merged the same way (num_seqs <= 4096).
+ *   workspace      DEVICE, 16-byte aligned, >= pa_decode_workspace_bytes(...)
+ *                  bytes when that is non-zero (may be NULL otherwise);
+ *                  scratch only, overwritten.  Calls that share a workspace
+ *                  must be ordered on one stream.
  */
 pa_status pa_decode_attention(void* out, const void* query, const void* k_pool, const void* v_pool,
                               const int32_t* block_tables, const int32_t* context_lens,

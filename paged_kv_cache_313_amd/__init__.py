@@ -14,10 +14,10 @@ from typing import Optional
 import torch
 
 from . import _lib
-from ._lib import PagedKVError, load  # noqa: F401
+from ._lib import PA_PARTITION_BALANCED, PagedKVError, load  # noqa: F401
 
 __all__ = ["kv_append", "block_copy", "decode_attention", "decode_workspace_bytes",
-           "choose_partition", "PagedKVError", "load"]
+           "choose_partition", "PagedKVError", "load", "PA_PARTITION_BALANCED"]
 
 _DTYPES = {torch.float32: _lib.PA_F32, torch.float16: _lib.PA_F16, torch.bfloat16: _lib.PA_BF16}
 
@@ -85,10 +85,10 @@ def block_copy(k_pool: torch.Tensor, v_pool: torch.Tensor, block_mapping: torch.
     _lib.check("pa_block_copy", st)
 
 
-def decode_workspace_bytes(num_seqs: int, num_q_heads: int, head_dim: int, max_context_len: int,
-                           partition_size: int) -> int:
-    n = load().pa_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_len,
-                                         partition_size)
+def decode_workspace_bytes(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                           max_context_len: int, partition_size: int) -> int:
+    n = load().pa_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                         max_context_len, partition_size)
     if n == (1 << 64) - 1:
         raise ValueError("invalid arguments to pa_decode_workspace_bytes")
     return int(n)
@@ -107,7 +107,9 @@ def decode_attention(query: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Te
 
     query [S, Hq, D]; pools [NB, Hkv, bs, D]; block_tables int32 [S, MB];
     context_lens int32 [S]; ``max_context_len`` is a host-side upper bound of
-    ``context_lens``.  ``partition_size`` None lets the library choose.
+    ``context_lens``.  ``partition_size``: 0 = no split, P > 0 = fixed
+    P-token partitions, PA_PARTITION_BALANCED = balanced split, None = the
+    library's choice.
     Returns ``out`` [S, Hq, D] in the query's dtype.
     """
     lib = load()
@@ -125,7 +127,7 @@ def decode_attention(query: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Te
         partition_size = choose_partition(S, Hkv, max_context_len, bs)
     if out is None:
         out = torch.empty_like(query)
-    need = decode_workspace_bytes(S, Hq, D, max_context_len, partition_size)
+    need = decode_workspace_bytes(S, Hq, Hkv, D, max_context_len, partition_size)
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=query.device)
     ws_ptr = _dev(workspace, "workspace") if workspace is not None else None

@@ -10,6 +10,7 @@ LIB_PATH = os.path.join(HERE, "libpagedkv.so")
 
 PA_OK = 0
 PA_F32, PA_F16, PA_BF16 = 0, 1, 2
+PA_PARTITION_BALANCED = -1
 STATUS_NAMES = {0: "PA_OK", 1: "PA_ERR_NULL", 2: "PA_ERR_SHAPE", 3: "PA_ERR_BLOCK_SIZE",
                 4: "PA_ERR_DTYPE", 5: "PA_ERR_PARTITION", 6: "PA_ERR_WORKSPACE", 7: "PA_ERR_HIP",
                 8: "PA_ERR_ALIGN"}
@@ -21,7 +22,7 @@ _c_i32, _c_i64, _c_size, _c_f32, _vp = (ctypes.c_int32, ctypes.c_int64, ctypes.c
 SIGNATURES = {
     "pa_kv_append": (_c_i32, [_vp, _vp, _vp, _vp, _vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
                               _c_i32, _vp]),
-    "pa_decode_workspace_bytes": (_c_size, [_c_i32, _c_i32, _c_i32, _c_i32, _c_i32]),
+    "pa_decode_workspace_bytes": (_c_size, [_c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32]),
     "pa_decode_choose_partition": (_c_i32, [_c_i32, _c_i32, _c_i32, _c_i32]),
     "pa_decode_attention": (_c_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _c_i32, _c_i32, _c_i32, _c_i32,
                                      _c_i32, _c_i32, _c_i32, _c_i32, _c_f32, _c_i32, _c_i32, _vp,

@@ -5,6 +5,9 @@
 
 #include <climits>
 #include <cstdint>
+#include <map>
+#include <mutex>
+#include <utility>
 
 #include "../../include/pa.h"
 #include "pa_common.hpp"
@@ -38,7 +41,44 @@ int64_t num_partitions(int32_t max_context_len, int32_t partition_size) {
   return ((int64_t)max_context_len + partition_size - 1) / partition_size;
 }
 
+size_t align16(size_t x) { return (x + 15) & ~(size_t)15; }
+
+// Balanced-mode workspace: tile prefix sums, then 2 partial slots per
+// workgroup of group-size rows (m, l, and head_dim partial outputs).
+size_t balanced_ws_bytes(int32_t num_seqs, int32_t group, int32_t head_dim) {
+  const size_t rows = 2 * (size_t)pa::kBalancedMaxWg * (size_t)group;
+  return align16(((size_t)num_seqs + 1) * sizeof(int32_t)) + rows * ((size_t)head_dim + 2) * sizeof(float);
+}
+
 }  // namespace
+
+namespace pa {
+
+hipError_t balanced_grid(const void* kernel, int block_threads, int* nwg) {
+  static std::mutex mu;
+  static std::map<std::pair<const void*, int>, int> cache;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = cache.find({kernel, dev});
+  if (it != cache.end()) {
+    *nwg = it->second;
+    return hipSuccess;
+  }
+  int cus = 0, per_cu = 0;
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, block_threads, 0);
+  if (e != hipSuccess) return e;
+  int n = cus * (per_cu > 0 ? per_cu : 1);
+  if (n > kBalancedMaxWg) n = kBalancedMaxWg;
+  cache[{kernel, dev}] = n;
+  *nwg = n;
+  return hipSuccess;
+}
+
+}  // namespace pa
 
 PA_EXPORT const char* pa_status_string(pa_status s) {
   switch (s) {
@@ -48,7 +88,8 @@ PA_EXPORT const char* pa_status_string(pa_status s) {
     case PA_ERR_BLOCK_SIZE: return "PA_ERR_BLOCK_SIZE: block_size must be 8, 16 or 32";
     case PA_ERR_DTYPE: return "PA_ERR_DTYPE: dtype must be PA_F32, PA_F16 or PA_BF16";
     case PA_ERR_PARTITION:
-      return "PA_ERR_PARTITION: partition_size must be 0 or a positive multiple of 16 and of block_size";
+      return "PA_ERR_PARTITION: partition_size must be 0, PA_PARTITION_BALANCED (at most 4096 "
+             "sequences) or a positive multiple of 16 and of block_size";
     case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE: workspace missing or too small";
     case PA_ERR_HIP: return "PA_ERR_HIP: a HIP launch failed (see pa_last_hip_error)";
     case PA_ERR_ALIGN: return "PA_ERR_ALIGN: data pointers must be 16-byte aligned";
@@ -93,10 +134,14 @@ PA_EXPORT pa_status pa_block_copy(void* k_pool, void* v_pool, const int32_t* blo
                                           num_blocks, reinterpret_cast<hipStream_t>(stream)));
 }
 
-PA_EXPORT size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
-                                           int32_t max_context_len, int32_t partition_size) {
-  if (num_seqs < 0 || num_q_heads < 1 || head_dim < 1 || max_context_len < 0 || partition_size < 0)
+PA_EXPORT size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                           int32_t head_dim, int32_t max_context_len,
+                                           int32_t partition_size) {
+  if (num_seqs < 0 || num_q_heads < 1 || num_kv_heads < 1 || num_q_heads % num_kv_heads != 0 ||
+      head_dim < 1 || max_context_len < 0 || partition_size < PA_PARTITION_BALANCED)
     return (size_t)-1;
+  if (partition_size == PA_PARTITION_BALANCED)
+    return balanced_ws_bytes(num_seqs, num_q_heads / num_kv_heads, head_dim);
   const int64_t np = num_partitions(max_context_len, partition_size);
   if (partition_size == 0 || np <= 1) return 0;
   return (size_t)num_seqs * (size_t)num_q_heads * (size_t)np * ((size_t)head_dim + 2) * sizeof(float);
@@ -104,13 +149,13 @@ PA_EXPORT size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads
 
 PA_EXPORT int32_t pa_decode_choose_partition(int32_t num_seqs, int32_t num_kv_heads,
                                              int32_t max_context_len, int32_t block_size) {
-  (void)num_seqs;
   (void)num_kv_heads;
   (void)block_size;
-  // 512 tokens (a multiple of every supported block size and of the 16-token
-  // tile): long sequences split into many similar-sized units, which evens out
-  // ragged batches across the 256 CUs; short batches are not split at all.
-  return max_context_len > 512 ? 512 : 0;
+  // The balanced split gives every resident workgroup the same number of
+  // tiles, so ragged batches and a few very long sequences finish together;
+  // tiny batches (one table window or less) are not worth a second launch.
+  if (max_context_len <= 64 || num_seqs > pa::kBalancedMaxSeqs) return 0;
+  return PA_PARTITION_BALANCED;
 }
 
 PA_EXPORT pa_status pa_decode_attention(void* out, const void* query, const void* k_pool,
@@ -128,17 +173,19 @@ PA_EXPORT pa_status pa_decode_attention(void* out, const void* query, const void
       max_blocks_per_seq < 1 || num_blocks < 1 || max_context_len < 0)
     return PA_ERR_SHAPE;
   if (num_q_heads % num_kv_heads != 0 || !group_ok(num_q_heads / num_kv_heads)) return PA_ERR_SHAPE;
-  if (partition_size < 0 || (partition_size > 0 && (partition_size % 16 != 0 ||
-                                                     partition_size % block_size != 0)))
+  const bool balanced = partition_size == PA_PARTITION_BALANCED;
+  if (partition_size < PA_PARTITION_BALANCED ||
+      (partition_size > 0 && (partition_size % 16 != 0 || partition_size % block_size != 0)))
     return PA_ERR_PARTITION;
+  if (balanced && num_seqs > pa::kBalancedMaxSeqs) return PA_ERR_PARTITION;
   if (num_seqs == 0) return PA_OK;
   if (!out || !query || !k_pool || !v_pool || !block_tables || !context_lens) return PA_ERR_NULL;
   if (!aligned16(out) || !aligned16(query) || !aligned16(k_pool) || !aligned16(v_pool))
     return PA_ERR_ALIGN;
 
   const int32_t group = num_q_heads / num_kv_heads;
-  const int64_t np = num_partitions(max_context_len, partition_size);
-  const bool split = np > 1;
+  const int64_t np = balanced ? 1 : num_partitions(max_context_len, partition_size);
+  const bool split = balanced || np > 1;
   const bool mfma = dtype != PA_F32 && group >= 2;
   const int32_t heads_per_unit = mfma ? group : (group < 4 ? group : 4);
   const int64_t chunks = mfma ? num_kv_heads : num_q_heads / heads_per_unit;
@@ -158,21 +205,30 @@ PA_EXPORT pa_status pa_decode_attention(void* out, const void* query, const void
   a.max_blocks_per_seq = max_blocks_per_seq;
   a.num_blocks = num_blocks;
   a.max_context_len = max_context_len;
-  a.partition_size = split ? partition_size : (max_context_len > 16 ? max_context_len : 16);
+  a.partition_size = (partition_size > 0 && np > 1) ? partition_size
+                                                    : (max_context_len > 16 ? max_context_len : 16);
   a.num_parts = (int32_t)np;
   a.split = split ? 1 : 0;
   a.head_chunks = (int32_t)chunks;
+  a.mode = balanced ? pa::kModeBalanced : pa::kModeUnit;
   a.scale_log2 = scale * pa::kLog2e;
   if (split) {
-    const size_t need = pa_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_len,
-                                                  partition_size);
+    const size_t need = pa_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                                  max_context_len, partition_size);
     if (!workspace || workspace_bytes < need) return PA_ERR_WORKSPACE;
-    if ((reinterpret_cast<uintptr_t>(workspace) & 3u) != 0) return PA_ERR_ALIGN;
-    const size_t rows = (size_t)num_seqs * num_q_heads * (size_t)np;
-    float* ws = static_cast<float*>(workspace);
-    a.ws_m = ws;
-    a.ws_l = ws + rows;
-    a.ws_o = ws + 2 * rows;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 15u) != 0) return PA_ERR_ALIGN;
+    char* ws = static_cast<char*>(workspace);
+    size_t rows;
+    if (balanced) {
+      a.ws_cum = reinterpret_cast<int32_t*>(ws);
+      ws += align16(((size_t)num_seqs + 1) * sizeof(int32_t));
+      rows = 2 * (size_t)pa::kBalancedMaxWg * (size_t)heads_per_unit;
+    } else {
+      rows = (size_t)num_seqs * num_q_heads * (size_t)np;
+    }
+    a.ws_m = reinterpret_cast<float*>(ws);
+    a.ws_l = a.ws_m + rows;
+    a.ws_o = a.ws_l + rows;
   }
   return hip_status(pa::launch_decode(a, elem_of(dtype), head_dim, block_size, group,
                                       reinterpret_cast<hipStream_t>(stream)));

@@ -21,6 +21,18 @@ struct F32 { using elem = float;    static constexpr int bytes = 4; };
 struct F16 { using elem = uint16_t; static constexpr int bytes = 2; };
 struct BF16 { using elem = uint16_t; static constexpr int bytes = 2; };
 
+// Buffer resource over [base, base + bytes): loads through it are range
+// checked by the hardware (an offset past the end reads zeros), and the
+// base lives in SGPRs, so a lane only supplies a 32-bit offset.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kRsrcWord3 = 0x00020000;  // raw 32-bit data, gfx9-family buffer descriptor
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kRsrcWord3);
+}
+__device__ __forceinline__ u32x4 buf_ld16(rsrc_t r, uint32_t voff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 0);
+}
+
 __device__ __forceinline__ u32x4 ld16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
@@ -107,14 +119,23 @@ __device__ __forceinline__ float quad_bcast(float x) {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // ---- work-unit mapping -----------------------------------------------------
-// Workgroup b runs on XCD b % 8.  Give each XCD a contiguous range of logical
-// units so neighbouring units (e.g. samples sharing a prompt's blocks) meet in
-// the same L2.  Bijective on [0, n).
+// Workgroup b runs on XCD b % 8 (dealt round-robin).  Map b to a logical unit
+// so that each XCD receives runs of 8 consecutive logical units, the runs
+// dealt round-robin: neighbouring units (e.g. samples that share a prompt's
+// blocks) meet in one XCD's L2 at about the same time, and every XCD still
+// gets an even mix of the whole grid.  Bijective on [0, n); the last n % 64
+// units map to themselves.
 __device__ __forceinline__ uint32_t xcd_unit(uint32_t b, uint32_t n) {
-  const uint32_t q = n / kNumXcd, r = n % kNumXcd;
-  const uint32_t x = b % kNumXcd, k = b / kNumXcd;
-  return x * q + (x < r ? x : r) + k;
+  const uint32_t full = n & ~63u;
+  if (b >= full) return b;
+  const uint32_t x = b & 7u, k = b >> 3;
+  return ((k >> 3) << 6) | (x << 3) | (k & 7u);
 }
+
+constexpr int kModeUnit = 0;       // one workgroup per (sequence, head group[, partition])
+constexpr int kModeBalanced = 1;   // resident grid, equal share of the flattened tiles each
+constexpr int kBalancedMaxSeqs = 4096;   // sequences a balanced launch can take (LDS prefix)
+constexpr int kBalancedMaxWg = 2048;     // workgroups a balanced workspace is sized for
 
 // Arguments of the decode kernels (by value, in the kernarg segment).
 struct DecodeArgs {
@@ -127,12 +148,15 @@ struct DecodeArgs {
   float* ws_m;                // [S, Hq, NP] running max (log2 domain)
   float* ws_l;                // [S, Hq, NP] running sum
   float* ws_o;                // [S, Hq, NP, D] un-normalised partial outputs
+                              // (balanced mode: [2 W, H] and [2 W, H, D] partial slots)
+  int32_t* ws_cum;            // balanced mode: [S + 1] tile prefix sums
   int32_t num_seqs, num_q_heads, num_kv_heads;
   int32_t max_blocks_per_seq, num_blocks, max_context_len;
   int32_t partition_size;     // tokens per unit (>= max_context_len when not split)
   int32_t num_parts;          // partitions in the grid (1 when not split)
   int32_t split;              // 1 when partial results go through the workspace
-  int32_t head_chunks;        // q-head chunks per sequence (VALU path)
+  int32_t head_chunks;        // head groups per sequence (Hkv on the MFMA path)
+  int32_t mode;               // kModeUnit or kModeBalanced
   float scale_log2;           // scale * log2(e)
 };
 

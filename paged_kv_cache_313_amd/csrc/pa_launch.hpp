@@ -19,9 +19,13 @@ hipError_t launch_block_copy(void* k_pool, void* v_pool, const int32_t* block_ma
                              int32_t num_pairs, int64_t block_bytes, int32_t num_blocks,
                              hipStream_t stream);
 
-// Decode: partition pass (direct output for single-partition sequences) plus,
-// when split, the merge kernel.  `use_mfma` selects the grouped-query MFMA
-// kernel (f16/bf16, group size 2..16); otherwise the VALU kernel.
+// Workgroups of `kernel` (block of `block_threads`) that the current device
+// keeps resident at once, capped at kBalancedMaxWg; cached per kernel/device.
+hipError_t balanced_grid(const void* kernel, int block_threads, int* nwg);
+
+// Decode: the segment kernel of the chosen mode plus, when results are split,
+// its merge kernel.  f16/bf16 with group size 2..16 run the MFMA core, all
+// other cases the VALU core.
 hipError_t launch_decode(const DecodeArgs& args, Elem elem, int head_dim, int block_size,
                          int group, hipStream_t stream);
 

@@ -116,7 +116,9 @@ def decode(lib, **kw):
     (dict(Hq=24, Hkv=8), 2),                  # group 3 unsupported
     (dict(Hq=64, Hkv=2), 2),                  # group 32 unsupported
     (dict(MB=0), 2), (dict(NB=0), 2), (dict(maxL=-1), 2), (dict(S=-1), 2),
-    (dict(P=-16), 5), (dict(P=24), 5), (dict(P=16, bs=32), 5), (dict(P=8, bs=8), 5),
+    (dict(P=-16), 5), (dict(P=-2), 5), (dict(P=24), 5), (dict(P=16, bs=32), 5), (dict(P=8, bs=8), 5),
+    (dict(P=-1, S=4097), 5),                  # balanced split takes at most 4096 sequences
+    (dict(P=-1), 6),                          # balanced split needs a workspace
     (dict(out=None), 1), (dict(q=None), 1), (dict(tbl=None), 1), (dict(lens=None), 1),
     (dict(k=B + 4), 8), (dict(out=A + 2), 8),
     (dict(P=32, maxL=128), 6),                # split needs a workspace
@@ -129,18 +131,24 @@ def test_decode_argument_checks(lib, kw, status):
 
 def test_workspace_size(lib):
     f = lib.pa_decode_workspace_bytes
-    assert f(16, 32, 128, 131072, 512) == 16 * 32 * 256 * 130 * 4
-    assert f(16, 32, 128, 131072, 0) == 0
-    assert f(16, 32, 128, 500, 512) == 0              # one partition: written directly
-    assert f(3, 8, 64, 513, 512) == 3 * 8 * 2 * 66 * 4
-    assert f(-1, 8, 64, 513, 512) == ctypes.c_size_t(-1).value
+    assert f(16, 32, 8, 128, 131072, 512) == 16 * 32 * 256 * 130 * 4
+    assert f(16, 32, 8, 128, 131072, 0) == 0
+    assert f(16, 32, 8, 128, 500, 512) == 0              # one partition: written directly
+    assert f(3, 8, 8, 64, 513, 512) == 3 * 8 * 2 * 66 * 4
+    # balanced: prefix sums (padded to 16 B) + 2 slots x 2048 workgroups x group rows
+    assert f(256, 32, 8, 128, 8193, -1) == 1040 + 2 * 2048 * 4 * 130 * 4
+    assert f(5, 8, 8, 64, 100, -1) == 32 + 2 * 2048 * 1 * 66 * 4
+    assert f(-1, 8, 8, 64, 513, 512) == ctypes.c_size_t(-1).value
+    assert f(4, 8, 3, 64, 513, 512) == ctypes.c_size_t(-1).value
+    assert f(4, 8, 8, 64, 513, -2) == ctypes.c_size_t(-1).value
 
 
 @pytest.mark.parametrize("maxL", [0, 1, 100, 512, 513, 8193, 131072])
 @pytest.mark.parametrize("bs", [8, 16, 32])
 def test_chosen_partition_is_valid(lib, maxL, bs):
     p = lib.pa_decode_choose_partition(16, 8, maxL, bs)
-    assert p == 0 or (p > 0 and p % 16 == 0 and p % bs == 0)
+    assert p in (0, -1) or (p > 0 and p % 16 == 0 and p % bs == 0)
+    assert lib.pa_decode_choose_partition(5000, 8, maxL, bs) == 0   # too many for a balanced launch
 
 
 def test_binding_refuses_cpu_tensors(lib):

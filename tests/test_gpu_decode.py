@@ -36,7 +36,7 @@ CASES += [("bf16", 128, 16, 2), ("bf16", 128, 16, 8), ("bf16", 128, 16, 16), ("f
           ("f32", 64, 16, 2), ("f32", 128, 16, 8)]
 
 
-@pytest.mark.parametrize("partition", [0, 64, 512])
+@pytest.mark.parametrize("partition", [0, 64, 512, -1])
 @pytest.mark.parametrize("dtype,D,bs,G", CASES)
 def test_decode_matches_oracle(dtype, D, bs, G, partition):
     b = batch(dtype, D, bs, G)
@@ -56,7 +56,8 @@ def test_single_token_is_value_row_exactly(dtype, G):
             assert out[s, h].tobytes() == b.v_pool[blk, h // G, 0].tobytes()
 
 
-@pytest.mark.parametrize("dtype,G,partition", [("bf16", 4, 64), ("f16", 1, 0), ("f32", 2, 64)])
+@pytest.mark.parametrize("dtype,G,partition", [("bf16", 4, 64), ("f16", 1, 0), ("f32", 2, 64),
+                                               ("bf16", 4, -1)])
 def test_physical_permutation_bit_identical(dtype, G, partition):
     b = batch(dtype, 128, 16, G)
     note(f"permutation {dtype} G={G}")
@@ -86,7 +87,8 @@ def test_repeat_runs_bit_identical():
     assert outs[0].tobytes() == outs[1].tobytes() == outs[2].tobytes()
 
 
-@pytest.mark.parametrize("dtype,G,partition", [("bf16", 4, 64), ("f32", 1, 0), ("f16", 1, 32)])
+@pytest.mark.parametrize("dtype,G,partition", [("bf16", 4, 64), ("f32", 1, 0), ("f16", 1, 32),
+                                               ("bf16", 4, -1), ("f16", 1, -1)])
 def test_empty_sequences_give_zero_rows(dtype, G, partition):
     b = batch(dtype, 64, 16, G, lens=[0, 40, 0, 3])
     note(f"empty sequences {dtype}")
@@ -125,7 +127,8 @@ def test_lengths_clamped_to_max_context_len():
 def test_explicit_workspace_and_stream():
     b = batch("bf16", 128, 32, 4, lens=[700, 1500, 33])
     d = torch_io.to_device(b)
-    need = P.decode_workspace_bytes(b.num_seqs, b.num_q_heads, b.head_dim, b.max_context_len, 512)
+    need = P.decode_workspace_bytes(b.num_seqs, b.num_q_heads, b.num_kv_heads, b.head_dim,
+                                    b.max_context_len, 512)
     assert need > 0
     ws = torch.empty(need, dtype=torch.uint8, device="cuda")
     out = torch.empty_like(d.query)
@@ -136,3 +139,21 @@ def test_explicit_workspace_and_stream():
                            b.max_context_len, 512, out=out, workspace=ws, stream=s)
     s.synchronize()
     check_close(gpu_out_f64(out, "bf16"), oracle_out(b), "bf16", "workspace")
+
+
+@pytest.mark.parametrize("partition", [64, -1])
+@pytest.mark.parametrize("dtype,G", [("bf16", 4), ("f32", 4), ("f16", 1)])
+def test_split_ignores_stale_workspace(dtype, G, partition):
+    """The workspace is scratch: a split decode must read back only what it
+    wrote in the same call, so NaN left there beforehand cannot reach the
+    output (short batches leave some balanced workgroups without tiles)."""
+    b = batch(dtype, 64, 8, G)
+    d = torch_io.to_device(b)
+    need = P.decode_workspace_bytes(b.num_seqs, b.num_q_heads, b.num_kv_heads, b.head_dim,
+                                    b.max_context_len, partition)
+    ws = torch.full((need // 4,), float("nan"), dtype=torch.float32, device="cuda")
+    note(f"stale workspace {dtype} G={G} P={partition}")
+    out = P.decode_attention(d.query, d.k_pool, d.v_pool, d.block_tables, d.context_lens, b.scale,
+                             b.max_context_len, partition, workspace=ws)
+    torch.cuda.synchronize()
+    check_close(gpu_out_f64(out, dtype), oracle_out(b), dtype, "stale workspace")
