@@ -193,7 +193,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}): "
-              "the decode path has no multi-GPU leg in this build", file=sys.stderr)
+              "the decode path here is a single-GPU kernel; sharding across GPUs is not implemented", file=sys.stderr)
         sys.exit(2)
     if args.calibrate_copy_mib:
         calibrate_copy(args.calibrate_copy_mib)

@@ -43,10 +43,10 @@ int64_t num_partitions(int32_t max_context_len, int32_t partition_size) {
 
 size_t align16(size_t x) { return (x + 15) & ~(size_t)15; }
 
-// Balanced-mode workspace: tile prefix sums, then 2 partial slots per
-// workgroup of group-size rows (m, l, and head_dim partial outputs).
+// Balanced-mode workspace: tile prefix sums, then 2 partial slots per wave of
+// group-size rows (m, l, and head_dim partial outputs).
 size_t balanced_ws_bytes(int32_t num_seqs, int32_t group, int32_t head_dim) {
-  const size_t rows = 2 * (size_t)pa::kBalancedMaxWg * (size_t)group;
+  const size_t rows = 2 * (size_t)pa::kBalancedMaxWaves * (size_t)group;
   return align16(((size_t)num_seqs + 1) * sizeof(int32_t)) + rows * ((size_t)head_dim + 2) * sizeof(float);
 }
 
@@ -54,7 +54,7 @@ size_t balanced_ws_bytes(int32_t num_seqs, int32_t group, int32_t head_dim) {
 
 namespace pa {
 
-hipError_t balanced_grid(const void* kernel, int block_threads, int* nwg) {
+hipError_t balanced_grid(const void* kernel, int block_threads, int max_wg, int* nwg) {
   static std::mutex mu;
   static std::map<std::pair<const void*, int>, int> cache;
   int dev = 0;
@@ -72,7 +72,7 @@ hipError_t balanced_grid(const void* kernel, int block_threads, int* nwg) {
   e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, block_threads, 0);
   if (e != hipSuccess) return e;
   int n = cus * (per_cu > 0 ? per_cu : 1);
-  if (n > kBalancedMaxWg) n = kBalancedMaxWg;
+  if (n > max_wg) n = max_wg;
   cache[{kernel, dev}] = n;
   *nwg = n;
   return hipSuccess;
@@ -222,7 +222,7 @@ PA_EXPORT pa_status pa_decode_attention(void* out, const void* query, const void
     if (balanced) {
       a.ws_cum = reinterpret_cast<int32_t*>(ws);
       ws += align16(((size_t)num_seqs + 1) * sizeof(int32_t));
-      rows = 2 * (size_t)pa::kBalancedMaxWg * (size_t)heads_per_unit;
+      rows = 2 * (size_t)pa::kBalancedMaxWaves * (size_t)heads_per_unit;
     } else {
       rows = (size_t)num_seqs * num_q_heads * (size_t)np;
     }

@@ -73,6 +73,66 @@ template <> struct Unpack<F16> {
   }
 };
 
+// ---- dot products of one 16-byte chunk pair, into 4 independent partials ----
+// (16-bit types: v_dot2c_f32_{f16,bf16}, products exact in fp32)
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+template <class T> struct Dot16;
+template <> struct Dot16<F32> {
+  __device__ __forceinline__ static void run(u32x4 q, u32x4 k, float* d) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) d[e] = fmaf(__uint_as_float(q[e]), __uint_as_float(k[e]), d[e]);
+  }
+};
+template <> struct Dot16<F16> {
+  __device__ __forceinline__ static void run(u32x4 q, u32x4 k, float* d) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t qe = q[e], ke = k[e];
+      d[e] = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, qe), __builtin_bit_cast(f16x2, ke), d[e], false);
+    }
+  }
+};
+template <> struct Dot16<BF16> {
+  __device__ __forceinline__ static void run(u32x4 q, u32x4 k, float* d) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t qe = q[e], ke = k[e];
+      d[e] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qe), __builtin_bit_cast(bf16x2, ke),
+                                             d[e], false);
+    }
+  }
+};
+
+// acc[0..NE) += p * (16-byte chunk v), fp32 accumulate (fp16: v_fma_mix_f32)
+template <class T> struct Axpy16;
+template <> struct Axpy16<F32> {
+  __device__ __forceinline__ static void run(float p, u32x4 v, float* acc) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] = fmaf(p, __uint_as_float(v[e]), acc[e]);
+  }
+};
+template <> struct Axpy16<F16> {
+  __device__ __forceinline__ static void run(float p, u32x4 v, float* acc) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t x = v[e];
+      acc[2 * e] = fmaf(p, (float)__builtin_bit_cast(_Float16, (uint16_t)(x & 0xffffu)), acc[2 * e]);
+      acc[2 * e + 1] = fmaf(p, (float)__builtin_bit_cast(_Float16, (uint16_t)(x >> 16)), acc[2 * e + 1]);
+    }
+  }
+};
+template <> struct Axpy16<BF16> {
+  __device__ __forceinline__ static void run(float p, u32x4 v, float* acc) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t x = v[e];
+      acc[2 * e] = fmaf(p, __uint_as_float(x << 16), acc[2 * e]);
+      acc[2 * e + 1] = fmaf(p, __uint_as_float(x & 0xffff0000u), acc[2 * e + 1]);
+    }
+  }
+};
+
 // ---- fp32 -> storage, round to nearest even --------------------------------
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);
@@ -135,7 +195,7 @@ __device__ __forceinline__ uint32_t xcd_unit(uint32_t b, uint32_t n) {
 constexpr int kModeUnit = 0;       // one workgroup per (sequence, head group[, partition])
 constexpr int kModeBalanced = 1;   // resident grid, equal share of the flattened tiles each
 constexpr int kBalancedMaxSeqs = 4096;   // sequences a balanced launch can take (LDS prefix)
-constexpr int kBalancedMaxWg = 2048;     // workgroups a balanced workspace is sized for
+constexpr int kBalancedMaxWaves = 4096;  // waves a balanced workspace is sized for
 
 // Arguments of the decode kernels (by value, in the kernarg segment).
 struct DecodeArgs {
@@ -148,7 +208,7 @@ struct DecodeArgs {
   float* ws_m;                // [S, Hq, NP] running max (log2 domain)
   float* ws_l;                // [S, Hq, NP] running sum
   float* ws_o;                // [S, Hq, NP, D] un-normalised partial outputs
-                              // (balanced mode: [2 W, H] and [2 W, H, D] partial slots)
+                              // (balanced mode: 2 slots per wave of H rows each)
   int32_t* ws_cum;            // balanced mode: [S + 1] tile prefix sums
   int32_t num_seqs, num_q_heads, num_kv_heads;
   int32_t max_blocks_per_seq, num_blocks, max_context_len;

@@ -6,25 +6,25 @@
 // changed to read non-contiguous blocks; the simplified sketch walks the table
 // block by block and loads K and V of each physical page).  The sketch
 // normalises per block; the operation reached here is one softmax over the
-// whole context, evaluated as an online softmax: a running max m, a running
-// sum l and an un-normalised accumulator are rescaled by exp(m_old - m_new)
-// whenever the max grows.  Scores are kept in the log2 domain
-// (scale * log2(e) folded in) so every exponential is one v_exp_f32.
+// whole context, evaluated as an online softmax: running maxima, running sums
+// and un-normalised accumulators are rescaled by exp(m_old - m_new) when a max
+// grows.  Scores are kept in the log2 domain (scale * log2(e) folded in) so
+// every exponential is one v_exp_f32.
 //
 // A *segment* is a token range [tok0, tok1) of one sequence for one group of
-// query heads sharing a KV head.  A workgroup of NW waves runs a segment: the
-// segment's block-table slice is staged in LDS (taking the table->block
-// dependent load off the tile path), the waves take interleaved 16-token
-// tiles, and at the end the waves merge through LDS.  Three ways to cut the
-// work into segments:
-//  * unit mode, no split: one workgroup per (sequence, head group);
-//  * unit mode, fixed partitions of P tokens: one workgroup per (sequence,
-//    head group, partition), partials merged by decode_merge_parts_kernel;
-//  * balanced mode: the grid holds exactly the workgroups the GPU keeps
-//    resident, and each takes an equal share of the flattened
-//    (sequence, head group, tile) space, so ragged batches finish together;
-//    a (sequence, head group) shared by several workgroups is merged by
-//    decode_merge_balanced_kernel.
+// query heads sharing a KV head, and one wave runs it from start to end: it
+// stages the segment's block-table slice in its own LDS window (taking the
+// table->block dependent load off the tile path), streams the 16-token tiles
+// with the next tile's loads in flight, reduces across its lanes and writes
+// the result itself.  Waves never wait for one another, so a wave starting a
+// segment does not stall its neighbours.  Three ways to cut the work:
+//  * unit mode, no split: one segment per (sequence, head group);
+//  * unit mode, fixed partitions of P tokens: one segment per (sequence, head
+//    group, partition), partials merged by decode_merge_parts_kernel;
+//  * balanced mode: the grid holds exactly the waves the GPU keeps resident,
+//    and each takes an equal share of the flattened (sequence, head group,
+//    tile) space, so ragged batches finish together; a (sequence, head group)
+//    shared by several waves is merged by decode_merge_balanced_kernel.
 #include <type_traits>
 
 #include "pa_common.hpp"
@@ -33,120 +33,125 @@
 namespace pa {
 
 constexpr int kTile = 16;      // tokens per tile
-constexpr int kTblWin = 256;   // block-table entries staged in LDS at a time
+constexpr int kTblWin = 256;   // block-table entries a wave stages in LDS at a time
+// A lane rescales its accumulators only when a score exceeds its running max
+// by more than this (log2 units), so every p <= 2^8 and sums stay far from
+// fp32 overflow; the result is the same up to rounding.
+constexpr float kLazy = 8.f;
 
-template <int NW>
-__device__ __forceinline__ void stage_table(int32_t* s_tbl, const int32_t* row, int first, int count,
-                                            int num_blocks) {
-  for (int i = threadIdx.x; i < count; i += NW * kWave) {
+// Stage table entries [first, first+count) of one sequence into this wave's
+// LDS window (ids clamped into the pool: memory-safe on bad tables).  LDS
+// operations of one wave complete in order; the wait makes the entries
+// visible to every lane before the wave reads them.
+__device__ __forceinline__ void stage_table_wave(int32_t* tbl, const int32_t* row, int first, int count,
+                                                 int num_blocks, int lane) {
+  for (int i = lane; i < count; i += kWave) {
     const int e = row[first + i];
-    s_tbl[i] = ((unsigned)e < (unsigned)num_blocks) ? e : 0;  // memory-safe clamp
+    tbl[i] = ((unsigned)e < (unsigned)num_blocks) ? e : 0;
   }
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+  __builtin_amdgcn_wave_barrier();
 }
 
-// Walk the 16-token tiles assigned to this wave (tiles wave, wave+NW, ...),
-// keeping the next tile's K/V loads in flight while the current one is
-// computed.  The loop runs over pairs of tiles with ping-pong buffers and has a
-// single exit, so that no path (not even a structurized, never-taken one)
-// returns to the loop head with the prefetch outstanding; that lets the
-// compiler's vmcnt waits leave the newer loads in flight.  Loads are
-// unconditional: a prefetch past the wave's last tile re-reads that tile (an
-// L2 hit) instead of branching.
-template <int NW, class Buf, class Load, class Compute>
-__device__ __forceinline__ void tile_loop(int ntiles, int wave, Load&& load, Compute&& compute) {
-  if (wave >= ntiles) return;
-  const int n = (ntiles - wave + NW - 1) / NW;   // tiles of this wave
-  const int last = wave + (n - 1) * NW;
+// Walk tiles 0 .. ntiles-1 keeping the next tile's K/V loads in flight while
+// the current one is computed.  The loop runs over pairs of tiles with
+// ping-pong buffers and has a single exit, so that no path (not even a
+// structurized, never-taken one) returns to the loop head with the prefetch
+// outstanding; that lets the compiler's vmcnt waits leave the newer loads in
+// flight.  Loads are unconditional: a prefetch past the last tile re-reads it
+// (an L2 hit) instead of branching.
+template <class Buf, class Load, class Compute>
+__device__ __forceinline__ void tile_loop(int ntiles, Load&& load, Compute&& compute) {
+  if (ntiles <= 0) return;
+  const int last = ntiles - 1;
   Buf a, b;
-  int ti = wave;
-  load(ti, a);
-  for (int k = 0; k + 2 <= n; k += 2) {
-    load(min(ti + NW, last), b);
+  int ti = 0;
+  load(0, a);
+  for (int k = 0; k + 2 <= ntiles; k += 2) {
+    load(min(ti + 1, last), b);
     compute(ti, a);
-    load(min(ti + 2 * NW, last), a);
-    compute(ti + NW, b);
-    ti += 2 * NW;
+    load(min(ti + 2, last), a);
+    compute(ti + 1, b);
+    ti += 2;
   }
-  if (n & 1) compute(ti, a);
+  if (ntiles & 1) compute(ti, a);
 }
 
 // Byte offsets, from the start of a KV head's slice of the pool, of the
-// 16-token tile that starts `rel` tokens after the first staged block.  The block id is
-// wave-uniform, so the offsets live in SGPRs and each lane adds a constant
-// 32-bit offset: no per-lane address arithmetic on the tile path.  With
-// block_size >= 16 the tile lies in one block (lo == hi); with 8 its tokens
-// [8, 16) are in the next block, which may be past the window's last staged
-// entry only when every one of those tokens is masked (then lo is reused).
+// 16-token tile that starts `rel` tokens after the first staged block.  The
+// block id is wave-uniform, so the offsets live in SGPRs and each lane adds a
+// constant 32-bit offset: no per-lane address arithmetic on the tile path.
+// With block_size >= 16 the tile lies in one block (lo == hi); with 8 its
+// tokens [8, 16) are in the next block, which may be past the window's last
+// staged entry only when every one of those tokens is masked (then lo is
+// reused).
 template <int BS, int ROWB>
-__device__ __forceinline__ void tile_offsets(const int32_t* s_tbl, int rel, int nent,
-                                             size_t blk_stride, size_t& lo, size_t& hi) {
+__device__ __forceinline__ void tile_offsets(const int32_t* tbl, int rel, int nent, size_t blk_stride,
+                                             size_t& lo, size_t& hi) {
   if constexpr (BS >= 16) {
-    const int b = __builtin_amdgcn_readfirstlane(s_tbl[rel / BS]);
+    const int b = __builtin_amdgcn_readfirstlane(tbl[rel / BS]);
     lo = hi = (size_t)b * blk_stride + (size_t)(rel % BS) * ROWB;
   } else {
     const int e = rel / BS;
-    const int b0 = __builtin_amdgcn_readfirstlane(s_tbl[e]);
-    const int b1 = e + 1 < nent ? __builtin_amdgcn_readfirstlane(s_tbl[e + 1]) : b0;
+    const int b0 = __builtin_amdgcn_readfirstlane(tbl[e]);
+    const int b1 = e + 1 < nent ? __builtin_amdgcn_readfirstlane(tbl[e + 1]) : b0;
     lo = (size_t)b0 * blk_stride;
     hi = (size_t)b1 * blk_stride;
   }
 }
 
-// Per-wave results of a segment, merged across the workgroup's waves.
-template <int H, int D, int NW>
-struct SegSmem {
-  int32_t tbl[kTblWin];
-  float m[NW][H], l[NW][H];
-  float acc[NW][H][D];
+// Where a segment's result goes: the output rows (direct) or partial rows
+// prow0 + hh * pstride of the workspace (m, l, un-normalised acc).
+struct Dest {
+  bool direct;
+  size_t prow0, pstride;
 };
 
-// Merge the NW waves' (m, l, acc) and write H rows: the output (direct) or a
-// partial (m, l, un-normalised acc) at workspace rows prow0 + hh * pstride.
-template <class T, int D, int H, int NW>
-__device__ __forceinline__ void emit_rows(const DecodeArgs& a, const SegSmem<H, D, NW>& sm, int s,
-                                          int h0, bool direct, size_t prow0, size_t pstride) {
-  for (int idx = threadIdx.x; idx < H * D; idx += NW * kWave) {
-    const int hh = idx / D, d = idx - (idx / D) * D;
-    float M = kNegInf;
+// Write n consecutive results of head row `orow`, starting at element d0.
+template <class T, int N>
+__device__ __forceinline__ void emit_chunk(const DecodeArgs& a, const Dest& dst, size_t orow, int hh,
+                                           int d0, int D, const float* acc, float l) {
+  if (dst.direct) {
+    const float inv = 1.f / l;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) M = fmaxf(M, sm.m[w][hh]);
-    float lt = 0.f, o = 0.f;
+    for (int e = 0; e < N; ++e) store_elem<T>(a.out, orow * D + d0 + e, acc[e] * inv);
+  } else {
+    const size_t pr = dst.prow0 + (size_t)hh * dst.pstride;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      const float f = fast_exp2(sm.m[w][hh] - M);   // a wave with no tile has m = -inf: f = 0
-      lt += f * sm.l[w][hh];
-      o += f * sm.acc[w][hh][d];
-    }
-    if (direct) {
-      store_elem<T>(a.out, ((size_t)s * a.num_q_heads + h0 + hh) * D + d, o / lt);
-    } else {
-      const size_t pr = prow0 + (size_t)hh * pstride;
-      a.ws_o[pr * D + d] = o;
-      if (d == 0) {
-        a.ws_m[pr] = M;
-        a.ws_l[pr] = lt;
-      }
-    }
+    for (int e = 0; e < N; ++e) a.ws_o[pr * D + d0 + e] = acc[e];
   }
 }
 
-template <class T, int D, int H, int NW>
-__device__ __forceinline__ void store_zero_rows(const DecodeArgs& a, int s, int h0) {
-  for (int idx = threadIdx.x; idx < H * D; idx += NW * kWave)
+__device__ __forceinline__ void emit_ml(const DecodeArgs& a, const Dest& dst, int hh, float m, float l) {
+  if (!dst.direct) {
+    const size_t pr = dst.prow0 + (size_t)hh * dst.pstride;
+    a.ws_m[pr] = m;
+    a.ws_l[pr] = l;
+  }
+}
+
+template <class T, int D, int H>
+__device__ __forceinline__ void store_zero_rows(const DecodeArgs& a, int s, int h0, int lane) {
+  for (int idx = lane; idx < H * D; idx += kWave)
     store_elem<T>(a.out, ((size_t)s * a.num_q_heads + h0) * D + idx, 0.f);
 }
 
 // ============================================================================
 // VALU core: any dtype, H q heads (1, 2 or 4) of one KV head.
-// Lane layout per tile: token tt = lane / 4, quarter qp = lane % 4; the lane
-// holds the row bytes [16 (4 j + qp), +16) for j < NL, i.e. D/4 elements.
+// Lane layout per tile: token slot tt = lane / 4, quarter qp = lane % 4; the
+// lane holds the row bytes [16 (4 j + qp), +16) for j < NL, i.e. D/4
+// elements.  QK^T: v_dot2c_f32_{f16,bf16} (fp32 FMA for fp32) in four
+// independent chains, then a quad sum; P.V: v_fma_mix_f32 for fp16, fp32 FMAs
+// otherwise.  Each token slot keeps its own running max, sum and accumulator,
+// so the tile loop needs no cross-lane reduction beyond the quad's dot sum;
+// the slots are merged with the log-sum-exp rule at the end of the segment.
 // ============================================================================
 template <int NL>
 struct ValuBuf {
   u32x4 k[NL], v[NL];
 };
 
-template <class T, int D, int BS, int H, int NW>
+template <class T, int D, int BS, int H>
 struct ValuCore {
   static constexpr int EB = T::bytes;
   static constexpr int ROWB = D * EB;
@@ -158,26 +163,23 @@ struct ValuCore {
   static_assert(kTblWin * BS % kTile == 0, "window");
   // bytes a tile's buffer resource spans: its 16 rows (8 per block at block_size 8)
   static constexpr uint32_t kTileBytes = (BS >= 16 ? kTile : BS) * ROWB;
-  using Smem = SegSmem<H, D, NW>;
 
-  // q heads h0 .. h0+H-1 of sequence s over tokens [tok0, tok1); leaves the
-  // per-wave results in sm and ends with a barrier.
-  __device__ static void run(const DecodeArgs& a, Smem& sm, int s, int h0, int tok0, int tok1) {
+  // q heads h0 .. h0+H-1 of sequence s over tokens [tok0, tok1), run by one
+  // wave; tbl is the wave's LDS window.
+  __device__ static void run(const DecodeArgs& a, int32_t* tbl, int s, int h0, int tok0, int tok1,
+                             const Dest& dst) {
     const int lane = threadIdx.x & (kWave - 1);
-    // wave-uniform by construction; readfirstlane tells the compiler so that
-    // the tile loop runs on scalar branches (no exec-mask flow blocks)
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int G = a.num_q_heads / a.num_kv_heads;
     const int g = h0 / G;
     const int tt = lane >> 2, qp = lane & 3;
 
-    float qf[H][DPL];  // query rows in fp32, the lane's D/4 elements
+    u32x4 qraw[H][NL];  // the lane's D/4 query elements of each head, as stored
 #pragma unroll
     for (int hh = 0; hh < H; ++hh) {
       const char* qrow = reinterpret_cast<const char*>(a.query) +
                          ((size_t)s * a.num_q_heads + h0 + hh) * ROWB + qp * 16;
 #pragma unroll
-      for (int j = 0; j < NL; ++j) Unpack<T>::run(ld16(qrow + j * 64), &qf[hh][j * NE]);
+      for (int j = 0; j < NL; ++j) qraw[hh][j] = ld16(qrow + j * 64);
     }
     float m_run[H], l_run[H], acc[H][DPL];
 #pragma unroll
@@ -203,13 +205,11 @@ struct ValuCore {
       const int off0 = wb - fblk * BS;
       const int we = min((fblk + kTblWin) * BS, tok1);
       const int nent = (we - 1) / BS - fblk + 1;
-      __syncthreads();
-      stage_table<NW>(sm.tbl, trow, fblk, nent, a.num_blocks);
-      __syncthreads();
+      stage_table_wave(tbl, trow, fblk, nent, a.num_blocks, lane);
 
       auto load = [&](int ti, ValuBuf<NL>& buf) {
         size_t lo, hi;
-        tile_offsets<BS, ROWB>(sm.tbl, off0 + ti * kTile, nent, blk_stride, lo, hi);
+        tile_offsets<BS, ROWB>(tbl, off0 + ti * kTile, nent, blk_stride, lo, hi);
         if constexpr (BS >= 16) {  // one block region: SGPR base + lane offset
           const rsrc_t rk = make_rsrc(kbase + lo, kTileBytes);
           const rsrc_t rv = make_rsrc(vbase + lo, kTileBytes);
@@ -227,83 +227,72 @@ struct ValuCore {
       };
       auto compute = [&](int ti, const ValuBuf<NL>& buf) {
         const bool valid = wb + ti * kTile + tt < we;
-        float kf[DPL];
-#pragma unroll
-        for (int j = 0; j < NL; ++j) Unpack<T>::run(buf.k[j], &kf[j * NE]);
         float pr[H];
 #pragma unroll
         for (int hh = 0; hh < H; ++hh) {
-          float dot = 0.f;
+          float d[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int i = 0; i < DPL; ++i) dot = fmaf(qf[hh][i], kf[i], dot);
+          for (int j = 0; j < NL; ++j) Dot16<T>::run(qraw[hh][j], buf.k[j], d);
+          float dot = (d[0] + d[1]) + (d[2] + d[3]);
           dot += xor_lane<1>(dot);
           dot += xor_lane<2>(dot);
           const float sc = valid ? dot * a.scale_log2 : kNegInf;
-          float tmax = sc;
-          tmax = fmaxf(tmax, xor_lane<4>(tmax));
-          tmax = fmaxf(tmax, xor_lane<8>(tmax));
-          tmax = fmaxf(tmax, xor_lane<16>(tmax));
-          tmax = fmaxf(tmax, xor_lane<32>(tmax));
-          const float m_new = fmaxf(m_run[hh], tmax);
-          if (m_new > m_run[hh]) {  // same value in every lane: a uniform branch
-            const float alpha = fast_exp2(m_run[hh] - m_new);
+          const bool grow = sc > m_run[hh] + kLazy;   // true for a slot's first token
+          if (__any(grow)) {
+            const float m_new = grow ? sc : m_run[hh];
+            const float alpha = grow ? fast_exp2(m_run[hh] - m_new) : 1.f;
             l_run[hh] *= alpha;
 #pragma unroll
             for (int i = 0; i < DPL; ++i) acc[hh][i] *= alpha;
             m_run[hh] = m_new;
           }
-          pr[hh] = fast_exp2(sc - m_run[hh]);
+          pr[hh] = valid ? fast_exp2(sc - m_run[hh]) : 0.f;
           l_run[hh] += pr[hh];
         }
-        float vf[DPL];
 #pragma unroll
-        for (int j = 0; j < NL; ++j) Unpack<T>::run(buf.v[j], &vf[j * NE]);
+        for (int j = 0; j < NL; ++j) {
+          const u32x4 z = {0u, 0u, 0u, 0u};
+          const u32x4 vj = valid ? buf.v[j] : z;   // tail slots may hold NaN
 #pragma unroll
-        for (int i = 0; i < DPL; ++i) vf[i] = valid ? vf[i] : 0.f;  // tail slots may hold NaN
-#pragma unroll
-        for (int hh = 0; hh < H; ++hh)
-#pragma unroll
-          for (int i = 0; i < DPL; ++i) acc[hh][i] = fmaf(pr[hh], vf[i], acc[hh][i]);
+          for (int hh = 0; hh < H; ++hh) Axpy16<T>::run(pr[hh], vj, &acc[hh][j * NE]);
+        }
       };
-      tile_loop<NW, ValuBuf<NL>>((we - wb + kTile - 1) / kTile, wave, load, compute);
+      tile_loop<ValuBuf<NL>>((we - wb + kTile - 1) / kTile, load, compute);
       wb = we;
     }
 
-    // sum over the 16 token slots of the wave (lanes with equal qp)
+    // merge the 16 token slots (lanes with equal qp): rescale to the common
+    // max, then sum; slots that saw no token have m = -inf and weigh 0
 #pragma unroll
     for (int hh = 0; hh < H; ++hh) {
-      float l = l_run[hh];
+      float M = m_run[hh];
+      M = fmaxf(M, xor_lane<4>(M));
+      M = fmaxf(M, xor_lane<8>(M));
+      M = fmaxf(M, xor_lane<16>(M));
+      M = fmaxf(M, xor_lane<32>(M));
+      const float f = m_run[hh] == kNegInf ? 0.f : fast_exp2(m_run[hh] - M);
+      float l = l_run[hh] * f;
       l += xor_lane<4>(l);
       l += xor_lane<8>(l);
       l += xor_lane<16>(l);
       l += xor_lane<32>(l);
-      l_run[hh] = l;
 #pragma unroll
       for (int i = 0; i < DPL; ++i) {
-        float x = acc[hh][i];
+        float x = acc[hh][i] * f;
         x += xor_lane<4>(x);
         x += xor_lane<8>(x);
         x += xor_lane<16>(x);
         x += xor_lane<32>(x);
         acc[hh][i] = x;
       }
-    }
-    if (lane < 4) {
-#pragma unroll
-      for (int hh = 0; hh < H; ++hh)
+      const size_t orow = (size_t)s * a.num_q_heads + h0 + hh;
+      if (tt == 0) {  // lanes 0..3 hold the whole row
 #pragma unroll
         for (int j = 0; j < NL; ++j)
-#pragma unroll
-          for (int e = 0; e < NE; ++e) sm.acc[wave][hh][(4 * j + qp) * NE + e] = acc[hh][j * NE + e];
-      if (lane == 0) {
-#pragma unroll
-        for (int hh = 0; hh < H; ++hh) {
-          sm.m[wave][hh] = m_run[hh];
-          sm.l[wave][hh] = l_run[hh];
-        }
+          emit_chunk<T, NE>(a, dst, orow, hh, (4 * j + qp) * NE, D, &acc[hh][j * NE], l);
       }
+      if (lane == 0) emit_ml(a, dst, hh, M, l);
     }
-    __syncthreads();
   }
 };
 
@@ -320,7 +309,8 @@ struct ValuCore {
 // r = 0..3, in every lane -- the same 4 tokens that the lane's V loads cover.
 // P.V stays on the VALU in fp32: each lane holds one 16-byte chunk of d for
 // its tokens, fetches p of the other heads from its quad (DPP) or row, and
-// accumulates G x 8 fp32 values.
+// accumulates G x 8 fp32 values.  Each row gr keeps its own running max per
+// head (no cross-row reduction per tile); rows merge at the end.
 // ============================================================================
 template <class T, int G>
 __device__ __forceinline__ float bcast_head(float x, int h, int lane) {
@@ -354,7 +344,7 @@ struct MfmaBuf {
   u32x4 k[NQK], v[NVI];
 };
 
-template <class T, int D, int BS, int G, int NW>
+template <class T, int D, int BS, int G>
 struct MfmaCore {
   static constexpr int ROWB = D * 2;
   static constexpr int NQK = D / 32;   // MFMAs per tile (k = 32 per MFMA)
@@ -364,13 +354,12 @@ struct MfmaCore {
   static_assert(16 % G == 0 && G >= 2, "group");
   static_assert(kTblWin * BS % kTile == 0, "window");
   static constexpr uint32_t kTileBytes = (BS >= 16 ? kTile : BS) * ROWB;
-  using Smem = SegSmem<G, D, NW>;
 
   // the G q heads h0 .. h0+G-1 (KV head h0 / G) of sequence s over tokens
-  // [tok0, tok1); leaves the per-wave results in sm and ends with a barrier.
-  __device__ static void run(const DecodeArgs& a, Smem& sm, int s, int h0, int tok0, int tok1) {
+  // [tok0, tok1), run by one wave; tbl is the wave's LDS window.
+  __device__ static void run(const DecodeArgs& a, int32_t* tbl, int s, int h0, int tok0, int tok1,
+                             const Dest& dst) {
     const int lane = threadIdx.x & (kWave - 1);
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int gr = lane >> 4, w = lane & 15;
     const int g = h0 / G;
 
@@ -381,8 +370,8 @@ struct MfmaCore {
 #pragma unroll
       for (int i = 0; i < NQK; ++i) qop[i] = ld16(qrow + (4 * i + gr) * 16);
     }
-    float m_run = kNegInf, l_run = 0.f;  // for head w % G
-    float acc[G][8];                     // d = 8 * (w % CPR) + e
+    float m_run = kNegInf, l_run = 0.f;  // head w % G, tokens of row gr
+    float acc[G][8];                     // row gr, d = 8 * (w % CPR) + e
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
@@ -400,20 +389,16 @@ struct MfmaCore {
     const bool k_hi = BS < 16 && w >= 8;
     const bool v_hi = BS < 16 && gr >= 2;
 
-    // windows of at most kTblWin blocks; a segment may start inside a block
-    // (balanced mode, block_size 32): off0 is that start within its block
     for (int wb = tok0; wb < tok1;) {
       const int fblk = wb / BS;
       const int off0 = wb - fblk * BS;
       const int we = min((fblk + kTblWin) * BS, tok1);
       const int nent = (we - 1) / BS - fblk + 1;
-      __syncthreads();
-      stage_table<NW>(sm.tbl, trow, fblk, nent, a.num_blocks);
-      __syncthreads();
+      stage_table_wave(tbl, trow, fblk, nent, a.num_blocks, lane);
 
       auto load = [&](int ti, MfmaBuf<NQK, NVI>& buf) {
         size_t lo, hi;
-        tile_offsets<BS, ROWB>(sm.tbl, off0 + ti * kTile, nent, blk_stride, lo, hi);
+        tile_offsets<BS, ROWB>(tbl, off0 + ti * kTile, nent, blk_stride, lo, hi);
         if constexpr (BS >= 16) {  // one block region: SGPR base + lane offset
           const rsrc_t rk = make_rsrc(kbase + lo, kTileBytes);
           const rsrc_t rv = make_rsrc(vbase + lo, kTileBytes);
@@ -439,12 +424,11 @@ struct MfmaCore {
         float sc[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) sc[r] = (ts + 4 * gr + r < we) ? sacc[r] * a.scale_log2 : kNegInf;
-        float tmax = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
-        tmax = fmaxf(tmax, xor_lane<16>(tmax));
-        tmax = fmaxf(tmax, xor_lane<32>(tmax));
-        const float m_new = fmaxf(m_run, tmax);
-        if (__any(m_new > m_run)) {
-          const float alpha = fast_exp2(m_run - m_new);
+        const float tmax = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+        const bool grow = tmax > m_run + kLazy;   // true for the row's first valid token
+        if (__any(grow)) {
+          const float m_new = grow ? tmax : m_run;
+          const float alpha = grow ? fast_exp2(m_run - m_new) : 1.f;
           m_run = m_new;
           l_run *= alpha;
 #pragma unroll
@@ -457,18 +441,18 @@ struct MfmaCore {
         float pr[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          pr[r] = fast_exp2(sc[r] - m_run);
+          pr[r] = sc[r] == kNegInf ? 0.f : fast_exp2(sc[r] - m_run);
           l_run += pr[r];
         }
 #pragma unroll
         for (int j = 0; j < NVI; ++j) {
           const int idx = w + 16 * j;
           const int rt = idx / CPR;   // token of the group: uniform for D = 128
-          float vf[8];
-          Unpack<T>::run(buf.v[j], vf);
           const bool vvalid = ts + 4 * gr + rt < we;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) vf[e] = vvalid ? vf[e] : 0.f;
+          const u32x4 z = {0u, 0u, 0u, 0u};
+          const u32x4 vj = vvalid ? buf.v[j] : z;   // tail slots may hold NaN
+          float vf[8];
+          Unpack<T>::run(vj, vf);
 #pragma unroll
           for (int h = 0; h < G; ++h) {
             float ph;
@@ -484,48 +468,56 @@ struct MfmaCore {
           }
         }
       };
-      tile_loop<NW, MfmaBuf<NQK, NVI>>((we - wb + kTile - 1) / kTile, wave, load, compute);
+      tile_loop<MfmaBuf<NQK, NVI>>((we - wb + kTile - 1) / kTile, load, compute);
       wb = we;
     }
 
-    // l: sum over the four token groups; acc: sum over lanes holding the same chunk
-    l_run += xor_lane<16>(l_run);
-    l_run += xor_lane<32>(l_run);
+    // merge the four rows: rescale each to the head's common max, then sum
+    float M = m_run;
+    M = fmaxf(M, xor_lane<16>(M));
+    M = fmaxf(M, xor_lane<32>(M));
+    const float f = m_run == kNegInf ? 0.f : fast_exp2(m_run - M);
+    float l = l_run * f;
+    l += xor_lane<16>(l);
+    l += xor_lane<32>(l);
 #pragma unroll
-    for (int h = 0; h < G; ++h)
+    for (int h = 0; h < G; ++h) {
+      const float fh = bcast_head<T, G>(f, h, lane);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        float x = acc[h][e];
+        float x = acc[h][e] * fh;
         if constexpr (CPR == 8) x += xor_lane<8>(x);
         x += xor_lane<16>(x);
         x += xor_lane<32>(x);
         acc[h][e] = x;
       }
-    if (gr == 0 && w < CPR) {
-#pragma unroll
-      for (int h = 0; h < G; ++h)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) sm.acc[wave][h][8 * w + e] = acc[h][e];
     }
-    if (lane < G) {
-      sm.m[wave][lane] = m_run;
-      sm.l[wave][lane] = l_run;
+    // every row now holds all sums; row gr writes the heads h with h % 4 == gr
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float lh = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(l), h));
+      const float mh = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(M), h));
+      const size_t orow = (size_t)s * a.num_q_heads + h0 + h;
+      if (gr == (h & 3) && w < CPR) emit_chunk<T, 8>(a, dst, orow, h, 8 * w, D, acc[h], lh);
+      if (lane == 0) emit_ml(a, dst, h, mh, lh);
     }
-    __syncthreads();
   }
 };
 
 // ============================================================================
-// Unit-mode kernel: workgroup = (sequence, head group, partition).  Sequence
-// is the fastest index of the logical unit; xcd_unit spreads runs of
-// neighbouring units over the XCDs.
+// Unit-mode kernel: wave = (sequence, head group, partition), sequence the
+// fastest index.  xcd_unit spreads runs of neighbouring workgroups over the
+// XCDs.
 // ============================================================================
 template <class Core, class T, int D, int NW>
 __global__ __launch_bounds__(NW * kWave) void decode_unit_kernel(DecodeArgs a, int block_size) {
   constexpr int H = Core::HEADS;
-  __shared__ typename Core::Smem sm;
-  const uint32_t u = xcd_unit(blockIdx.x, gridDim.x);
+  __shared__ int32_t s_tbl[NW][kTblWin];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const uint32_t u = xcd_unit(blockIdx.x, gridDim.x) * NW + wave;
   const int S = a.num_seqs, C = a.head_chunks;
+  if (u >= (uint32_t)S * C * a.num_parts) return;
   const int s = (int)(u % (uint32_t)S);
   const uint32_t rest = u / (uint32_t)S;
   const int c = (int)(rest % (uint32_t)C);
@@ -535,28 +527,37 @@ __global__ __launch_bounds__(NW * kWave) void decode_unit_kernel(DecodeArgs a, i
   const int P = a.partition_size;
   const int t0 = p * P;
   if (L == 0) {
-    if (p == 0) store_zero_rows<T, D, H, NW>(a, s, h0);
+    if (p == 0) store_zero_rows<T, D, H>(a, s, h0, lane);
     return;
   }
   if (t0 >= L) return;
   const int t1 = min(t0 + P, L);
-  const bool direct = !a.split || L <= P;
-  Core::run(a, sm, s, h0, t0, t1);
   // partial rows: (s, h, p) -> ((s * Hq + h) * NP + p)
-  emit_rows<T, D, H, NW>(a, sm, s, h0, direct,
-                         ((size_t)s * a.num_q_heads + h0) * a.num_parts + p, (size_t)a.num_parts);
+  const Dest dst{!a.split || L <= P, ((size_t)s * a.num_q_heads + h0) * a.num_parts + p,
+                 (size_t)a.num_parts};
+  Core::run(a, s_tbl[wave], s, h0, t0, t1, dst);
 }
 
 // ============================================================================
 // Balanced-mode kernel.  Flattened space: sequence s owns tiles
 // [C cum[s], C cum[s+1]) (C head groups of ceil(L_s / 16) tiles each, head
-// group major).  Of ntot tiles, workgroup w takes [w ntot / W, (w+1) ntot / W).  A (sequence, head
-// group) wholly inside the range is written directly; the first and the last
-// segment of the range, when they are pieces of a larger one, go to partial
-// slots 2w and 2w+1 (H rows each).  Workgroup 0 also stores cum for the merge.
+// group major).  Of ntot tiles, wave w of W takes [w ntot / W, (w+1) ntot / W).
+// A (sequence, head group) wholly inside the range is written directly; the
+// first and the last segment of the range, when they are pieces of a larger
+// one, go to partial slots 2w and 2w+1 (H rows each).  Each XCD gets a
+// contiguous run of waves (so samples sharing a prompt's blocks meet in one
+// L2); workgroup 0 also stores cum for the merge.
 // ============================================================================
 __device__ __forceinline__ int64_t range_start(int64_t w, int64_t ntot, int64_t W) {
   return w * ntot / W;
+}
+
+// Workgroup b runs on XCD b % 8: give XCD x the contiguous logical range
+// [x q + min(x, r), ...) of the n workgroups (q = n / 8, r = n % 8).
+__device__ __forceinline__ uint32_t xcd_contiguous(uint32_t b, uint32_t n) {
+  const uint32_t q = n / kNumXcd, r = n % kNumXcd;
+  const uint32_t x = b % kNumXcd, k = b / kNumXcd;
+  return x * q + (x < r ? x : r) + k;
 }
 
 template <int NT>
@@ -592,15 +593,17 @@ __device__ __forceinline__ void tile_prefix(const DecodeArgs& a, int block_size,
 template <class Core, class T, int D, int NW>
 __global__ __launch_bounds__(NW * kWave) void decode_balanced_kernel(DecodeArgs a, int block_size) {
   constexpr int H = Core::HEADS;
-  __shared__ typename Core::Smem sm;
   __shared__ int32_t s_cum[kBalancedMaxSeqs + 1];
   __shared__ int32_t s_part[NW * kWave];
+  __shared__ int32_t s_tbl[NW][kTblWin];
   const int S = a.num_seqs, C = a.head_chunks;
   tile_prefix<NW * kWave>(a, block_size, s_cum, s_part);
   if (blockIdx.x == 0)
     for (int s = threadIdx.x; s <= S; s += NW * kWave) a.ws_cum[s] = s_cum[s];
 
-  const int64_t W = gridDim.x, w = blockIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int64_t W = (int64_t)gridDim.x * NW;
+  const int64_t w = (int64_t)xcd_contiguous(blockIdx.x, gridDim.x) * NW + wave;
   const int64_t ntot = (int64_t)C * s_cum[S];
   int64_t f = range_start(w, ntot, W);
   const int64_t fb = range_start(w + 1, ntot, W);
@@ -622,10 +625,9 @@ __global__ __launch_bounds__(NW * kWave) void decode_balanced_kernel(DecodeArgs 
     const int n = (int)min((int64_t)(nt - t), fb - f);
     const int L = clamp_len(a, s, block_size);
     const int tok0 = t * kTile, tok1 = min((t + n) * kTile, L);
-    Core::run(a, sm, s, c * H, tok0, tok1);
-    const bool whole = t == 0 && t + n == nt;
     const size_t slot = 2 * (size_t)w + (first ? 0 : 1);
-    emit_rows<T, D, H, NW>(a, sm, s, c * H, whole, slot * H, 1);
+    const Dest dst{t == 0 && t + n == nt, slot * H, 1};
+    Core::run(a, s_tbl[wave], s, c * H, tok0, tok1, dst);
     first = false;
     f += n;
     t += n;
@@ -707,48 +709,97 @@ __global__ __launch_bounds__(kWave) void decode_merge_parts_kernel(DecodeArgs a,
   for (int e = 0; e < EPL; ++e) store_elem<T>(a.out, (size_t)row * D + e * kWave + lane, num[e] / den);
 }
 
-// Balanced mode, per (sequence, head group): the workgroups that shared its
-// tile range [A, B) are w_lo .. w_hi (w_lo: the last workgroup whose range
-// starts at or before A); workgroup w left its piece in slot
-// 2w + (its range starts at or after A ? 0 : 1).  Empty sequences get zeros.
+// Balanced mode, per (sequence, head group): the waves that shared its tile
+// range [A, B) are w_lo .. w_hi (w_lo: the last wave whose range starts at or
+// before A); wave w left its piece in slot 2w + (its range starts at or after
+// A ? 0 : 1), and waves with an empty range (more waves than tiles) wrote
+// nothing.  One workgroup per (sequence, head group), one wave per head: lane
+// p holds piece p (64 at a time) for the max and the sum, then all lanes walk
+// the pieces with slot and weight read from lane j (loads unrolled by 8),
+// each accumulating D/64 outputs.  Lanes without a piece point at w_lo's
+// piece (always written in this call) with weight 0, so nothing left in the
+// workspace by an earlier call is read.  Empty sequences get zeros.
+constexpr int kMergeWaves = 4;
+
 template <class T, int D, int H>
-__global__ __launch_bounds__(256) void decode_merge_balanced_kernel(DecodeArgs a, int block_size,
-                                                                    int nwg) {
+__global__ __launch_bounds__(kMergeWaves * kWave) void decode_merge_balanced_kernel(DecodeArgs a,
+                                                                                   int block_size,
+                                                                                   int nwaves) {
+  constexpr int EPL = D / kWave;
   const int C = a.head_chunks;
   const int s = blockIdx.x / C, c = blockIdx.x - (blockIdx.x / C) * C;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int L = clamp_len(a, s, block_size);
   const int nt = (L + kTile - 1) / kTile;
   const size_t orow = (size_t)s * a.num_q_heads + (size_t)c * H;
   if (nt == 0) {
-    for (int idx = threadIdx.x; idx < H * D; idx += blockDim.x) store_elem<T>(a.out, orow * D + idx, 0.f);
+    for (int idx = threadIdx.x; idx < H * D; idx += kMergeWaves * kWave)
+      store_elem<T>(a.out, orow * D + idx, 0.f);
     return;
   }
-  const int64_t W = nwg;
+  const int64_t W = nwaves;
   const int64_t ntot = (int64_t)C * a.ws_cum[a.num_seqs];
   const int64_t A = (int64_t)C * a.ws_cum[s] + (int64_t)c * nt, B = A + nt;
   const int64_t w_lo = ((A + 1) * W - 1) / ntot, w_hi = (B * W - 1) / ntot;
-  if (w_lo == w_hi) return;                 // one workgroup wrote it directly
-  // workgroups with an empty range (more workgroups than tiles) wrote nothing
-  for (int idx = threadIdx.x; idx < H * D; idx += blockDim.x) {
-    const int hh = idx / D, d = idx - (idx / D) * D;
+  if (w_lo == w_hi) return;                 // one wave wrote it directly
+  const int k = (int)(w_hi - w_lo + 1);
+  const int slot_lo = (int)(2 * w_lo + (range_start(w_lo, ntot, W) >= A ? 0 : 1));
+  auto piece_slot = [&](int p, bool& ok) {
+    const int64_t w = w_lo + p;
+    const int64_t ws = range_start(w, ntot, W);
+    ok = p < k && ws != range_start(w + 1, ntot, W);
+    return ok ? (int)(2 * w + (ws >= A ? 0 : 1)) : slot_lo;
+  };
+  for (int hh = wave; hh < H; hh += kMergeWaves) {
     float M = kNegInf;
-    for (int64_t w = w_lo; w <= w_hi; ++w) {
-      const int64_t ws = range_start(w, ntot, W);
-      if (ws == range_start(w + 1, ntot, W)) continue;
-      const size_t slot = 2 * (size_t)w + (ws >= A ? 0 : 1);
-      M = fmaxf(M, a.ws_m[slot * H + hh]);
+    for (int p0 = 0; p0 < k; p0 += kWave) {
+      bool ok;
+      const int slot = piece_slot(p0 + lane, ok);
+      M = fmaxf(M, a.ws_m[(size_t)slot * H + hh]);
     }
-    float num = 0.f, den = 0.f;
-    for (int64_t w = w_lo; w <= w_hi; ++w) {
-      const int64_t ws = range_start(w, ntot, W);
-      if (ws == range_start(w + 1, ntot, W)) continue;
-      const size_t slot = 2 * (size_t)w + (ws >= A ? 0 : 1);
-      const size_t r = slot * H + hh;
-      const float f = fast_exp2(a.ws_m[r] - M);
-      den = fmaf(f, a.ws_l[r], den);
-      num = fmaf(f, a.ws_o[r * D + d], num);
+    M = fmaxf(M, xor_lane<1>(M));
+    M = fmaxf(M, xor_lane<2>(M));
+    M = fmaxf(M, xor_lane<4>(M));
+    M = fmaxf(M, xor_lane<8>(M));
+    M = fmaxf(M, xor_lane<16>(M));
+    M = fmaxf(M, xor_lane<32>(M));
+    float den = 0.f, num[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) num[e] = 0.f;
+    for (int p0 = 0; p0 < k; p0 += kWave) {
+      bool ok;
+      const int slot = piece_slot(p0 + lane, ok);
+      const float wgt = ok ? fast_exp2(a.ws_m[(size_t)slot * H + hh] - M) : 0.f;
+      den = fmaf(wgt, a.ws_l[(size_t)slot * H + hh], den);
+      const int cnt = min(kWave, k - p0);
+      constexpr int U = 8;
+      for (int j0 = 0; j0 < cnt; j0 += U) {
+        float ov[U][EPL];
+        float wj[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int j = min(j0 + u, cnt - 1);
+          const int sj = __builtin_amdgcn_readlane(slot, j);
+          wj[u] = j0 + u < cnt ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wgt), j)) : 0.f;
+          const float* o = a.ws_o + ((size_t)sj * H + hh) * D + lane;
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) ov[u][e] = o[e * kWave];
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) num[e] = fmaf(wj[u], ov[u][e], num[e]);
+      }
     }
-    store_elem<T>(a.out, (orow + hh) * D + d, num / den);
+    den += xor_lane<1>(den);
+    den += xor_lane<2>(den);
+    den += xor_lane<4>(den);
+    den += xor_lane<8>(den);
+    den += xor_lane<16>(den);
+    den += xor_lane<32>(den);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) store_elem<T>(a.out, (orow + hh) * D + e * kWave + lane, num[e] / den);
   }
 }
 
@@ -758,26 +809,28 @@ __global__ __launch_bounds__(256) void decode_merge_balanced_kernel(DecodeArgs a
 #ifndef PA_WAVES_PER_UNIT
 #define PA_WAVES_PER_UNIT 4
 #endif
-constexpr int kWavesPerUnit = PA_WAVES_PER_UNIT;
+constexpr int kWavesPerGroup = PA_WAVES_PER_UNIT;
 
 template <class Core, class T, int D>
 static hipError_t run_core(const DecodeArgs& a, int bs, hipStream_t st) {
-  constexpr int NW = kWavesPerUnit;
+  constexpr int NW = kWavesPerGroup;
   constexpr int H = Core::HEADS;
   if (a.mode == kModeBalanced) {
     auto kern = decode_balanced_kernel<Core, T, D, NW>;
     int nwg = 0;
-    hipError_t e = balanced_grid(reinterpret_cast<const void*>(kern), NW * kWave, &nwg);
+    hipError_t e = balanced_grid(reinterpret_cast<const void*>(kern), NW * kWave, kBalancedMaxWaves / NW,
+                                 &nwg);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, dim3(nwg), dim3(NW * kWave), 0, st, a, bs);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((decode_merge_balanced_kernel<T, D, H>), dim3((uint32_t)a.num_seqs * a.head_chunks),
-                       dim3(256), 0, st, a, bs, nwg);
+                       dim3(kMergeWaves * kWave), 0, st, a, bs, nwg * NW);
     return hipGetLastError();
   }
-  const uint32_t units = (uint32_t)a.num_seqs * a.head_chunks * a.num_parts;
-  hipLaunchKernelGGL((decode_unit_kernel<Core, T, D, NW>), dim3(units), dim3(NW * kWave), 0, st, a, bs);
+  const uint64_t units = (uint64_t)a.num_seqs * a.head_chunks * a.num_parts;
+  const uint32_t groups = (uint32_t)((units + NW - 1) / NW);
+  hipLaunchKernelGGL((decode_unit_kernel<Core, T, D, NW>), dim3(groups), dim3(NW * kWave), 0, st, a, bs);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !a.split) return e;
   hipLaunchKernelGGL((decode_merge_parts_kernel<T, D>), dim3((uint32_t)a.num_seqs * a.num_q_heads),
@@ -787,24 +840,23 @@ static hipError_t run_core(const DecodeArgs& a, int bs, hipStream_t st) {
 
 template <class T, int D, int BS>
 static hipError_t dispatch_bs(const DecodeArgs& a, int group, hipStream_t st) {
-  constexpr int NW = kWavesPerUnit;
   if constexpr (!std::is_same<T, F32>::value) {
     switch (group) {
-      case 2: return run_core<MfmaCore<T, D, BS, 2, NW>, T, D>(a, BS, st);
-      case 4: return run_core<MfmaCore<T, D, BS, 4, NW>, T, D>(a, BS, st);
-      case 8: return run_core<MfmaCore<T, D, BS, 8, NW>, T, D>(a, BS, st);
-      case 16: return run_core<MfmaCore<T, D, BS, 16, NW>, T, D>(a, BS, st);
+      case 2: return run_core<MfmaCore<T, D, BS, 2>, T, D>(a, BS, st);
+      case 4: return run_core<MfmaCore<T, D, BS, 4>, T, D>(a, BS, st);
+      case 8: return run_core<MfmaCore<T, D, BS, 8>, T, D>(a, BS, st);
+      case 16: return run_core<MfmaCore<T, D, BS, 16>, T, D>(a, BS, st);
       default: break;   // group 1: VALU
     }
   }
   switch (a.num_q_heads / a.head_chunks) {
-    case 1: return run_core<ValuCore<T, D, BS, 1, NW>, T, D>(a, BS, st);
+    case 1: return run_core<ValuCore<T, D, BS, 1>, T, D>(a, BS, st);
     default: break;
   }
   if constexpr (std::is_same<T, F32>::value) {  // fp32 groups: 2 or 4 heads per unit
     switch (a.num_q_heads / a.head_chunks) {
-      case 2: return run_core<ValuCore<T, D, BS, 2, NW>, T, D>(a, BS, st);
-      case 4: return run_core<ValuCore<T, D, BS, 4, NW>, T, D>(a, BS, st);
+      case 2: return run_core<ValuCore<T, D, BS, 2>, T, D>(a, BS, st);
+      case 4: return run_core<ValuCore<T, D, BS, 4>, T, D>(a, BS, st);
       default: break;
     }
   }
