@@ -54,7 +54,7 @@ size_t balanced_ws_bytes(int32_t num_seqs, int32_t group, int32_t head_dim) {
 
 namespace pa {
 
-hipError_t balanced_grid(const void* kernel, int block_threads, int max_wg, int* nwg) {
+hipError_t balanced_grid(const void* kernel, int block_threads, int max_per_cu, int max_wg, int* nwg) {
   static std::mutex mu;
   static std::map<std::pair<const void*, int>, int> cache;
   int dev = 0;
@@ -71,7 +71,9 @@ hipError_t balanced_grid(const void* kernel, int block_threads, int max_wg, int*
   if (e != hipSuccess) return e;
   e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, block_threads, 0);
   if (e != hipSuccess) return e;
-  int n = cus * (per_cu > 0 ? per_cu : 1);
+  if (per_cu < 1) per_cu = 1;
+  if (max_per_cu > 0 && per_cu > max_per_cu) per_cu = max_per_cu;
+  int n = cus * per_cu;
   if (n > max_wg) n = max_wg;
   cache[{kernel, dev}] = n;
   *nwg = n;

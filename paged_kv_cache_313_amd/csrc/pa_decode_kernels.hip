@@ -38,6 +38,10 @@ constexpr int kTblWin = 256;   // block-table entries a wave stages in LDS at a 
 // by more than this (log2 units), so every p <= 2^8 and sums stay far from
 // fp32 overflow; the result is the same up to rounding.
 constexpr float kLazy = 8.f;
+// Tiles in flight per wave (tile_loop's ring): the current one and the next.
+// Rings of 3 and 4 (8 KiB tiles, fewer resident waves for their registers)
+// streamed no faster on the GQA batches.
+constexpr int kRing = 2;
 
 // Stage table entries [first, first+count) of one sequence into this wave's
 // LDS window (ids clamped into the pool: memory-safe on bad tables).  LDS
@@ -53,28 +57,33 @@ __device__ __forceinline__ void stage_table_wave(int32_t* tbl, const int32_t* ro
   __builtin_amdgcn_wave_barrier();
 }
 
-// Walk tiles 0 .. ntiles-1 keeping the next tile's K/V loads in flight while
-// the current one is computed.  The loop runs over pairs of tiles with
-// ping-pong buffers and has a single exit, so that no path (not even a
-// structurized, never-taken one) returns to the loop head with the prefetch
-// outstanding; that lets the compiler's vmcnt waits leave the newer loads in
-// flight.  Loads are unconditional: a prefetch past the last tile re-reads it
-// (an L2 hit) instead of branching.
-template <class Buf, class Load, class Compute>
+// Walk tiles 0 .. ntiles-1 keeping the next NB-1 tiles' K/V loads in flight
+// while the current one is computed.  The loop runs over NB tiles at a time
+// with a ring of NB buffers and has a single exit, so that no path (not even
+// a structurized, never-taken one) returns to the loop head with the
+// prefetches outstanding; that lets the compiler's vmcnt waits leave the newer
+// loads in flight.  Loads are unconditional: a prefetch past the last tile
+// re-reads it (an L2 hit) instead of branching.  After the loop fewer than NB
+// tiles remain, and they are exactly the ones already in buf[0 ..].
+template <class Buf, int NB = 2, class Load, class Compute>
 __device__ __forceinline__ void tile_loop(int ntiles, Load&& load, Compute&& compute) {
+  static_assert(NB >= 2, "ring");
   if (ntiles <= 0) return;
   const int last = ntiles - 1;
-  Buf a, b;
+  Buf buf[NB];
+#pragma unroll
+  for (int j = 0; j + 1 < NB; ++j) load(min(j, last), buf[j]);
   int ti = 0;
-  load(0, a);
-  for (int k = 0; k + 2 <= ntiles; k += 2) {
-    load(min(ti + 1, last), b);
-    compute(ti, a);
-    load(min(ti + 2, last), a);
-    compute(ti + 1, b);
-    ti += 2;
+  for (; ti + NB <= ntiles; ti += NB) {
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      load(min(ti + j + NB - 1, last), buf[(j + NB - 1) % NB]);
+      compute(ti + j, buf[j]);
+    }
   }
-  if (ntiles & 1) compute(ti, a);
+#pragma unroll
+  for (int j = 0; j + 1 < NB; ++j)
+    if (ti + j < ntiles) compute(ti + j, buf[j]);
 }
 
 // Byte offsets, from the start of a KV head's slice of the pool, of the
@@ -159,6 +168,7 @@ struct ValuCore {
   static constexpr int NE = 16 / EB;      // elements per 16 bytes
   static constexpr int DPL = NL * NE;     // elements per lane (= D / 4)
   static constexpr int HEADS = H;
+  static constexpr int kBalancedWgPerCu = 0;  // as many as stay resident
   static_assert(DPL * 4 == D, "layout");
   static_assert(kTblWin * BS % kTile == 0, "window");
   // bytes a tile's buffer resource spans: its 16 rows (8 per block at block_size 8)
@@ -257,7 +267,7 @@ struct ValuCore {
           for (int hh = 0; hh < H; ++hh) Axpy16<T>::run(pr[hh], vj, &acc[hh][j * NE]);
         }
       };
-      tile_loop<ValuBuf<NL>>((we - wb + kTile - 1) / kTile, load, compute);
+      tile_loop<ValuBuf<NL>, kRing>((we - wb + kTile - 1) / kTile, load, compute);
       wb = we;
     }
 
@@ -351,6 +361,11 @@ struct MfmaCore {
   static constexpr int CPR = D / 8;    // 16-byte chunks per token row
   static constexpr int NVI = D / 32;   // V chunks per lane per tile (16 * CPR / 64)
   static constexpr int HEADS = G;
+  // Balanced grid: one workgroup per CU.  With 8 KiB tiles and one tile
+  // prefetched per wave, more resident waves only add concurrent streams: on
+  // the Llama-3-8B-shaped batch 1 workgroup per CU streamed 1-2 % faster than
+  // 2 or 3, and equal on the long-context batch.
+  static constexpr int kBalancedWgPerCu = 1;
   static_assert(16 % G == 0 && G >= 2, "group");
   static_assert(kTblWin * BS % kTile == 0, "window");
   static constexpr uint32_t kTileBytes = (BS >= 16 ? kTile : BS) * ROWB;
@@ -468,7 +483,7 @@ struct MfmaCore {
           }
         }
       };
-      tile_loop<MfmaBuf<NQK, NVI>>((we - wb + kTile - 1) / kTile, load, compute);
+      tile_loop<MfmaBuf<NQK, NVI>, kRing>((we - wb + kTile - 1) / kTile, load, compute);
       wb = we;
     }
 
@@ -818,8 +833,8 @@ static hipError_t run_core(const DecodeArgs& a, int bs, hipStream_t st) {
   if (a.mode == kModeBalanced) {
     auto kern = decode_balanced_kernel<Core, T, D, NW>;
     int nwg = 0;
-    hipError_t e = balanced_grid(reinterpret_cast<const void*>(kern), NW * kWave, kBalancedMaxWaves / NW,
-                                 &nwg);
+    hipError_t e = balanced_grid(reinterpret_cast<const void*>(kern), NW * kWave, Core::kBalancedWgPerCu,
+                                 kBalancedMaxWaves / NW, &nwg);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, dim3(nwg), dim3(NW * kWave), 0, st, a, bs);
     e = hipGetLastError();

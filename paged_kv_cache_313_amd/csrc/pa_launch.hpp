@@ -20,8 +20,9 @@ hipError_t launch_block_copy(void* k_pool, void* v_pool, const int32_t* block_ma
                              hipStream_t stream);
 
 // Workgroups of `kernel` (block of `block_threads`) that the current device
-// keeps resident at once, capped at max_wg; cached per kernel/device.
-hipError_t balanced_grid(const void* kernel, int block_threads, int max_wg, int* nwg);
+// keeps resident at once, at most max_per_cu per compute unit (0: no cap) and
+// max_wg in all; cached per kernel/device.
+hipError_t balanced_grid(const void* kernel, int block_threads, int max_per_cu, int max_wg, int* nwg);
 
 // Decode: the segment kernel of the chosen mode plus, when results are split,
 // its merge kernel.  f16/bf16 with group size 2..16 run the MFMA core, all
