@@ -1,0 +1,172 @@
+"""Reference KV block manager (pure Python).
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import, call or
+execute this module: only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` use it.  It shares no code with the
+native block manager in libpagedkv.
+
+What it models, and where the pages define it:
+
+* One global allocator owns the physical blocks of the KV pool, like an MMU
+  owns page frames (paged-KV analysis page, section 2.3, the component table:
+  KV block manager).
+* Every sequence has its own block table that maps logical block j (tokens
+  [j * block_size, (j + 1) * block_size)) to a physical block (same table,
+  "Block Table"; section 2.2).
+* Blocks are taken only when a sequence needs one, so only a sequence's last
+  block can be partly filled (vLLM entity page, "what it is").
+* Parallel samples, beams and common prompts share physical blocks through
+  reference counts; a sequence about to write into a block that other
+  sequences still reference first gets its own copy -- copy-on-write (vLLM
+  entity page, "what it is"; paged-KV analysis page, section 3.2, the
+  copy-on-write paragraph).
+* A finished request gives its blocks back at once (paged-KV analysis page,
+  section 3.3, continuous batching).
+* Effective utilisation = sum of sequence lengths / (blocks in use * block
+  size) (paged-KV analysis page, section 4.2).
+
+Readings where the pages are silent:
+
+* Allocation order: the lowest-numbered free block is taken first.  Any order
+  is correct; fixing one makes two implementations comparable bit for bit.
+* fork(parent) creates a sequence with the parent's length and a copy of its
+  table; every block of the table gains one reference.  This is how parallel
+  sampling and beam search share a prompt.
+* append_slots(seqs, counts) reserves counts[i] new token positions at the end
+  of sequence seqs[i], for i in order.  For each position p = current length:
+    - p % block_size == 0: a fresh block is appended to the table;
+    - else, if the last block has more than one reference: copy-on-write --
+      a fresh block replaces it in this table, the pair (old, fresh) is
+      emitted, and the old block loses one reference;
+    - the slot emitted is table[p // block_size] * block_size + p % block_size.
+  The copies must be applied (pre-call state) before the appends are written;
+  a sequence later in the same batch that still shares the old block then
+  finds it with fewer references.  A batch is all-or-nothing: if the free
+  blocks do not cover it, nothing changes and OutOfBlocks is raised.
+* free_sequence drops one reference from every block of the table; blocks
+  left with none return to the free pool.
+"""
+
+from __future__ import annotations
+
+import copy
+import heapq
+from fractions import Fraction
+
+
+class OutOfBlocks(RuntimeError):
+    pass
+
+
+class UnknownSequence(KeyError):
+    pass
+
+
+class BlockManager:
+    def __init__(self, num_blocks: int, block_size: int):
+        if num_blocks <= 0 or block_size <= 0:
+            raise ValueError("num_blocks and block_size must be positive")
+        self.num_blocks = num_blocks
+        self.block_size = block_size
+        self.ref = [0] * num_blocks
+        self.free = list(range(num_blocks))      # a heap: lowest id on top
+        heapq.heapify(self.free)
+        self.seqs: dict[int, dict] = {}
+        self.next_id = 0
+
+    # -- sequences ---------------------------------------------------------
+    def add_sequence(self) -> int:
+        sid = self.next_id
+        self.next_id += 1
+        self.seqs[sid] = {"table": [], "len": 0}
+        return sid
+
+    def _seq(self, sid: int) -> dict:
+        if sid not in self.seqs:
+            raise UnknownSequence(sid)
+        return self.seqs[sid]
+
+    def fork(self, parent: int) -> int:
+        p = self._seq(parent)
+        sid = self.next_id
+        self.next_id += 1
+        self.seqs[sid] = {"table": list(p["table"]), "len": p["len"]}
+        for b in p["table"]:
+            self.ref[b] += 1
+        return sid
+
+    def free_sequence(self, sid: int) -> None:
+        s = self._seq(sid)
+        for b in s["table"]:
+            self.ref[b] -= 1
+            if self.ref[b] == 0:
+                heapq.heappush(self.free, b)
+        del self.seqs[sid]
+
+    def length(self, sid: int) -> int:
+        return self._seq(sid)["len"]
+
+    # -- allocation --------------------------------------------------------
+    def _take(self) -> int:
+        if not self.free:
+            raise OutOfBlocks()
+        b = heapq.heappop(self.free)
+        self.ref[b] = 1
+        return b
+
+    def append_slots(self, seqs, counts):
+        """Returns (slots, cow_pairs): one slot per new token in batch order,
+        and the (src, dst) copies to apply before writing them."""
+        if len(seqs) != len(counts):
+            raise ValueError("seqs and counts differ in length")
+        for sid, n in zip(seqs, counts):
+            self._seq(sid)
+            if n < 0:
+                raise ValueError("negative token count")
+        saved = (copy.deepcopy(self.seqs), list(self.ref), list(self.free))
+        slots, pairs = [], []
+        try:
+            for sid, n in zip(seqs, counts):
+                s = self.seqs[sid]
+                for _ in range(n):
+                    p = s["len"]
+                    j, o = divmod(p, self.block_size)
+                    if o == 0:
+                        s["table"].append(self._take())
+                    elif self.ref[s["table"][j]] > 1:
+                        old = s["table"][j]
+                        fresh = self._take()
+                        self.ref[old] -= 1
+                        s["table"][j] = fresh
+                        pairs.append((old, fresh))
+                    slots.append(s["table"][j] * self.block_size + o)
+                    s["len"] = p + 1
+        except OutOfBlocks:
+            self.seqs, self.ref, self.free = saved
+            raise
+        return slots, pairs
+
+    # -- read-outs ---------------------------------------------------------
+    def block_tables(self, seqs, max_blocks_per_seq: int):
+        """Padded tables (-1 past each sequence's last block) and lengths."""
+        tables, lens = [], []
+        for sid in seqs:
+            s = self._seq(sid)
+            if len(s["table"]) > max_blocks_per_seq:
+                raise ValueError("max_blocks_per_seq too small")
+            tables.append(s["table"] + [-1] * (max_blocks_per_seq - len(s["table"])))
+            lens.append(s["len"])
+        return tables, lens
+
+    def num_free_blocks(self) -> int:
+        return len(self.free)
+
+    def blocks_in_use(self) -> int:
+        return self.num_blocks - len(self.free)
+
+    def utilisation(self) -> Fraction:
+        """Tokens held by live sequences over token slots of the blocks in use
+        (a shared block's tokens count once per sequence that reads them)."""
+        used = self.blocks_in_use()
+        total = sum(s["len"] for s in self.seqs.values())
+        return Fraction(total, used * self.block_size) if used else Fraction(0)
