@@ -188,6 +188,41 @@ def traffic_from_profile(config, partition):
     return c.get("hbm_bytes_per_launch")
 
 
+def block_manager_leg(b, steps: int) -> dict:
+    """Host cost of the native block manager for this batch's decode step:
+    every sequence reserves one new slot (append_slots) and the batch's block
+    tables are emitted (block_tables), through the Python binding."""
+    import numpy as np
+
+    import paged_kv_cache_313_amd as P
+
+    S, bs = b.num_seqs, b.block_size
+    lens = b.context_lens.astype(np.int64)
+    need = int(((lens + steps + 1 + bs - 1) // bs).sum())
+    bm = P.BlockManager(need + S, bs)
+    ids = np.array([bm.add_sequence() for _ in range(S)], dtype=np.int64)
+    t = time.perf_counter()
+    bm.append_slots(ids, lens.astype(np.int32))          # the batch's existing context
+    t_fill = time.perf_counter() - t
+    ones = np.ones(S, dtype=np.int32)
+    mb = int((lens.max() + steps + bs) // bs) + 1
+    t_app, t_tab = [], []
+    for _ in range(steps):
+        t0 = time.perf_counter()
+        bm.append_slots(ids, ones)
+        t1 = time.perf_counter()
+        bm.block_tables(ids, mb)
+        t2 = time.perf_counter()
+        t_app.append(t1 - t0)
+        t_tab.append(t2 - t1)
+    bm.close()
+    return {"seqs": S, "append_slots_us": 1e6 * float(np.median(t_app)),
+            "block_tables_us": 1e6 * float(np.median(t_tab)),
+            "fill_context_ms": 1e3 * t_fill, "steps": steps,
+            "what": "median host time per decode step of pa_bm_append_slots (1 token per sequence) and "
+                    "pa_bm_block_tables (padded int32 tables), Python binding included"}
+
+
 def main():
     args = parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -274,6 +309,8 @@ def main():
     alg_bytes, kv_bytes = algorithmic_bytes(b)
     achieved = alg_bytes / (dec_ms * 1e-3) / 1e9
 
+    bm_leg = block_manager_leg(b, max(args.steps, 10))
+
     # parity of this run's output against the oracle run above (all sequences)
     parity = None
     if cpu_out is not None:
@@ -316,6 +353,7 @@ def main():
                      "algorithmic_bytes_per_launch": alg_bytes},
         "cpu_baseline": cpu,
         "parity": parity,
+        "block_manager": bm_leg,
     }
     print(json.dumps(line), flush=True)
 

@@ -60,7 +60,10 @@ typedef enum {
   PA_ERR_PARTITION = 5,   /* partition_size invalid (see pa_decode_attention)       */
   PA_ERR_WORKSPACE = 6,   /* workspace missing or smaller than required        */
   PA_ERR_HIP = 7,         /* a kernel launch failed; see pa_last_hip_error()   */
-  PA_ERR_ALIGN = 8        /* a data pointer is not 16-byte aligned             */
+  PA_ERR_ALIGN = 8,       /* a data pointer is not 16-byte aligned             */
+  PA_ERR_NO_BLOCKS = 9,   /* block manager: the free blocks do not cover a batch */
+  PA_ERR_SEQUENCE = 10,   /* block manager: a sequence id that is not live     */
+  PA_ERR_CAPACITY = 11    /* block manager: a caller's output buffer is too small */
 } pa_status;
 
 typedef enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype;

@@ -1,9 +1,10 @@
 """paged_kv_cache_313_amd -- PagedAttention's decode hot path for AMD MI355X.
 
-Thin Python binding over ``libpagedkv.so`` (C ABI in ``include/pa.h``).  The
-functions here only marshal torch device tensors into pointers and sizes and
-pass the current HIP stream; every step of the path runs in the library's HIP
-kernels.  There is no CPU or PyTorch fallback: if the library is missing or a
+Thin Python binding over ``libpagedkv.so`` (C ABI in ``include/pa.h`` and
+``include/pa_block_manager.h``).  The functions here only marshal torch device
+tensors into pointers and sizes and pass the current HIP stream; every step of
+the path runs in the library's HIP kernels, and block allocation in its native
+block manager (``BlockManager``).  There is no CPU or PyTorch fallback: if the library is missing or a
 tensor is not on the GPU, the call raises.
 """
 
@@ -15,9 +16,10 @@ import torch
 
 from . import _lib
 from ._lib import PA_PARTITION_BALANCED, PagedKVError, load  # noqa: F401
+from .block_manager import BlockManager  # noqa: F401
 
 __all__ = ["kv_append", "block_copy", "decode_attention", "decode_workspace_bytes",
-           "choose_partition", "PagedKVError", "load", "PA_PARTITION_BALANCED"]
+           "choose_partition", "PagedKVError", "load", "PA_PARTITION_BALANCED", "BlockManager"]
 
 _DTYPES = {torch.float32: _lib.PA_F32, torch.float16: _lib.PA_F16, torch.bfloat16: _lib.PA_BF16}
 

@@ -95,6 +95,9 @@ PA_EXPORT const char* pa_status_string(pa_status s) {
     case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE: workspace missing or too small";
     case PA_ERR_HIP: return "PA_ERR_HIP: a HIP launch failed (see pa_last_hip_error)";
     case PA_ERR_ALIGN: return "PA_ERR_ALIGN: data pointers must be 16-byte aligned";
+    case PA_ERR_NO_BLOCKS: return "PA_ERR_NO_BLOCKS: not enough free blocks for the batch";
+    case PA_ERR_SEQUENCE: return "PA_ERR_SEQUENCE: no live sequence has this id";
+    case PA_ERR_CAPACITY: return "PA_ERR_CAPACITY: an output buffer is too small";
   }
   return "unknown pa_status";
 }

@@ -1,0 +1,96 @@
+"""Serving steps driven by the native block manager: prompts are written,
+samples forked, every sample decodes a token per step (copy-on-write copies,
+appends, attention over the manager's tables), samples finish and new requests
+reuse their blocks.  Each step the manager's outputs equal the reference
+manager's, and the GPU pools and outputs equal the oracle's (pools bit for
+bit, attention within the bf16 bound)."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.pa_oracle as O
+import paged_kv_cache_313_amd as P
+from oracle.block_manager import BlockManager as RefBM
+from workloads import synth as W
+from workloads import torch_io
+
+from gpu_util import check_close, gpu_out_f64, note
+
+pytestmark = pytest.mark.gpu
+
+DT = "bf16"
+
+
+def draw(rng, shape):
+    return W.to_storage(rng.standard_normal(shape, dtype=np.float32), DT)
+
+
+@pytest.mark.parametrize("bs,partition", [(16, -1), (8, 0), (32, 64)])
+def test_manager_driven_decode_steps(bs, partition):
+    rng = np.random.default_rng(3130 + bs)
+    NB, Hkv, G, D = 160, 2, 4, 128
+    Hq = Hkv * G
+    scale = W.default_scale(D)
+    nat, ref = P.BlockManager(NB, bs), RefBM(NB, bs)
+    k_host = W.poison_array((NB, Hkv, bs, D), DT)
+    v_host = W.poison_array((NB, Hkv, bs, D), DT)
+    k_dev = torch_io.storage_to_torch(k_host, DT, "cuda")
+    v_dev = torch_io.storage_to_torch(v_host, DT, "cuda")
+
+    def step(seqs, counts):
+        slots, pairs = nat.append_slots(seqs, counts)
+        want = ref.append_slots(seqs, counts)
+        assert slots.tolist() == want[0] and [tuple(p) for p in pairs.tolist()] == want[1]
+        n = len(slots)
+        key, val = draw(rng, (n, Hkv, D)), draw(rng, (n, Hkv, D))
+        if len(pairs):
+            P.block_copy(k_dev, v_dev, torch.from_numpy(pairs).cuda())
+            O.block_copy(k_host, v_host, pairs)
+        if n:
+            P.kv_append(torch_io.storage_to_torch(key, DT, "cuda"), torch_io.storage_to_torch(val, DT, "cuda"),
+                        k_dev, v_dev, torch.from_numpy(slots).cuda())
+            O.kv_append(k_host, v_host, key, val, slots, bs)
+
+    def decode(seqs, label):
+        mb = max(len(ref.seqs[s]["table"]) for s in seqs)
+        tables, lens = nat.block_tables(seqs, mb)
+        q = draw(rng, (len(seqs), Hq, D))
+        note(f"block manager bs={bs} P={partition} {label}")
+        out = P.decode_attention(torch_io.storage_to_torch(q, DT, "cuda"), k_dev, v_dev,
+                                 torch.from_numpy(tables).cuda(), torch.from_numpy(lens).cuda(), scale,
+                                 int(lens.max()), partition)
+        torch.cuda.synchronize()
+        want = O.decode_attention(q, k_host, v_host, tables, lens, scale, bs, DT)
+        check_close(gpu_out_f64(out, DT), want, DT, label)
+
+    prompts = []
+    for plen in (37, 40, 13):                   # partly filled last blocks, and one full
+        s = nat.add_sequence()
+        assert ref.add_sequence() == s
+        prompts.append((s, plen))
+    step([s for s, _ in prompts], [n for _, n in prompts])
+    live = []
+    for s, _ in prompts:
+        live.append(s)
+        for _ in range(2):
+            c = nat.fork(s)
+            assert ref.fork(s) == c
+            live.append(c)
+    for t in range(12):
+        step(live, [1] * len(live))
+        decode(live, f"step {t}")
+        if t == 5:                              # two samples finish, a new request arrives
+            done = (live[1], live[4])
+            for s in done:
+                nat.free_sequence(s)
+                ref.free_sequence(s)
+            live = [s for s in live if s not in done]
+            s = nat.add_sequence()
+            assert ref.add_sequence() == s
+            step([s], [29])
+            live.append(s)
+        assert nat.refcounts().tolist() == ref.ref
+    torch.cuda.synchronize()
+    assert torch_io.torch_to_storage(k_dev, DT).tobytes() == k_host.tobytes()
+    assert torch_io.torch_to_storage(v_dev, DT).tobytes() == v_host.tobytes()
