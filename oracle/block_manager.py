@@ -45,6 +45,15 @@ Readings where the pages are silent:
   blocks do not cover it, nothing changes and OutOfBlocks is raised.
 * free_sequence drops one reference from every block of the table; blocks
   left with none return to the free pool.
+* Preemption evicts all of a request's blocks at once (Cross-Paper Synthesis
+  page, section 3, the preemption item).  swap_out(seq) returns the table's
+  blocks in table order -- the caller copies them to host memory before
+  anything else writes them -- drops one reference from each, and leaves the
+  sequence swapped: it keeps its length but holds no block, and only
+  swap_in or free_sequence may name it.  swap_in(seq) takes as many fresh
+  blocks as it held (lowest first, all-or-nothing) and returns them in table
+  order; the caller copies the host data into them.  Blocks it shared before
+  come back as private copies.  Utilisation counts resident sequences only.
 """
 
 from __future__ import annotations
@@ -59,7 +68,8 @@ class OutOfBlocks(RuntimeError):
 
 
 class UnknownSequence(KeyError):
-    pass
+    """No live sequence has this id, or it is swapped out where a resident
+    one is needed (and the other way round)."""
 
 
 class BlockManager:
@@ -71,7 +81,8 @@ class BlockManager:
         self.ref = [0] * num_blocks
         self.free = list(range(num_blocks))      # a heap: lowest id on top
         heapq.heapify(self.free)
-        self.seqs: dict[int, dict] = {}
+        self.seqs: dict[int, dict] = {}        # resident sequences
+        self.swapped: dict[int, dict] = {}     # swapped out: length and block count
         self.next_id = 0
 
     # -- sequences ---------------------------------------------------------
@@ -82,6 +93,7 @@ class BlockManager:
         return sid
 
     def _seq(self, sid: int) -> dict:
+        """A resident sequence."""
         if sid not in self.seqs:
             raise UnknownSequence(sid)
         return self.seqs[sid]
@@ -95,16 +107,44 @@ class BlockManager:
             self.ref[b] += 1
         return sid
 
-    def free_sequence(self, sid: int) -> None:
-        s = self._seq(sid)
-        for b in s["table"]:
+    def _drop(self, table) -> None:
+        for b in table:
             self.ref[b] -= 1
             if self.ref[b] == 0:
                 heapq.heappush(self.free, b)
+
+    def free_sequence(self, sid: int) -> None:
+        if sid in self.swapped:
+            del self.swapped[sid]
+            return
+        s = self._seq(sid)
+        self._drop(s["table"])
         del self.seqs[sid]
 
     def length(self, sid: int) -> int:
+        if sid in self.swapped:
+            return self.swapped[sid]["len"]
         return self._seq(sid)["len"]
+
+    # -- preemption ----------------------------------------------------------
+    def swap_out(self, sid: int) -> list:
+        s = self._seq(sid)
+        ids = list(s["table"])
+        self._drop(ids)
+        del self.seqs[sid]
+        self.swapped[sid] = {"len": s["len"], "nblocks": len(ids)}
+        return ids
+
+    def swap_in(self, sid: int) -> list:
+        if sid not in self.swapped:
+            raise UnknownSequence(sid)
+        w = self.swapped[sid]
+        if len(self.free) < w["nblocks"]:
+            raise OutOfBlocks()
+        ids = [self._take() for _ in range(w["nblocks"])]
+        del self.swapped[sid]
+        self.seqs[sid] = {"table": ids, "len": w["len"]}
+        return ids
 
     # -- allocation --------------------------------------------------------
     def _take(self) -> int:

@@ -31,6 +31,10 @@ What it computes, and where the pages define it:
 * Partitioned decode -- the same attention evaluated per 512-token slice and
   merged by the log-sum-exp rescale (not on the pages; it is the split that
   long contexts need).  Exactly equal to the dense result up to rounding.
+* Swap out / swap in -- preemption evicts all blocks of a request to host
+  memory and brings them back later (Cross-Paper Synthesis page, section 3);
+  the host copy is block-first (vLLM entity page, key observations).  Byte
+  copies.
 * Utilisation readout -- effective memory utilisation = sum of sequence
   lengths / (allocated blocks * page size) (paged-KV analysis page, section
   4.2).
@@ -103,6 +107,31 @@ def block_copy(k_pool: np.ndarray, v_pool: np.ndarray, block_mapping: np.ndarray
     for src, dst in pairs:
         k_pool[int(dst)] = k_src[int(src)]
         v_pool[int(dst)] = v_src[int(src)]
+
+
+def swap_out(k_pool: np.ndarray, v_pool: np.ndarray, block_ids, host: np.ndarray) -> None:
+    """Preemption moves every block of a request out of HBM at once
+    (Cross-Paper Synthesis page, section 3, the preemption item).  The host
+    copy is block-first -- entry i holds block block_ids[i]'s K tile then its V
+    tile, so one request's KV is one contiguous run (vLLM entity page, key
+    observations: block-first layout for KV movement).  host has shape
+    [n, 2, Hkv, block_size, D]; entries whose id is outside the pool are left
+    as they are."""
+    ids = np.asarray(block_ids, dtype=np.int64).reshape(-1)
+    for i, b in enumerate(ids):
+        if 0 <= b < k_pool.shape[0]:
+            host[i, 0] = k_pool[b]
+            host[i, 1] = v_pool[b]
+
+
+def swap_in(host: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray, block_ids) -> None:
+    """The way back: block block_ids[i] of both pools receives entry i of the
+    block-first host copy (ids outside the pool are skipped)."""
+    ids = np.asarray(block_ids, dtype=np.int64).reshape(-1)
+    for i, b in enumerate(ids):
+        if 0 <= b < k_pool.shape[0]:
+            k_pool[b] = host[i, 0]
+            v_pool[b] = host[i, 1]
 
 
 # ----------------------------------------------------------------------------

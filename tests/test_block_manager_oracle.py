@@ -28,6 +28,7 @@ class World:
         self.bm = bm
         self.pool = np.full((bm.num_blocks, bm.block_size), -1, dtype=np.int64)
         self.hist = {}
+        self.host = {}        # swapped-out sequences' blocks, block-first
         self.next_token = 0
 
     def add(self):
@@ -43,6 +44,17 @@ class World:
     def free(self, sid):
         self.bm.free_sequence(sid)
         del self.hist[sid]
+        self.host.pop(sid, None)
+
+    def swap_out(self, sid):
+        ids = self.bm.swap_out(sid)
+        self.host[sid] = self.pool[ids].copy()       # before anything reuses the blocks
+        return ids
+
+    def swap_in(self, sid):
+        ids = self.bm.swap_in(sid)
+        self.pool[ids] = self.host.pop(sid)
+        return ids
 
     def append(self, seqs, counts):
         before = {b: self.bm.ref[b] for b in range(self.bm.num_blocks)}
@@ -72,6 +84,10 @@ class World:
         bm = self.bm
         count = [0] * bm.num_blocks
         for sid, h in self.hist.items():
+            if sid in self.host:
+                assert sid in bm.swapped and sid not in bm.seqs and bm.length(sid) == len(h)
+                assert len(self.host[sid]) == -(-len(h) // bm.block_size)
+                continue
             s = bm.seqs[sid]
             assert s["len"] == len(h)
             assert len(s["table"]) == -(-len(h) // bm.block_size)
@@ -81,19 +97,28 @@ class World:
             assert got == h, f"sequence {sid} reads back other tokens"
         assert count == bm.ref, "reference counts differ from table membership"
         assert sorted(bm.free) == [b for b in range(bm.num_blocks) if count[b] == 0]
-        assert set(bm.seqs) == set(self.hist)
+        assert set(bm.seqs) | set(bm.swapped) == set(self.hist)
+        assert not set(bm.seqs) & set(bm.swapped)
 
 
-def random_ops(world, rng, steps, max_batch=6, max_tokens=40):
+def random_ops(world, rng, steps, max_batch=6, max_tokens=40, swaps=True):
     for _ in range(steps):
-        live = sorted(world.hist)
+        live = sorted(s for s in world.hist if s not in world.host)
+        out = sorted(world.host)
         r = rng.random()
         if not live or r < 0.15:
             world.add()
         elif r < 0.30:
             world.fork(rng.choice(live))
         elif r < 0.40 and len(live) > 1:
-            world.free(rng.choice(live))
+            world.free(rng.choice(live + out))
+        elif swaps and r < 0.47:
+            world.swap_out(rng.choice(live))
+        elif swaps and r < 0.54 and out:
+            try:
+                world.swap_in(rng.choice(out))
+            except OutOfBlocks:
+                pass
         else:
             seqs = rng.sample(live, min(len(live), rng.randint(1, max_batch)))
             counts = [rng.choice([0, 1, 1, 1, rng.randint(1, max_tokens)]) for _ in seqs]
@@ -228,10 +253,20 @@ class LeakyCopyBM(BlockManager):
 
 class KeepOnFreeBM(BlockManager):
     def free_sequence(self, sid):
-        del self.seqs[sid]                         # never gives blocks back
+        if sid in self.seqs:
+            del self.seqs[sid]                     # never gives blocks back
+        else:
+            super().free_sequence(sid)
 
 
-@pytest.mark.parametrize("cls", [NoCopyBM, LeakyCopyBM, KeepOnFreeBM])
+class ReversedSwapInBM(BlockManager):
+    def swap_in(self, sid):
+        ids = super().swap_in(sid)
+        self.seqs[sid]["table"] = ids[::-1]      # table order lost on the way back
+        return ids
+
+
+@pytest.mark.parametrize("cls", [NoCopyBM, LeakyCopyBM, KeepOnFreeBM, ReversedSwapInBM])
 def test_planted_mistakes_are_caught(cls):
     caught = False
     for seed in range(10):
@@ -242,3 +277,35 @@ def test_planted_mistakes_are_caught(cls):
             caught = True
             break
     assert caught
+
+
+def test_swap_round_trip_and_errors():
+    world = World(BlockManager(16, 4))
+    a = world.add()
+    world.append([a], [10])                       # 3 blocks
+    b = world.fork(a)
+    ids = world.swap_out(a)
+    assert ids == [0, 1, 2] and world.bm.num_free_blocks() == 16 - 3   # b still holds them
+    world.check()
+    with pytest.raises(UnknownSequence):
+        world.bm.append_slots([a], [1])
+    with pytest.raises(UnknownSequence):
+        world.bm.fork(a)
+    world.append([b], [1])                        # b now owns block 2 alone: no copy
+    back = world.swap_in(a)
+    assert back == [3, 4, 5]                      # private copies, lowest first
+    world.check()
+    world.free(b)
+    world.append([a], [3])
+    world.check()
+    # all-or-nothing: not enough blocks to come back
+    c = world.add()
+    world.append([c], [40])                       # 10 blocks: 3 + 10 of 16
+    world.swap_out(a)
+    d = world.add()
+    world.append([d], [4 * 5])                    # 5 blocks: 15 of 16 used
+    with pytest.raises(OutOfBlocks):
+        world.swap_in(a)
+    world.check()
+    world.free(a)                                 # a swapped sequence can be dropped
+    world.check()

@@ -400,3 +400,46 @@ def test_planted_mistakes_are_caught(monkeypatch):
     with monkeypatch.context() as m:
         m.setattr(O, "gather_tokens_fast", shifted)
         assert _fails(check)
+
+
+# -- swap out / swap in -------------------------------------------------------
+
+def _pools(seed=0, nb=12, hkv=2, bs=4, d=8):
+    rng = np.random.default_rng(seed)
+    k = rng.standard_normal((nb, hkv, bs, d))
+    v = rng.standard_normal((nb, hkv, bs, d))
+    return k, v
+
+
+def test_swap_out_layout_is_block_first():
+    k, v = _pools()
+    ids = [7, 2, 9]
+    host = np.zeros((3, 2) + k.shape[1:])
+    O.swap_out(k, v, ids, host)
+    flat = host.reshape(3, -1)
+    for i, b in enumerate(ids):   # one contiguous run per block: its K tile, then its V tile
+        assert np.array_equal(flat[i], np.concatenate([k[b].ravel(), v[b].ravel()]))
+
+
+def test_swap_round_trip_equals_block_copy():
+    k, v = _pools(1)
+    k2, v2 = k.copy(), v.copy()
+    src, dst = [3, 0, 8], [5, 11, 1]
+    host = np.zeros((3, 2) + k.shape[1:])
+    O.swap_out(k, v, src, host)
+    O.swap_in(host, k, v, dst)
+    O.block_copy(k2, v2, np.array(list(zip(src, dst))))
+    assert np.array_equal(k, k2) and np.array_equal(v, v2)
+
+
+def test_swap_in_restores_clobbered_blocks_and_skips_bad_ids():
+    k, v = _pools(2)
+    k0, v0 = k.copy(), v.copy()
+    ids = [4, 6, -1, 99]
+    host = np.full((4, 2) + k.shape[1:], 7.0)
+    O.swap_out(k, v, ids, host)
+    assert (host[2:] == 7.0).all()                # out-of-pool ids leave their entries
+    k[[4, 6]] = np.nan
+    v[[4, 6]] = np.nan
+    O.swap_in(host, k, v, ids)
+    assert np.array_equal(k, k0) and np.array_equal(v, v0)
