@@ -51,6 +51,7 @@ def parse_args():
     ap.add_argument("--partition", type=int, default=None, help="partition size (default: library choice)")
     ap.add_argument("--table-layout", default="shuffled", choices=["shuffled", "identity"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-swap", action="store_true", help="skip the swap (preemption traffic) leg")
     ap.add_argument("--cpu-seconds", type=float, default=8.0, help="minimum wall time of the oracle timing")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB (5 times), the "
@@ -223,6 +224,70 @@ def block_manager_leg(b, steps: int) -> dict:
                     "pa_bm_block_tables (padded int32 tables), Python binding included"}
 
 
+HOST_LINK_PEAK_GBPS = 64.0   # PCIe 5.0 x16, one direction
+
+
+def swap_leg(d, b, reps: int = 5, target_bytes: int = 1 << 30) -> dict:
+    """Preemption traffic: pa_swap_out / pa_swap_in of about 1 GiB of whole
+    blocks between the pools and a pinned block-first host buffer, timed with
+    HIP events; out and in at once on two streams (both link directions); and
+    a plain torch device-to-host copy of the same bytes as the link's
+    achievable rate.  Swap-in writes back the bytes swap-out read, so the
+    pools are left as they were."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_313_amd as P
+
+    blk_bytes = 2 * b.num_kv_heads * b.block_size * b.head_dim * b.elt_bytes
+    n = int(min(b.num_blocks // 2, max(1, target_bytes // blk_bytes)))
+    rng = np.random.default_rng(7)
+    perm = rng.permutation(b.num_blocks).astype(np.int32)
+    ids_a = torch.from_numpy(perm[:n]).cuda()
+    ids_b = torch.from_numpy(perm[n:2 * n]).cuda()
+    host_a = P.swap_buffer(n, d.k_pool)
+    host_b = P.swap_buffer(n, d.k_pool)
+    nbytes = n * blk_bytes
+    s0 = torch.cuda.current_stream()
+    s1 = torch.cuda.Stream()
+
+    def timed(fn, stream):
+        ms = []
+        for _ in range(reps + 1):
+            e0 = torch.cuda.Event(enable_timing=True); e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream); fn(); e1.record(stream)
+            e1.synchronize()
+            ms.append(e0.elapsed_time(e1))
+        return float(np.median(ms[1:]))
+
+    out_ms = timed(lambda: P.swap_out(d.k_pool, d.v_pool, ids_a, host_a, stream=s0), s0)
+    in_ms = timed(lambda: P.swap_in(host_a, d.k_pool, d.v_pool, ids_a, stream=s0), s0)
+    P.swap_out(d.k_pool, d.v_pool, ids_b, host_b, stream=s0)
+    torch.cuda.synchronize()
+    walls = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        P.swap_out(d.k_pool, d.v_pool, ids_a, host_a, stream=s0)
+        P.swap_in(host_b, d.k_pool, d.v_pool, ids_b, stream=s1)
+        torch.cuda.synchronize()
+        walls.append(time.perf_counter() - t0)
+    duplex_ms = 1e3 * float(np.median(walls))
+    flat_dev = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    flat_host = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+    d2h_ms = timed(lambda: flat_host.copy_(flat_dev, non_blocking=True), s0)
+    h2d_ms = timed(lambda: flat_dev.copy_(flat_host, non_blocking=True), s0)
+    gbps = lambda ms, k=1: k * nbytes / (ms * 1e-3) / 1e9
+    return {"blocks": n, "bytes": nbytes, "block_bytes": blk_bytes,
+            "swap_out_ms": out_ms, "swap_out_gbps": gbps(out_ms),
+            "swap_in_ms": in_ms, "swap_in_gbps": gbps(in_ms),
+            "duplex_ms": duplex_ms, "duplex_gbps": gbps(duplex_ms, 2),
+            "plain_d2h_gbps": gbps(d2h_ms), "plain_h2d_gbps": gbps(h2d_ms),
+            "link_peak_gbps_per_direction": HOST_LINK_PEAK_GBPS,
+            "what": "random scattered blocks <-> pinned block-first host buffer, one launch per list; "
+                    "duplex = swap-out and swap-in of two lists at once on two streams (wall time); "
+                    "plain = one contiguous torch copy of the same bytes"}
+
+
 def main():
     args = parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -310,6 +375,7 @@ def main():
     achieved = alg_bytes / (dec_ms * 1e-3) / 1e9
 
     bm_leg = block_manager_leg(b, max(args.steps, 10))
+    swap = None if args.no_swap else swap_leg(d, b)
 
     # parity of this run's output against the oracle run above (all sequences)
     parity = None
@@ -354,6 +420,7 @@ def main():
         "cpu_baseline": cpu,
         "parity": parity,
         "block_manager": bm_leg,
+        "swap": swap,
     }
     print(json.dumps(line), flush=True)
 

@@ -6,12 +6,17 @@
  * `block_size` tokens that live anywhere in a shared physical pool; each
  * sequence reaches its blocks through its own block table (vLLM/PagedAttention
  * paged-KV analysis page, sections 2.2 and 2.3; vLLM entity page, "what it
- * is").  Three operations run on the device:
+ * is").  Operations on the device:
  *
  *   pa_kv_append         write the newest tokens' K/V into their slots
  *   pa_block_copy        copy-on-write duplication of shared blocks
  *   pa_decode_attention  one query token per sequence attends over its paged
  *                        context
+ *   pa_swap_out/_in      move whole blocks between the pools and pinned host
+ *                        memory (preemption)
+ *
+ * The host-side block manager that decides where tokens live is declared in
+ * pa_block_manager.h.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -29,8 +34,9 @@
  *   block_size 8, 16 or 32, num_q_heads a multiple of num_kv_heads with group
  *   size Hq/Hkv in {1, 2, 4, 8, 16}.  Pool pointers and the key/value/query/out
  *   pointers must be 16-byte aligned.
- * - Argument checks are pure host checks made before any HIP call, so a
- *   rejected call has no side effect.  A failed launch returns PA_ERR_HIP and
+ * - Argument checks are pure host checks made before any HIP call (the swap
+ *   calls also ask HIP whether their host buffer is pinned), so a rejected
+ *   call has no side effect.  A failed launch returns PA_ERR_HIP and
  *   pa_last_hip_error() gives the hipError_t value.
  * - Device-side contents are the caller's contract: table entries and slot
  *   ids in range, slots unique within a call, CoW destinations distinct and
@@ -63,7 +69,8 @@ typedef enum {
   PA_ERR_ALIGN = 8,       /* a data pointer is not 16-byte aligned             */
   PA_ERR_NO_BLOCKS = 9,   /* block manager: the free blocks do not cover a batch */
   PA_ERR_SEQUENCE = 10,   /* block manager: a sequence id that is not live     */
-  PA_ERR_CAPACITY = 11    /* block manager: a caller's output buffer is too small */
+  PA_ERR_CAPACITY = 11,   /* block manager: a caller's output buffer is too small */
+  PA_ERR_HOST_MEMORY = 12 /* swap: the host buffer is not pinned, GPU-mapped memory */
 } pa_status;
 
 typedef enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype;
@@ -183,6 +190,45 @@ pa_status pa_decode_attention(void* out, const void* query, const void* k_pool, 
 pa_status pa_block_copy(void* k_pool, void* v_pool, const int32_t* block_mapping, int32_t num_pairs,
                         int32_t num_kv_heads, int32_t block_size, int32_t head_dim,
                         int32_t num_blocks, pa_dtype dtype, void* stream);
+
+/*
+ * pa_swap_out / pa_swap_in -- move whole blocks between the pools and pinned
+ * host memory, one launch per block list.
+ *
+ * Preemption evicts every block of a request at once and brings them back
+ * when it resumes (Cross-Paper Synthesis page, section 3, the preemption
+ * item); the pages blame slow KV movement on many small copies and credit a
+ * block-first layout (vLLM entity page, key observations).  The host buffer is
+ * block-first: entry i is block block_ids[i]'s K tile followed by its V tile,
+ *     host[i][0][h][o][:] = k_pool[block_ids[i]][h][o][:]
+ *     host[i][1][h][o][:] = v_pool[block_ids[i]][h][o][:]
+ * (shape [num_ids][2][num_kv_heads][block_size][head_dim] of dtype).
+ * pa_swap_out writes the host buffer from the pools; pa_swap_in writes the
+ * listed pool blocks from the host buffer.  Byte copies; ids outside
+ * [0, num_blocks) are skipped (their host entries are not touched).  For
+ * pa_swap_in the ids must be distinct.
+ *
+ *   k_pool, v_pool DEVICE pools (read by swap_out, written by swap_in)
+ *   block_ids      DEVICE int32 [num_ids]
+ *   host_dst/src   HOST pinned memory from hipHostMalloc (torch: pin_memory),
+ *                  16-byte aligned, >= num_ids * 2 * Hkv * bs * D * elt bytes;
+ *                  the GPU reads or writes it directly over the host link.
+ *                  PA_ERR_HOST_MEMORY unless HIP knows it as pinned host
+ *                  memory mapped for the GPU at the same address (checked
+ *                  with hipPointerGetAttributes and hipHostGetDevicePointer,
+ *                  which have no other effect).  The host sees swap_out's data, and may
+ *                  reuse swap_in's buffer, once the stream has passed the call.
+ * num_ids == 0 is a no-op returning PA_OK.  Blocks that a block manager frees
+ * on swap-out may be handed out again at once: enqueue pa_swap_out before any
+ * work that writes them, on the same stream.
+ */
+pa_status pa_swap_out(const void* k_pool, const void* v_pool, const int32_t* block_ids, int32_t num_ids,
+                      void* host_dst, int32_t num_kv_heads, int32_t block_size, int32_t head_dim,
+                      int32_t num_blocks, pa_dtype dtype, void* stream);
+
+pa_status pa_swap_in(const void* host_src, void* k_pool, void* v_pool, const int32_t* block_ids,
+                     int32_t num_ids, int32_t num_kv_heads, int32_t block_size, int32_t head_dim,
+                     int32_t num_blocks, pa_dtype dtype, void* stream);
 
 /* Static, human-readable name of a status code.  HOST only. */
 const char* pa_status_string(pa_status status);

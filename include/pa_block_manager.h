@@ -24,7 +24,11 @@
  *   - a batch of appends is all-or-nothing (on PA_ERR_NO_BLOCKS nothing
  *     changes, so the caller can preempt and retry);
  *   - the copies a batch emits must be applied (pa_block_copy) before the
- *     tokens are written (pa_kv_append), both on one stream.
+ *     tokens are written (pa_kv_append), both on one stream;
+ *   - preemption evicts all of a request's blocks at once (Cross-Paper
+ *     Synthesis page, section 3): a swapped-out sequence keeps its length
+ *     but holds no block; on swap-in it gets fresh blocks (blocks it shared
+ *     before come back as private copies).
  *
  * Every pointer here is HOST memory owned by the caller; no call touches the
  * GPU.  A manager is not thread-safe: calls on one manager must not overlap.
@@ -61,7 +65,8 @@ pa_status pa_bm_add_sequence(pa_block_manager* bm, int64_t* seq_id);
 pa_status pa_bm_fork(pa_block_manager* bm, int64_t parent, int64_t* child);
 
 /* Drop the sequence: every block of its table loses a reference, and blocks
- * left with none become free.  PA_ERR_SEQUENCE if it is not live. */
+ * left with none become free (a swapped-out sequence holds none).
+ * PA_ERR_SEQUENCE if it is neither resident nor swapped out. */
 pa_status pa_bm_free_sequence(pa_block_manager* bm, int64_t seq_id);
 
 /* Reserve num_new[i] token positions at the end of sequence seq_ids[i], for
@@ -94,14 +99,32 @@ pa_status pa_bm_block_tables(const pa_block_manager* bm, const int64_t* seq_ids,
                              int32_t max_blocks_per_seq, int32_t* block_tables,
                              int32_t* context_lens);
 
+/* Preemption, out: the blocks of resident sequence seq_id in table order go
+ * to block_ids (HOST int32 [capacity]; *num_ids receives the count), each
+ * loses the sequence's reference (blocks left with none become free), and
+ * the sequence becomes swapped out.  The caller copies the listed blocks to
+ * host memory (pa_swap_out) before any work that may write them.  A swapped
+ * sequence may only be named by pa_bm_swap_in, pa_bm_free_sequence and
+ * pa_bm_sequence_length; elsewhere it is PA_ERR_SEQUENCE.  PA_ERR_CAPACITY
+ * (nothing changes) if its table is longer than capacity. */
+pa_status pa_bm_swap_out(pa_block_manager* bm, int64_t seq_id, int32_t* block_ids, int32_t capacity,
+                         int32_t* num_ids);
+
+/* Preemption, back: a swapped-out sequence takes as many fresh blocks as it
+ * held (lowest first), in table order, into block_ids (HOST int32
+ * [capacity]); the caller copies the host data into them (pa_swap_in).
+ * All-or-nothing: PA_ERR_NO_BLOCKS or PA_ERR_CAPACITY leave it swapped out. */
+pa_status pa_bm_swap_in(pa_block_manager* bm, int64_t seq_id, int32_t* block_ids, int32_t capacity,
+                        int32_t* num_ids);
+
 /* Number of free blocks (-1 if bm is NULL). */
 int32_t pa_bm_num_free_blocks(const pa_block_manager* bm);
 
-/* Length in tokens of a live sequence. */
+/* Length in tokens of a sequence, resident or swapped out. */
 pa_status pa_bm_sequence_length(const pa_block_manager* bm, int64_t seq_id, int64_t* length);
 
-/* Utilisation as an exact ratio: *tokens = sum of the lengths of the live
- * sequences, *slots = blocks in use * block_size (paged-KV analysis page,
+/* Utilisation as an exact ratio: *tokens = sum of the lengths of the
+ * resident sequences, *slots = blocks in use * block_size (paged-KV analysis page,
  * section 4.2).  A block shared by k sequences counts once in *slots and its
  * tokens k times in *tokens. */
 pa_status pa_bm_utilisation(const pa_block_manager* bm, int64_t* tokens, int64_t* slots);

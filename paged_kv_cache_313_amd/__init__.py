@@ -19,7 +19,8 @@ from ._lib import PA_PARTITION_BALANCED, PagedKVError, load  # noqa: F401
 from .block_manager import BlockManager  # noqa: F401
 
 __all__ = ["kv_append", "block_copy", "decode_attention", "decode_workspace_bytes",
-           "choose_partition", "PagedKVError", "load", "PA_PARTITION_BALANCED", "BlockManager"]
+           "choose_partition", "swap_out", "swap_in", "swap_buffer", "PagedKVError", "load",
+           "PA_PARTITION_BALANCED", "BlockManager"]
 
 _DTYPES = {torch.float32: _lib.PA_F32, torch.float16: _lib.PA_F16, torch.bfloat16: _lib.PA_BF16}
 
@@ -85,6 +86,51 @@ def block_copy(k_pool: torch.Tensor, v_pool: torch.Tensor, block_mapping: torch.
                            _dev(block_mapping, "block_mapping"), N, Hkv, bs, D, NB,
                            _dtype_code(k_pool), _stream(k_pool, stream))
     _lib.check("pa_block_copy", st)
+
+
+def _swap_args(k_pool, v_pool, block_ids, host):
+    if block_ids.dtype != torch.int32:
+        raise TypeError("block_ids must be int32")
+    NB, Hkv, bs, D = k_pool.shape
+    if v_pool.shape != k_pool.shape or v_pool.dtype != k_pool.dtype:
+        raise ValueError("k_pool and v_pool must match")
+    n = block_ids.numel()
+    if not isinstance(host, torch.Tensor) or host.is_cuda or not host.is_pinned():
+        raise ValueError("host must be a pinned CPU tensor (pin_memory=True)")
+    if not host.is_contiguous() or host.dtype != k_pool.dtype:
+        raise ValueError("host must be contiguous and of the pools' dtype")
+    if host.numel() < n * 2 * Hkv * bs * D:
+        raise ValueError("host buffer smaller than [num_ids, 2, Hkv, bs, D]")
+    return NB, Hkv, bs, D, n
+
+
+def swap_buffer(num_ids: int, k_pool: torch.Tensor) -> torch.Tensor:
+    """A pinned host buffer [num_ids, 2, Hkv, bs, D] for pa_swap_out / pa_swap_in."""
+    NB, Hkv, bs, D = k_pool.shape
+    return torch.empty((num_ids, 2, Hkv, bs, D), dtype=k_pool.dtype, pin_memory=True)
+
+
+def swap_out(k_pool: torch.Tensor, v_pool: torch.Tensor, block_ids: torch.Tensor, host: torch.Tensor,
+             stream=None) -> None:
+    """Copy blocks ``block_ids`` (device int32 [n]) of both pools into the
+    pinned, block-first host buffer ``host`` [n, 2, Hkv, bs, D] (K then V)."""
+    lib = load()
+    NB, Hkv, bs, D, n = _swap_args(k_pool, v_pool, block_ids, host)
+    st = lib.pa_swap_out(_dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"), _dev(block_ids, "block_ids"), n,
+                         host.data_ptr(), Hkv, bs, D, NB, _dtype_code(k_pool), _stream(k_pool, stream))
+    _lib.check("pa_swap_out", st)
+
+
+def swap_in(host: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor, block_ids: torch.Tensor,
+            stream=None) -> None:
+    """Write entry i of the pinned block-first host buffer into block
+    ``block_ids[i]`` of both pools."""
+    lib = load()
+    NB, Hkv, bs, D, n = _swap_args(k_pool, v_pool, block_ids, host)
+    st = lib.pa_swap_in(host.data_ptr(), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
+                        _dev(block_ids, "block_ids"), n, Hkv, bs, D, NB, _dtype_code(k_pool),
+                        _stream(k_pool, stream))
+    _lib.check("pa_swap_in", st)
 
 
 def decode_workspace_bytes(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int,

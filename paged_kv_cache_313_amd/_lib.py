@@ -14,7 +14,8 @@ PA_F32, PA_F16, PA_BF16 = 0, 1, 2
 PA_PARTITION_BALANCED = -1
 STATUS_NAMES = {0: "PA_OK", 1: "PA_ERR_NULL", 2: "PA_ERR_SHAPE", 3: "PA_ERR_BLOCK_SIZE",
                 4: "PA_ERR_DTYPE", 5: "PA_ERR_PARTITION", 6: "PA_ERR_WORKSPACE", 7: "PA_ERR_HIP",
-                8: "PA_ERR_ALIGN", 9: "PA_ERR_NO_BLOCKS", 10: "PA_ERR_SEQUENCE", 11: "PA_ERR_CAPACITY"}
+                8: "PA_ERR_ALIGN", 9: "PA_ERR_NO_BLOCKS", 10: "PA_ERR_SEQUENCE", 11: "PA_ERR_CAPACITY",
+                12: "PA_ERR_HOST_MEMORY"}
 
 _c_i32, _c_i64, _c_size, _c_f32, _vp = (ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t,
                                         ctypes.c_float, ctypes.c_void_p)
@@ -29,6 +30,8 @@ SIGNATURES = {
                                      _c_i32, _c_i32, _c_i32, _c_i32, _c_f32, _c_i32, _c_i32, _vp,
                                      _c_size, _vp]),
     "pa_block_copy": (_c_i32, [_vp, _vp, _vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _vp]),
+    "pa_swap_out": (_c_i32, [_vp, _vp, _vp, _c_i32, _vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _vp]),
+    "pa_swap_in": (_c_i32, [_vp, _vp, _vp, _vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _vp]),
     "pa_status_string": (ctypes.c_char_p, [_c_i32]),
     # include/pa_block_manager.h (host only)
     "pa_bm_create": (_c_i32, [_c_i32, _c_i32, ctypes.POINTER(_vp)]),
@@ -39,6 +42,8 @@ SIGNATURES = {
     "pa_bm_append_slots": (_c_i32, [_vp, _vp, _vp, _c_i32, _vp, _c_i64, _vp, _c_i32,
                                     ctypes.POINTER(_c_i32)]),
     "pa_bm_block_tables": (_c_i32, [_vp, _vp, _c_i32, _c_i32, _vp, _vp]),
+    "pa_bm_swap_out": (_c_i32, [_vp, _c_i64, _vp, _c_i32, ctypes.POINTER(_c_i32)]),
+    "pa_bm_swap_in": (_c_i32, [_vp, _c_i64, _vp, _c_i32, ctypes.POINTER(_c_i32)]),
     "pa_bm_num_free_blocks": (_c_i32, [_vp]),
     "pa_bm_sequence_length": (_c_i32, [_vp, _c_i64, ctypes.POINTER(_c_i64)]),
     "pa_bm_utilisation": (_c_i32, [_vp, ctypes.POINTER(_c_i64), ctypes.POINTER(_c_i64)]),

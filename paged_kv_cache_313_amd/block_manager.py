@@ -83,6 +83,23 @@ class BlockManager:
                                                 slots.size, _ptr(pairs), ids.size, ctypes.byref(n)))
         return slots, pairs[: n.value].copy()
 
+    # -- preemption ------------------------------------------------------------
+    def _ids_call(self, fn: str, seq_id: int) -> np.ndarray:
+        cap = max(1, -(-self.length(seq_id) // self.block_size))
+        ids = np.empty(cap, dtype=np.int32)
+        n = ctypes.c_int32()
+        _lib.check(fn, getattr(self._lib, fn)(self._h, int(seq_id), _ptr(ids), cap, ctypes.byref(n)))
+        return ids[: n.value].copy()
+
+    def swap_out(self, seq_id: int) -> np.ndarray:
+        """Blocks of the sequence in table order (copy them out before reuse);
+        the sequence becomes swapped out."""
+        return self._ids_call("pa_bm_swap_out", seq_id)
+
+    def swap_in(self, seq_id: int) -> np.ndarray:
+        """Fresh blocks for a swapped-out sequence, in table order."""
+        return self._ids_call("pa_bm_swap_in", seq_id)
+
     # -- read-outs -----------------------------------------------------------
     def block_tables(self, seq_ids, max_blocks_per_seq: int):
         ids = np.ascontiguousarray(seq_ids, dtype=np.int64)

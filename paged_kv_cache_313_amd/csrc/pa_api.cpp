@@ -98,6 +98,8 @@ PA_EXPORT const char* pa_status_string(pa_status s) {
     case PA_ERR_NO_BLOCKS: return "PA_ERR_NO_BLOCKS: not enough free blocks for the batch";
     case PA_ERR_SEQUENCE: return "PA_ERR_SEQUENCE: no live sequence has this id";
     case PA_ERR_CAPACITY: return "PA_ERR_CAPACITY: an output buffer is too small";
+    case PA_ERR_HOST_MEMORY:
+      return "PA_ERR_HOST_MEMORY: the host buffer is not pinned memory mapped for the GPU";
   }
   return "unknown pa_status";
 }
@@ -137,6 +139,46 @@ PA_EXPORT pa_status pa_block_copy(void* k_pool, void* v_pool, const int32_t* blo
   if (block_bytes / 16 > INT32_MAX) return PA_ERR_SHAPE;
   return hip_status(pa::launch_block_copy(k_pool, v_pool, block_mapping, num_pairs, block_bytes,
                                           num_blocks, reinterpret_cast<hipStream_t>(stream)));
+}
+
+static pa_status swap_call(bool out, void* k_pool, void* v_pool, void* host, const int32_t* block_ids,
+                           int32_t num_ids, int32_t num_kv_heads, int32_t block_size, int32_t head_dim,
+                           int32_t num_blocks, pa_dtype dtype, void* stream) {
+  if (!dtype_ok(dtype)) return PA_ERR_DTYPE;
+  if (!block_size_ok(block_size)) return PA_ERR_BLOCK_SIZE;
+  if (num_ids < 0 || num_kv_heads < 1 || !head_dim_ok(head_dim) || num_blocks < 1) return PA_ERR_SHAPE;
+  if (num_ids == 0) return PA_OK;
+  if (num_ids > INT32_MAX / 2) return PA_ERR_SHAPE;
+  if (!k_pool || !v_pool || !block_ids || !host) return PA_ERR_NULL;
+  if (!aligned16(k_pool) || !aligned16(v_pool) || !aligned16(host)) return PA_ERR_ALIGN;
+  const int64_t block_bytes = (int64_t)num_kv_heads * block_size * head_dim * elt_bytes(dtype);
+  if (block_bytes / 16 > INT32_MAX) return PA_ERR_SHAPE;
+  // the host buffer must be pinned host memory the GPU can address
+  // (hipHostMalloc): HIP must classify it as host memory and map it at the
+  // same address (as ROCm maps pinned memory); anything else is refused
+  hipPointerAttribute_t attr;
+  void* dev_host = nullptr;
+  if (hipPointerGetAttributes(&attr, host) != hipSuccess || attr.type != hipMemoryTypeHost ||
+      hipHostGetDevicePointer(&dev_host, host, 0) != hipSuccess || dev_host != host) {
+    (void)hipGetLastError();   // do not leave the lookup's error for the caller's next call
+    return PA_ERR_HOST_MEMORY;
+  }
+  return hip_status(pa::launch_swap(out, k_pool, v_pool, dev_host, block_ids, num_ids, block_bytes,
+                                    num_blocks, reinterpret_cast<hipStream_t>(stream)));
+}
+
+PA_EXPORT pa_status pa_swap_out(const void* k_pool, const void* v_pool, const int32_t* block_ids,
+                                int32_t num_ids, void* host_dst, int32_t num_kv_heads, int32_t block_size,
+                                int32_t head_dim, int32_t num_blocks, pa_dtype dtype, void* stream) {
+  return swap_call(true, const_cast<void*>(k_pool), const_cast<void*>(v_pool), host_dst, block_ids, num_ids,
+                   num_kv_heads, block_size, head_dim, num_blocks, dtype, stream);
+}
+
+PA_EXPORT pa_status pa_swap_in(const void* host_src, void* k_pool, void* v_pool, const int32_t* block_ids,
+                               int32_t num_ids, int32_t num_kv_heads, int32_t block_size, int32_t head_dim,
+                               int32_t num_blocks, pa_dtype dtype, void* stream) {
+  return swap_call(false, k_pool, v_pool, const_cast<void*>(host_src), block_ids, num_ids, num_kv_heads,
+                   block_size, head_dim, num_blocks, dtype, stream);
 }
 
 PA_EXPORT size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,

@@ -1,7 +1,8 @@
 // Host-side KV block manager: physical block allocation, per-sequence block
 // tables, reference-counted sharing with copy-on-write, release on finish
 // (vLLM/PagedAttention paged-KV analysis page, sections 2.2, 2.3, 3.2, 3.3;
-// vLLM entity page, "what it is").
+// vLLM entity page, "what it is"), and whole-request swap for preemption
+// (Cross-Paper Synthesis page, section 3).
 //
 // Free blocks live in a three-level bitmap (bit set = free): level 0 has one
 // bit per block, level 1 one bit per non-empty level-0 word, level 2 one bit
@@ -79,6 +80,11 @@ struct Sequence {
   int64_t len = 0;
 };
 
+struct SwappedOut {
+  int64_t len = 0;
+  int32_t nblocks = 0;
+};
+
 // one reversible change made by an append batch
 struct Undo {
   enum Kind : uint8_t { kTake, kRefDec, kTableSet, kTablePush, kLen } kind;
@@ -96,7 +102,8 @@ struct pa_block_manager {
   int64_t blocks_in_use = 0;
   std::vector<int32_t> ref;
   FreeBitmap free;
-  std::unordered_map<int64_t, Sequence> seqs;
+  std::unordered_map<int64_t, Sequence> seqs;        // resident
+  std::unordered_map<int64_t, SwappedOut> swapped;   // preempted to host memory
   std::vector<Undo> log;   // reused by every append batch
 
   int32_t take() {
@@ -182,6 +189,7 @@ PA_EXPORT pa_status pa_bm_fork(pa_block_manager* bm, int64_t parent, int64_t* ch
 
 PA_EXPORT pa_status pa_bm_free_sequence(pa_block_manager* bm, int64_t seq_id) {
   if (!bm) return PA_ERR_NULL;
+  if (bm->swapped.erase(seq_id)) return PA_OK;
   auto it = bm->seqs.find(seq_id);
   if (it == bm->seqs.end()) return PA_ERR_SEQUENCE;
   for (int32_t b : it->second.table) bm->release_ref(b);
@@ -286,12 +294,66 @@ PA_EXPORT pa_status pa_bm_block_tables(const pa_block_manager* bm, const int64_t
   return PA_OK;
 }
 
+PA_EXPORT pa_status pa_bm_swap_out(pa_block_manager* bm, int64_t seq_id, int32_t* block_ids,
+                                   int32_t capacity, int32_t* num_ids) {
+  if (!bm || !num_ids) return PA_ERR_NULL;
+  auto it = bm->seqs.find(seq_id);
+  if (it == bm->seqs.end()) return PA_ERR_SEQUENCE;
+  const std::vector<int32_t>& table = it->second.table;
+  const size_t n = table.size();
+  if (n > (size_t)(capacity < 0 ? 0 : capacity)) return PA_ERR_CAPACITY;
+  if (n && !block_ids) return PA_ERR_NULL;
+  try {
+    bm->swapped.emplace(seq_id, SwappedOut{it->second.len, (int32_t)n});
+  } catch (...) {
+    return PA_ERR_CAPACITY;
+  }
+  if (n) std::memcpy(block_ids, table.data(), n * sizeof(int32_t));
+  for (int32_t b : table) bm->release_ref(b);
+  bm->seqs.erase(it);
+  *num_ids = (int32_t)n;
+  return PA_OK;
+}
+
+PA_EXPORT pa_status pa_bm_swap_in(pa_block_manager* bm, int64_t seq_id, int32_t* block_ids,
+                                  int32_t capacity, int32_t* num_ids) {
+  if (!bm || !num_ids) return PA_ERR_NULL;
+  auto it = bm->swapped.find(seq_id);
+  if (it == bm->swapped.end()) return PA_ERR_SEQUENCE;
+  const int32_t n = it->second.nblocks;
+  if (n > capacity) return PA_ERR_CAPACITY;
+  if (n && !block_ids) return PA_ERR_NULL;
+  if (bm->free.count() < n) return PA_ERR_NO_BLOCKS;
+  Sequence s;
+  try {
+    s.table.reserve((size_t)n);
+    bm->seqs.reserve(bm->seqs.size() + 1);
+  } catch (...) {
+    return PA_ERR_CAPACITY;
+  }
+  s.len = it->second.len;
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t b = bm->take();   // cannot fail: n blocks are free
+    s.table.push_back(b);
+    block_ids[i] = b;
+  }
+  bm->seqs.emplace(seq_id, std::move(s));   // no rehash: reserved above
+  bm->swapped.erase(it);
+  *num_ids = n;
+  return PA_OK;
+}
+
 PA_EXPORT int32_t pa_bm_num_free_blocks(const pa_block_manager* bm) {
   return bm ? bm->free.count() : -1;
 }
 
 PA_EXPORT pa_status pa_bm_sequence_length(const pa_block_manager* bm, int64_t seq_id, int64_t* length) {
   if (!bm || !length) return PA_ERR_NULL;
+  auto sw = bm->swapped.find(seq_id);
+  if (sw != bm->swapped.end()) {
+    *length = sw->second.len;
+    return PA_OK;
+  }
   auto it = bm->seqs.find(seq_id);
   if (it == bm->seqs.end()) return PA_ERR_SEQUENCE;
   *length = it->second.len;

@@ -8,6 +8,13 @@
 //    of them writes into it (same page, sections 2.3 and 3.2).  All pairs go in
 //    one launch: many small per-block copies are what makes KV movement slow
 //    (vLLM entity page, key observations).
+//  - swap out / swap in: every block of a preempted request moves between the
+//    pools and pinned host memory (Cross-Paper Synthesis page, section 3, the
+//    preemption item), again in one launch per block list, into a block-first
+//    host layout (entry i = K tile then V tile of block ids[i]) so one
+//    request's KV is one contiguous host run (vLLM entity page, key
+//    observations).  The GPU's own loads and stores cross the host link; the
+//    scattered pool side is read or written in whole tiles.
 #include "pa_common.hpp"
 #include "pa_launch.hpp"
 
@@ -67,6 +74,52 @@ __global__ __launch_bounds__(kCopyThreads) void block_copy_kernel(
       if (c < chunks_per_block) d[c] = tmp[j];
     }
   }
+}
+
+// One workgroup per (list entry, K-or-V): moves one (block, all heads) tile
+// between its pool and its place in the block-first host buffer.  Eight
+// 16-byte chunks per thread in flight (32 KiB per workgroup) to cover the
+// host link's latency.  OUT: pool -> host; otherwise host -> pool.
+constexpr int kSwapChunksPerThread = 8;
+
+template <bool OUT>
+__global__ __launch_bounds__(kCopyThreads) void swap_kernel(u32x4* __restrict__ k_pool,
+                                                            u32x4* __restrict__ v_pool,
+                                                            u32x4* __restrict__ host,
+                                                            const int32_t* __restrict__ block_ids,
+                                                            int32_t chunks_per_block, int32_t num_blocks) {
+  const int32_t entry = blockIdx.x >> 1;
+  const int32_t kv = blockIdx.x & 1;
+  const int32_t id = block_ids[entry];
+  if (id < 0 || id >= num_blocks) return;
+  u32x4* pool = (kv ? v_pool : k_pool) + (int64_t)id * chunks_per_block;
+  u32x4* h = host + ((int64_t)entry * 2 + kv) * chunks_per_block;
+  const u32x4* s = OUT ? pool : h;
+  u32x4* d = OUT ? h : pool;
+  constexpr int step = kCopyThreads * kSwapChunksPerThread;
+  for (int32_t base = 0; base < chunks_per_block; base += step) {
+    u32x4 tmp[kSwapChunksPerThread];
+#pragma unroll
+    for (int j = 0; j < kSwapChunksPerThread; ++j) {
+      const int32_t c = base + j * kCopyThreads + threadIdx.x;
+      if (c < chunks_per_block) tmp[j] = s[c];
+    }
+#pragma unroll
+    for (int j = 0; j < kSwapChunksPerThread; ++j) {
+      const int32_t c = base + j * kCopyThreads + threadIdx.x;
+      if (c < chunks_per_block) d[c] = tmp[j];
+    }
+  }
+}
+
+hipError_t launch_swap(bool out, void* k_pool, void* v_pool, void* host, const int32_t* block_ids,
+                       int32_t num_ids, int64_t block_bytes, int32_t num_blocks, hipStream_t stream) {
+  const int32_t chunks = (int32_t)(block_bytes / 16);
+  auto kern = out ? swap_kernel<true> : swap_kernel<false>;
+  hipLaunchKernelGGL(kern, dim3(2 * num_ids), dim3(kCopyThreads), 0, stream,
+                     reinterpret_cast<u32x4*>(k_pool), reinterpret_cast<u32x4*>(v_pool),
+                     reinterpret_cast<u32x4*>(host), block_ids, chunks, num_blocks);
+  return hipGetLastError();
 }
 
 hipError_t launch_kv_append(const void* key, const void* value, void* k_pool, void* v_pool,

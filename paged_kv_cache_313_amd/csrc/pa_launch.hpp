@@ -15,6 +15,11 @@ hipError_t launch_kv_append(const void* key, const void* value, void* k_pool, vo
                             int32_t row_bytes, int32_t block_size, int32_t num_blocks,
                             hipStream_t stream);
 
+// Swap: out = pool tiles of block_ids -> block-first host buffer; else back.
+// `host` is the device-side address of pinned host memory.
+hipError_t launch_swap(bool out, void* k_pool, void* v_pool, void* host, const int32_t* block_ids,
+                       int32_t num_ids, int64_t block_bytes, int32_t num_blocks, hipStream_t stream);
+
 hipError_t launch_block_copy(void* k_pool, void* v_pool, const int32_t* block_mapping,
                              int32_t num_pairs, int64_t block_bytes, int32_t num_blocks,
                              hipStream_t stream);

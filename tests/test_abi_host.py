@@ -159,3 +159,26 @@ def test_binding_refuses_cpu_tensors(lib):
         P.decode_attention(q, torch.zeros(4, 4, 16, 64), torch.zeros(4, 4, 16, 64),
                            torch.zeros(2, 1, dtype=torch.int32), torch.ones(2, dtype=torch.int32),
                            0.125, 1, partition_size=0, out=torch.empty(2, 4, 64))
+
+
+SWAP_OK = dict(pool_k=A, pool_v=B, ids=A, n=4, host=B, hkv=8, bs=16, d=128, nb=100, dtype=BF16)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=7), 4), (dict(bs=12), 3), (dict(d=96), 2), (dict(n=-1), 2), (dict(nb=0), 2),
+    (dict(hkv=0), 2), (dict(ids=None), 1), (dict(host=None), 1), (dict(pool_k=None), 1),
+    (dict(host=B + 8), 8), (dict(pool_v=B + 4), 8), (dict(n=0, ids=None, host=None), 0),
+])
+def test_swap_argument_checks(lib, kw, status):
+    a = {**SWAP_OK, **kw}
+    assert lib.pa_swap_out(a["pool_k"], a["pool_v"], a["ids"], a["n"], a["host"], a["hkv"], a["bs"], a["d"],
+                           a["nb"], a["dtype"], None) == status
+    assert lib.pa_swap_in(a["host"], a["pool_k"], a["pool_v"], a["ids"], a["n"], a["hkv"], a["bs"], a["d"],
+                          a["nb"], a["dtype"], None) == status
+
+
+def test_swap_binding_refuses_pageable_host_memory(lib):
+    import torch
+    host = torch.empty(16)
+    with pytest.raises(ValueError):
+        P._swap_args(torch.empty(4, 1, 16, 64), torch.empty(4, 1, 16, 64), torch.zeros(1, dtype=torch.int32), host)

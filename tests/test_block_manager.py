@@ -25,6 +25,8 @@ def built():
 
 
 def same_state(nat, ref):
+    for sid in ref.swapped:
+        assert nat.length(sid) == ref.length(sid)
     live = sorted(ref.seqs)
     if live:
         mb = max(1, max(len(ref.seqs[s]["table"]) for s in live))
@@ -42,6 +44,7 @@ def run_history(seed, num_blocks, bs, steps, max_batch=8, max_tokens=50):
     n_fail = 0
     for _ in range(steps):
         live = sorted(ref.seqs)
+        out = sorted(ref.swapped)
         r = rng.random()
         if not live or r < 0.15:
             assert nat.add_sequence() == ref.add_sequence()
@@ -49,9 +52,25 @@ def run_history(seed, num_blocks, bs, steps, max_batch=8, max_tokens=50):
             p = rng.choice(live)
             assert nat.fork(p) == ref.fork(p)
         elif r < 0.40 and len(live) > 1:
-            s = rng.choice(live)
+            s = rng.choice(live + out)
             nat.free_sequence(s)
             ref.free_sequence(s)
+        elif r < 0.46:
+            s = rng.choice(live)
+            assert nat.swap_out(s).tolist() == ref.swap_out(s)
+        elif r < 0.52 and out:
+            s = rng.choice(out)
+            try:
+                want = ref.swap_in(s)
+            except OutOfBlocks:
+                want = None
+            if want is None:
+                with pytest.raises(P.PagedKVError) as e:
+                    nat.swap_in(s)
+                assert e.value.status == NO_BLOCKS
+                n_fail += 1
+            else:
+                assert nat.swap_in(s).tolist() == want
         else:
             k = rng.randint(1, max_batch)
             seqs = [rng.choice(live) for _ in range(k)]          # repeats allowed
@@ -163,3 +182,35 @@ def test_argument_checks():
     bm.free_sequence(b)
     assert bm.refcounts().tolist() == [1, 1, 0, 1]
     bm.close()
+
+
+def test_swapped_sequence_errors_and_round_trip():
+    bm = P.BlockManager(8, 4)
+    a = bm.add_sequence()
+    bm.append_slots([a], [10])
+    b = bm.fork(a)
+    assert bm.swap_out(a).tolist() == [0, 1, 2]
+    assert bm.num_free_blocks() == 5                # b still holds the three blocks
+    for call in (lambda: bm.append_slots([a], [1]), lambda: bm.fork(a), lambda: bm.block_tables([a], 4),
+                 lambda: bm.swap_out(a)):
+        with pytest.raises(P.PagedKVError) as e:
+            call()
+        assert e.value.status == BAD_SEQ
+    with pytest.raises(P.PagedKVError) as e:
+        bm.swap_in(b)                                # resident, not swapped
+    assert e.value.status == BAD_SEQ
+    assert bm.length(a) == 10
+    assert bm.swap_in(a).tolist() == [3, 4, 5]
+    t, l = bm.block_tables([a, b], 3)
+    assert t.tolist() == [[3, 4, 5], [0, 1, 2]] and l.tolist() == [10, 10]
+    bm.swap_out(b)
+    c = bm.add_sequence()
+    bm.append_slots([c], [4 * 4])                     # 4 of the 5 free blocks (b freed 3)
+    assert bm.num_free_blocks() == 8 - 3 - 4
+    with pytest.raises(P.PagedKVError) as e:
+        bm.swap_in(b)
+    assert e.value.status == NO_BLOCKS and bm.length(b) == 10
+    bm.free_sequence(b)
+    with pytest.raises(P.PagedKVError) as e:
+        bm.length(b)
+    assert e.value.status == BAD_SEQ

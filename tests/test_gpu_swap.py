@@ -1,0 +1,157 @@
+"""GPU swap out / swap in (pa_swap_out, pa_swap_in) against the oracle, bit
+for bit: block-first host layout, every dtype, block size and head size,
+out-of-pool ids skipped, interior pointers of a pinned buffer, pageable
+memory refused; and a preemption round trip driven by the native block
+manager in the middle of decode steps."""
+
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.pa_oracle as O
+import paged_kv_cache_313_amd as P
+from oracle.block_manager import BlockManager as RefBM
+from workloads import synth as W
+from workloads import torch_io
+
+from gpu_util import check_close, gpu_out_f64, note
+
+pytestmark = pytest.mark.gpu
+
+
+def pools(dtype, NB, Hkv, bs, D, seed):
+    rng = np.random.default_rng(seed)
+    k = W.to_storage(rng.standard_normal((NB, Hkv, bs, D), dtype=np.float32), dtype)
+    v = W.to_storage(rng.standard_normal((NB, Hkv, bs, D), dtype=np.float32), dtype)
+    return k, v
+
+
+def host_view(t, dtype):
+    return t.view(torch.uint16).numpy() if dtype == "bf16" else t.numpy()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("bs,D,Hkv", [(16, 128, 8), (8, 64, 2), (32, 128, 1)])
+def test_swap_out_in_bit_exact(dtype, bs, D, Hkv):
+    NB = 40
+    k, v = pools(dtype, NB, Hkv, bs, D, seed=bs + D)
+    dk, dv = torch_io.storage_to_torch(k, dtype, "cuda"), torch_io.storage_to_torch(v, dtype, "cuda")
+    ids = np.array([5, 0, 39, 17, -1, 40, 22], dtype=np.int32)
+    host = P.swap_buffer(len(ids), dk)
+    host.zero_()
+    note(f"swap out {dtype} bs={bs} D={D} Hkv={Hkv}")
+    P.swap_out(dk, dv, torch.from_numpy(ids).cuda(), host)
+    torch.cuda.synchronize()
+    want = np.zeros((len(ids), 2, Hkv, bs, D), dtype=k.dtype)
+    O.swap_out(k, v, ids, want)
+    assert host_view(host, dtype).tobytes() == want.tobytes()
+
+    # swap back into other blocks, after clobbering them
+    dst = np.array([1, 2, 3, 4, -7, 99, 38], dtype=np.int32)
+    dk[torch.from_numpy(dst[:4]).long().cuda()] = 0
+    O_k = k.copy()
+    O_k[dst[:4]] = 0
+    dv_ref = torch_io.torch_to_storage(dv, dtype).copy()
+    note(f"swap in {dtype} bs={bs} D={D} Hkv={Hkv}")
+    P.swap_in(host, dk, dv, torch.from_numpy(dst).cuda())
+    torch.cuda.synchronize()
+    O.swap_in(want, O_k, dv_ref, dst)
+    assert torch_io.torch_to_storage(dk, dtype).tobytes() == O_k.tobytes()
+    assert torch_io.torch_to_storage(dv, dtype).tobytes() == dv_ref.tobytes()
+
+
+def test_interior_pointer_of_pinned_buffer():
+    dtype, NB, Hkv, bs, D = "bf16", 16, 2, 16, 128
+    k, v = pools(dtype, NB, Hkv, bs, D, seed=1)
+    dk, dv = torch_io.storage_to_torch(k, dtype, "cuda"), torch_io.storage_to_torch(v, dtype, "cuda")
+    big = torch.zeros((5, 2, Hkv, bs, D), dtype=torch.bfloat16, pin_memory=True)
+    part = big[2:4]                                  # starts 2 entries into the allocation
+    ids = np.array([7, 3], dtype=np.int32)
+    note("swap interior pointer")
+    P.swap_out(dk, dv, torch.from_numpy(ids).cuda(), part)
+    torch.cuda.synchronize()
+    want = np.zeros((2, 2, Hkv, bs, D), dtype=np.uint16)
+    O.swap_out(k, v, ids, want)
+    assert host_view(part, dtype).tobytes() == want.tobytes()
+    assert not big[:2].view(torch.uint16).any() and not big[4:].view(torch.uint16).any()
+
+
+def test_pageable_host_memory_refused_by_library():
+    """The only id is outside the pool, so even a wrongly accepted buffer
+    would not be touched by the kernel."""
+    lib = P.load()
+    dk = torch.zeros((4, 1, 16, 64), dtype=torch.float16, device="cuda")
+    ids = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+    pageable = np.zeros(4 * 1 * 16 * 64 * 2 + 64, dtype=np.uint8)
+    addr = (pageable.ctypes.data + 15) // 16 * 16
+    note("swap pageable refused")
+    st = lib.pa_swap_out(dk.data_ptr(), dk.data_ptr(), ids.data_ptr(), 1, addr, 1, 16, 64, 4, 1, None)
+    assert st == 12
+
+
+def test_preemption_round_trip_in_decode_steps():
+    """Two of five sequences are preempted (manager swap-out + device swap-out),
+    the rest keep decoding and take the freed blocks, then the two come back
+    (swap-in) into fresh blocks and all five decode again."""
+    rng = np.random.default_rng(77)
+    dtype, NB, Hkv, G, D, bs = "bf16", 64, 2, 4, 128, 16
+    scale = W.default_scale(D)
+    nat, ref = P.BlockManager(NB, bs), RefBM(NB, bs)
+    k_host = W.poison_array((NB, Hkv, bs, D), dtype)
+    v_host = W.poison_array((NB, Hkv, bs, D), dtype)
+    dk, dv = torch_io.storage_to_torch(k_host, dtype, "cuda"), torch_io.storage_to_torch(v_host, dtype, "cuda")
+
+    def draw(shape):
+        return W.to_storage(rng.standard_normal(shape, dtype=np.float32), dtype)
+
+    def append(seqs, counts):
+        slots, pairs = nat.append_slots(seqs, counts)
+        want = ref.append_slots(seqs, counts)
+        assert slots.tolist() == want[0] and not len(pairs)
+        key, val = draw((len(slots), Hkv, D)), draw((len(slots), Hkv, D))
+        P.kv_append(torch_io.storage_to_torch(key, dtype, "cuda"), torch_io.storage_to_torch(val, dtype, "cuda"),
+                    dk, dv, torch.from_numpy(slots).cuda())
+        O.kv_append(k_host, v_host, key, val, slots, bs)
+
+    def decode(seqs, label):
+        tables, lens = nat.block_tables(seqs, 16)
+        q = draw((len(seqs), Hkv * G, D))
+        note(f"preemption {label}")
+        out = P.decode_attention(torch_io.storage_to_torch(q, dtype, "cuda"), dk, dv,
+                                 torch.from_numpy(tables).cuda(), torch.from_numpy(lens).cuda(), scale,
+                                 int(lens.max()), -1)
+        torch.cuda.synchronize()
+        check_close(gpu_out_f64(out, dtype), O.decode_attention(q, k_host, v_host, tables, lens, scale, bs, dtype),
+                    dtype, label)
+
+    seqs = [nat.add_sequence() for _ in range(5)]
+    assert [ref.add_sequence() for _ in range(5)] == seqs
+    append(seqs, [70, 33, 120, 16, 90])
+    decode(seqs, "before")
+    gone = [seqs[0], seqs[2]]
+    saved = {}
+    for s in gone:
+        ids = nat.swap_out(s)
+        assert ids.tolist() == ref.swap_out(s)
+        host = P.swap_buffer(len(ids), dk)
+        P.swap_out(dk, dv, torch.from_numpy(ids).cuda(), host)   # before the blocks are reused
+        want = np.empty((len(ids), 2, Hkv, bs, D), dtype=np.uint16)
+        O.swap_out(k_host, v_host, ids, want)
+        saved[s] = (host, want)
+    rest = [s for s in seqs if s not in gone]
+    append(rest, [100, 100, 100])                       # takes the freed blocks
+    decode(rest, "while preempted")
+    torch.cuda.synchronize()
+    for s in gone:
+        host, want = saved[s]
+        assert host.view(torch.uint16).numpy().tobytes() == want.tobytes()
+        ids = nat.swap_in(s)
+        assert ids.tolist() == ref.swap_in(s)
+        P.swap_in(host, dk, dv, torch.from_numpy(ids).cuda())
+        O.swap_in(want, k_host, v_host, ids)
+    append(seqs, [1] * 5)
+    decode(seqs, "after swap-in")
+    assert torch_io.torch_to_storage(dk, dtype).tobytes() == k_host.tobytes()
+    assert torch_io.torch_to_storage(dv, dtype).tobytes() == v_host.tobytes()
