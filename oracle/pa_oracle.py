@@ -31,6 +31,10 @@ What it computes, and where the pages define it:
 * Partitioned decode -- the same attention evaluated per 512-token slice and
   merged by the log-sum-exp rescale (not on the pages; it is the split that
   long contexts need).  Exactly equal to the dense result up to rounding.
+* Prefill over a cached prefix -- the new tokens of a request attend
+  causally over its whole paged context, shared prefix pages included
+  (paged-KV analysis page, sections 3.2 and 4.1).  Token at position p reads
+  tokens t <= p.  Written out as masked dense attention per (sequence, head).
 * Swap out / swap in -- preemption evicts all blocks of a request to host
   memory and brings them back later (Cross-Paper Synthesis page, section 3);
   the host copy is block-first (vLLM entity page, key observations).  Byte
@@ -215,6 +219,45 @@ def decode_attention(query, k_pool, v_pool, block_tables, context_lens, scale, b
             out[s, g * G:(g + 1) * G] = decode_group(query, k_pool, v_pool, block_tables,
                                                      context_lens, scale, block_size, dtype,
                                                      s, g, fast=fast)
+    return out
+
+
+def prefill_attention(query, k_pool, v_pool, block_tables, context_lens, query_start, scale,
+                      block_size, dtype=None, seqs=None) -> np.ndarray:
+    """Multi-token attention over a paged, partly cached context; float64
+    [T, Hq, D].
+
+    When a request's prompt shares a cached prefix, only its new tokens run
+    through prefill, reading the prefix's KV pages instead of recomputing
+    them (paged-KV analysis page, section 3.2 and the TTFT row of section
+    4.1).  Sequence s has context_lens[s] = L tokens in its pages, the last
+    n = query_start[s+1] - query_start[s] of which are its new tokens (already
+    appended); query row query_start[s] + j is the token at position
+    p = L - n + j, and attends causally, to tokens t <= p:
+        out = sum_{t<=p} exp(s_t - max) v_t / sum_{t<=p} exp(s_t - max),
+        s_t = scale * <q, k_t>.
+    n = 1 is decode attention.  ``seqs`` restricts the work (other rows NaN)."""
+    dtype = dtype or infer_dtype(query)
+    T, Hq, D = query.shape
+    Hkv = k_pool.shape[1]
+    G = Hq // Hkv
+    scale64 = float(np.float32(scale))
+    out = np.full((T, Hq, D), np.nan, dtype=np.float64)
+    starts = np.asarray(query_start, dtype=np.int64)
+    for s in (range(len(starts) - 1) if seqs is None else seqs):
+        q0, q1 = int(starts[s]), int(starts[s + 1])
+        n, L = q1 - q0, int(context_lens[s])
+        if n == 0:
+            continue
+        pos = np.arange(L - n, L)                                  # positions of the new tokens
+        for g in range(Hkv):
+            keys = upcast(gather_tokens_fast(k_pool, block_tables[s], L, block_size, g), dtype)
+            values = upcast(gather_tokens_fast(v_pool, block_tables[s], L, block_size, g), dtype)
+            for h in range(g * G, (g + 1) * G):
+                q = upcast(query[q0:q1, h], dtype)                 # [n, D]
+                scores = (q @ keys.T) * scale64                    # [n, L]
+                scores[np.arange(L)[None, :] > pos[:, None]] = -np.inf
+                out[q0:q1, h] = attention_weights(scores) @ values
     return out
 
 

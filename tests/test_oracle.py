@@ -443,3 +443,97 @@ def test_swap_in_restores_clobbered_blocks_and_skips_bad_ids():
     v[[4, 6]] = np.nan
     O.swap_in(host, k, v, ids)
     assert np.array_equal(k, k0) and np.array_equal(v, v0)
+
+
+# -- prefill over a cached prefix ----------------------------------------------
+
+def _prefill_case(seed, lens, news, Hq=4, Hkv=2, D=16, bs=4, dtype="f32"):
+    rng = np.random.default_rng(seed)
+    S = len(lens)
+    nbs = [-(-L // bs) for L in lens]
+    NB = sum(nbs) + 3
+    perm = rng.permutation(NB)
+    tables = np.full((S, max(nbs)), -1, dtype=np.int32)
+    k = 0
+    for s, nb in enumerate(nbs):
+        tables[s, :nb] = perm[k:k + nb]
+        k += nb
+    kp = W.to_storage(rng.standard_normal((NB, Hkv, bs, D), dtype=np.float32), dtype)
+    vp = W.to_storage(rng.standard_normal((NB, Hkv, bs, D), dtype=np.float32), dtype)
+    starts = np.concatenate([[0], np.cumsum(news)]).astype(np.int32)
+    q = W.to_storage(rng.standard_normal((int(starts[-1]), Hq, D), dtype=np.float32), dtype)
+    return q, kp, vp, tables, np.array(lens, dtype=np.int32), starts, bs
+
+
+def test_prefill_is_bottom_right_causal_sdpa():
+    """The new tokens are the last rows of ordinary causal attention over the
+    whole sequence: torch SDPA (fp64, is_causal) over all L positions, with
+    the cached prefix's queries filled at random, keeps the last n rows."""
+    lens, news = [37, 5, 64], [9, 5, 1]
+    q, kp, vp, tables, L, starts, bs = _prefill_case(3, lens, news)
+    Hq, Hkv, D = q.shape[1], kp.shape[1], q.shape[2]
+    out = O.prefill_attention(q, kp, vp, tables, L, starts, 0.25, bs)
+    rng = np.random.default_rng(9)
+    for s in range(len(lens)):
+        n, Ls = news[s], lens[s]
+        full_q = rng.standard_normal((Ls, Hq, D))
+        full_q[Ls - n:] = q[starts[s]:starts[s + 1]]
+        for g in range(Hkv):
+            kk = torch.from_numpy(O.gather_tokens(kp, tables[s], Ls, bs, g).astype(np.float64))
+            vv = torch.from_numpy(O.gather_tokens(vp, tables[s], Ls, bs, g).astype(np.float64))
+            for h in range(g * (Hq // Hkv), (g + 1) * (Hq // Hkv)):
+                qq = torch.from_numpy(full_q[:, h])
+                ref = torch.nn.functional.scaled_dot_product_attention(
+                    qq[None, None], kk[None, None], vv[None, None], is_causal=True, scale=0.25)[0, 0]
+                assert np.allclose(out[starts[s]:starts[s + 1], h], ref[Ls - n:].numpy(), atol=1e-12, rtol=0)
+
+
+def test_prefill_of_one_token_is_decode():
+    lens = [1, 17, 40]
+    q, kp, vp, tables, L, starts, bs = _prefill_case(5, lens, [1, 1, 1], dtype="bf16")
+    a = O.prefill_attention(q, kp, vp, tables, L, starts, 0.3, bs, "bf16")
+    b = O.decode_attention(q, kp, vp, tables, L, 0.3, bs, "bf16")
+    assert np.allclose(a, b, atol=1e-12, rtol=0)      # same sums, BLAS may order them differently
+
+
+def test_prefill_first_token_of_fresh_prompt_is_its_value():
+    """With no cached prefix (n = L) the first new token sees only itself."""
+    q, kp, vp, tables, L, starts, bs = _prefill_case(7, [12], [12])
+    out = O.prefill_attention(q, kp, vp, tables, L, starts, 0.5, bs)
+    blk = tables[0, 0]
+    for h in range(q.shape[1]):
+        assert np.array_equal(out[0, h], vp[blk, h // 2, 0].astype(np.float64))
+
+
+def test_prefill_brute_force_tiny():
+    q, kp, vp, tables, L, starts, bs = _prefill_case(11, [6, 3], [4, 3], Hq=2, Hkv=1, D=3, bs=2)
+    out = O.prefill_attention(q, kp, vp, tables, L, starts, 0.7, bs)
+    for s in range(2):
+        n, Ls = int(starts[s + 1] - starts[s]), int(L[s])
+        for j in range(n):
+            p = Ls - n + j
+            for h in range(2):
+                num = np.zeros(3)
+                den = 0.0
+                for t in range(p + 1):
+                    b, o = tables[s, t // bs], t % bs
+                    sc = float(np.float32(0.7))       # the scale argument is an fp32 value
+                    w = math.exp(sc * float(np.dot(q[starts[s] + j, h].astype(np.float64), kp[b, 0, o])))
+                    num += w * vp[b, 0, o].astype(np.float64)
+                    den += w
+                assert np.allclose(out[starts[s] + j, h], num / den, atol=1e-12, rtol=0)
+
+
+def test_prefill_planted_mistakes_are_caught():
+    """An off-by-one causal mask, or the mask anchored at the prefix start
+    (top-left), changes the output."""
+    q, kp, vp, tables, L, starts, bs = _prefill_case(13, [30], [8])
+    good = O.prefill_attention(q, kp, vp, tables, L, starts, 0.25, bs)
+    keys = O.gather_tokens(kp, tables[0], 30, bs, 0).astype(np.float64)
+    vals = O.gather_tokens(vp, tables[0], 30, bs, 0).astype(np.float64)
+    qq = q[:, 0].astype(np.float64)
+    sc = (qq @ keys.T) * 0.25
+    strict = sc.copy(); strict[np.arange(30)[None, :] >= np.arange(22, 30)[:, None]] = -np.inf
+    topleft = sc.copy(); topleft[np.arange(30)[None, :] > np.arange(8)[:, None]] = -np.inf
+    assert not np.allclose(O.attention_weights(strict) @ vals, good[:, 0])
+    assert not np.allclose(O.attention_weights(topleft) @ vals, good[:, 0])
