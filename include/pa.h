@@ -12,6 +12,8 @@
  *   pa_block_copy        copy-on-write duplication of shared blocks
  *   pa_decode_attention  one query token per sequence attends over its paged
  *                        context
+ *   pa_prefill_attention the new tokens of each sequence attend causally over
+ *                        its paged context (prefill over a cached prefix)
  *   pa_swap_out/_in      move whole blocks between the pools and pinned host
  *                        memory (preemption)
  *
@@ -170,6 +172,42 @@ pa_status pa_decode_attention(void* out, const void* query, const void* k_pool, 
                               int32_t num_blocks, int32_t max_context_len, float scale,
                               int32_t partition_size, pa_dtype dtype, void* workspace,
                               size_t workspace_bytes, void* stream);
+
+/*
+ * pa_prefill_attention -- causal multi-token attention over a paged, partly
+ * cached context (chunked prefill, prefix reuse).
+ *
+ * When a prompt shares a cached prefix, only its new tokens run through
+ * prefill and read the prefix's KV pages instead of recomputing them
+ * (paged-KV analysis page, section 3.2 and the TTFT row of section 4.1).
+ * Sequence s holds L = context_lens[s] tokens in its pages, the last
+ * n = query_start[s+1] - query_start[s] of which are its new tokens, already
+ * written with pa_kv_append.  Query row query_start[s] + j is the token at
+ * position p = L - n + j; for q head h (KV head h / (Hq / Hkv)):
+ *     out[row][h] = sum_{t <= p} exp(s_t - max) v_t / sum_{t <= p} exp(s_t - max),
+ *     s_t = scale * <query[row][h], k_t>.
+ * n = 1 is decode attention.  Probabilities are rounded to dtype for the
+ * matrix-core product with V; accumulation is fp32; the output is rounded
+ * once (nearest even) to dtype.
+ *
+ *   out            DEVICE [num_tokens][num_q_heads][head_dim] of dtype
+ *   query          DEVICE [num_tokens][num_q_heads][head_dim] of dtype
+ *   k_pool, v_pool DEVICE pools (see above), read only
+ *   block_tables   DEVICE int32 [num_seqs][max_blocks_per_seq]
+ *   context_lens   DEVICE int32 [num_seqs]
+ *   query_start    DEVICE int32 [num_seqs + 1], non-decreasing, from 0 to
+ *                  num_tokens (packed new tokens of every sequence)
+ *   max_query_len  HOST upper bound of the per-sequence n (sizes the grid)
+ * dtype must be PA_F16 or PA_BF16 (PA_ERR_DTYPE otherwise).  Rows of a
+ * sequence with n > L, or past max_query_len, are not written; ranges outside
+ * [0, num_tokens) are skipped.  No workspace.
+ */
+pa_status pa_prefill_attention(void* out, const void* query, const void* k_pool, const void* v_pool,
+                               const int32_t* block_tables, const int32_t* context_lens,
+                               const int32_t* query_start, int32_t num_seqs, int32_t num_tokens,
+                               int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                               int32_t block_size, int32_t max_blocks_per_seq, int32_t num_blocks,
+                               int32_t max_query_len, float scale, pa_dtype dtype, void* stream);
 
 /*
  * pa_block_copy -- copy-on-write block duplication, all pairs in one launch.

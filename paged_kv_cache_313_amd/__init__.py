@@ -18,7 +18,7 @@ from . import _lib
 from ._lib import PA_PARTITION_BALANCED, PagedKVError, load  # noqa: F401
 from .block_manager import BlockManager  # noqa: F401
 
-__all__ = ["kv_append", "block_copy", "decode_attention", "decode_workspace_bytes",
+__all__ = ["kv_append", "block_copy", "decode_attention", "prefill_attention", "decode_workspace_bytes",
            "choose_partition", "swap_out", "swap_in", "swap_buffer", "PagedKVError", "load",
            "PA_PARTITION_BALANCED", "BlockManager"]
 
@@ -187,4 +187,37 @@ def decode_attention(query: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Te
                                  int(partition_size), _dtype_code(query), ws_ptr, ws_bytes,
                                  _stream(query, stream))
     _lib.check("pa_decode_attention", st)
+    return out
+
+
+def prefill_attention(query: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+                      block_tables: torch.Tensor, context_lens: torch.Tensor, query_start: torch.Tensor,
+                      scale: float, max_query_len: int, out: Optional[torch.Tensor] = None,
+                      stream=None) -> torch.Tensor:
+    """Causal attention of the packed new tokens ``query`` [T, Hq, D] over
+    their sequences' paged contexts.  ``query_start`` int32 [S + 1] packs the
+    sequences' new tokens; sequence s's are the last
+    query_start[s+1] - query_start[s] of its context_lens[s] tokens (already
+    appended).  ``max_query_len`` bounds the per-sequence count.  f16/bf16."""
+    lib = load()
+    T, Hq, D = query.shape
+    NB, Hkv, bs, D2 = k_pool.shape
+    S = context_lens.numel()
+    if D2 != D or v_pool.shape != k_pool.shape:
+        raise ValueError("head_dim mismatch between query and pools")
+    for t, name in ((block_tables, "block_tables"), (context_lens, "context_lens"), (query_start, "query_start")):
+        if t.dtype != torch.int32:
+            raise TypeError(f"{name} must be int32")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or query_start.numel() != S + 1:
+        raise ValueError("block_tables must be [S, max_blocks_per_seq] and query_start [S + 1]")
+    if not (query.dtype == k_pool.dtype == v_pool.dtype):
+        raise TypeError("query and pools must share a dtype")
+    if out is None:
+        out = torch.empty_like(query)
+    st = lib.pa_prefill_attention(_dev(out, "out"), _dev(query, "query"), _dev(k_pool, "k_pool"),
+                                  _dev(v_pool, "v_pool"), _dev(block_tables, "block_tables"),
+                                  _dev(context_lens, "context_lens"), _dev(query_start, "query_start"), S, T,
+                                  Hq, Hkv, D, bs, block_tables.shape[1], NB, int(max_query_len), float(scale),
+                                  _dtype_code(query), _stream(query, stream))
+    _lib.check("pa_prefill_attention", st)
     return out

@@ -19,7 +19,8 @@ BUILD_DIR = os.path.join(HERE, "_build")
 LIB_NAME = "libpagedkv.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 
-SOURCES = ["pa_api.cpp", "pa_block_manager.cpp", "pa_copy_kernels.hip", "pa_decode_kernels.hip"]
+SOURCES = ["pa_api.cpp", "pa_block_manager.cpp", "pa_copy_kernels.hip", "pa_decode_kernels.hip",
+           "pa_prefill_kernels.hip"]
 HEADERS = ["pa_common.hpp", "pa_launch.hpp"]
 ARCH = "gfx950"
 

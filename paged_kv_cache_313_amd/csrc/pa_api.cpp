@@ -181,6 +181,47 @@ PA_EXPORT pa_status pa_swap_in(const void* host_src, void* k_pool, void* v_pool,
                    block_size, head_dim, num_blocks, dtype, stream);
 }
 
+PA_EXPORT pa_status pa_prefill_attention(void* out, const void* query, const void* k_pool,
+                                         const void* v_pool, const int32_t* block_tables,
+                                         const int32_t* context_lens, const int32_t* query_start,
+                                         int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads,
+                                         int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                         int32_t max_blocks_per_seq, int32_t num_blocks,
+                                         int32_t max_query_len, float scale, pa_dtype dtype,
+                                         void* stream) {
+  if (!dtype_ok(dtype) || dtype == PA_F32) return PA_ERR_DTYPE;
+  if (!block_size_ok(block_size)) return PA_ERR_BLOCK_SIZE;
+  if (num_seqs < 0 || num_tokens < 0 || num_q_heads < 1 || num_kv_heads < 1 || !head_dim_ok(head_dim) ||
+      max_blocks_per_seq < 1 || num_blocks < 1 || max_query_len < 0)
+    return PA_ERR_SHAPE;
+  if (num_q_heads % num_kv_heads != 0 || !group_ok(num_q_heads / num_kv_heads)) return PA_ERR_SHAPE;
+  if (num_seqs == 0 || num_tokens == 0 || max_query_len == 0) return PA_OK;
+  if (!out || !query || !k_pool || !v_pool || !block_tables || !context_lens || !query_start)
+    return PA_ERR_NULL;
+  if (!aligned16(out) || !aligned16(query) || !aligned16(k_pool) || !aligned16(v_pool)) return PA_ERR_ALIGN;
+  const int32_t group = num_q_heads / num_kv_heads;
+  const int64_t qblocks = ((int64_t)max_query_len + 64 / group - 1) / (64 / group);
+  if ((int64_t)num_seqs * num_kv_heads * qblocks > INT32_MAX) return PA_ERR_SHAPE;
+  pa::PrefillArgs a{};
+  a.out = out;
+  a.query = query;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.query_start = query_start;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_blocks = num_blocks;
+  a.num_tokens = num_tokens;
+  a.max_query_len = max_query_len;
+  a.scale_log2 = scale * pa::kLog2e;
+  return hip_status(pa::launch_prefill(a, elem_of(dtype), head_dim, block_size, group,
+                                       reinterpret_cast<hipStream_t>(stream)));
+}
+
 PA_EXPORT size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                            int32_t head_dim, int32_t max_context_len,
                                            int32_t partition_size) {

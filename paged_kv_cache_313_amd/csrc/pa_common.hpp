@@ -155,6 +155,32 @@ template <> __device__ __forceinline__ void store_elem<F16>(void* base, size_t i
   reinterpret_cast<uint16_t*>(base)[idx] = f32_to_f16_rne(v);
 }
 
+// ---- matrix cores -----------------------------------------------------------
+// D[16x16] += A[16x32] B[32x16] in fp32.  Lane l supplies A row l % 16 and B
+// column l % 16, each as the 8 k-values 8 (l / 16) .. 8 (l / 16) + 7 packed in
+// 16 bytes; it receives D rows 4 (l / 16) .. 4 (l / 16) + 3 of column l % 16.
+template <class T>
+__device__ __forceinline__ f32x4 mfma_16x16x32(u32x4 a, u32x4 b, f32x4 c);
+template <>
+__device__ __forceinline__ f32x4 mfma_16x16x32<BF16>(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+template <>
+__device__ __forceinline__ f32x4 mfma_16x16x32<F16>(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+// two fp32 values rounded (to nearest even) into one packed 16-bit pair
+template <class T> __device__ __forceinline__ uint32_t pack2(float lo, float hi);
+template <> __device__ __forceinline__ uint32_t pack2<BF16>(float lo, float hi) {
+  return (uint32_t)f32_to_bf16_rne(lo) | ((uint32_t)f32_to_bf16_rne(hi) << 16);
+}
+template <> __device__ __forceinline__ uint32_t pack2<F16>(float lo, float hi) {
+  return (uint32_t)f32_to_f16_rne(lo) | ((uint32_t)f32_to_f16_rne(hi) << 16);
+}
+
 // ---- cross-lane moves -------------------------------------------------------
 // butterfly exchange with lane ^ mask (ds_swizzle / bpermute through the LDS crossbar
 // for masks >= 16, DPP for the in-row masks)
@@ -218,6 +244,23 @@ struct DecodeArgs {
   int32_t head_chunks;        // head groups per sequence (Hkv on the MFMA path)
   int32_t mode;               // kModeUnit or kModeBalanced
   float scale_log2;           // scale * log2(e)
+};
+
+// Arguments of the prefill kernel.
+struct PrefillArgs {
+  void* out;                    // [T, Hq, D] dtype
+  const void* query;            // [T, Hq, D] dtype
+  const void* k_pool;           // [NB, Hkv, BS, D]
+  const void* v_pool;
+  const int32_t* block_tables;  // [S, MB]
+  const int32_t* context_lens;  // [S]
+  const int32_t* query_start;   // [S + 1]
+  int32_t num_seqs, num_q_heads, num_kv_heads;
+  int32_t max_blocks_per_seq, num_blocks;
+  int32_t num_tokens;           // rows of query and out
+  int32_t max_query_len;        // host bound of query_start[s+1] - query_start[s]
+  int32_t qblocks;              // query blocks per (sequence, KV head) in the grid
+  float scale_log2;             // scale * log2(e)
 };
 
 __device__ __forceinline__ int clamp_len(const DecodeArgs& a, int s, int block_size) {

@@ -35,4 +35,8 @@ hipError_t balanced_grid(const void* kernel, int block_threads, int max_per_cu, 
 hipError_t launch_decode(const DecodeArgs& args, Elem elem, int head_dim, int block_size,
                          int group, hipStream_t stream);
 
+// Prefill over a cached prefix (f16/bf16, group size 1..16): one launch.
+hipError_t launch_prefill(const PrefillArgs& args, Elem elem, int head_dim, int block_size, int group,
+                          hipStream_t stream);
+
 }  // namespace pa
