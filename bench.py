@@ -52,6 +52,9 @@ def parse_args():
     ap.add_argument("--table-layout", default="shuffled", choices=["shuffled", "identity"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-swap", action="store_true", help="skip the swap (preemption traffic) leg")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the prefill leg")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="only time pa_prefill_attention on the chunked-prefill workload and print its line")
     ap.add_argument("--cpu-seconds", type=float, default=8.0, help="minimum wall time of the oracle timing")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB (5 times), the "
@@ -225,6 +228,65 @@ def block_manager_leg(b, steps: int) -> dict:
 
 
 HOST_LINK_PEAK_GBPS = 64.0   # PCIe 5.0 x16, one direction
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense bf16 matrix-core peak of MI355X
+PREFILL_WORKLOAD = ("chunked prefill over cached prefixes, Llama-3-8B-shaped: 16 seqs, 512 new tokens each "
+                    "on 4096-token contexts (3584 cached), 32q/8kv heads, D128, bf16, bs16, causal")
+
+
+def prefill_leg(reps: int = 20, parity_seqs=(0, 9)) -> dict:
+    """pa_prefill_attention on the chunked-prefill workload: HIP-event time per
+    call, causal TFLOP/s against the bf16 matrix-core peak, and every output
+    of two sampled sequences against the oracle."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_313_amd as P
+    from workloads import synth as W
+    from workloads import torch_io
+
+    S, n, L, Hq, Hkv, D, bs = 16, 512, 4096, 32, 8, 128, 16
+    b = W.make_decode_batch(313100, num_seqs=S, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, dtype="bf16",
+                            block_size=bs, context_lens=[L] * S, name="prefill")
+    rng = np.random.default_rng(313101)
+    q = W.to_storage(rng.standard_normal((S * n, Hq, D), dtype=np.float32), "bf16")
+    starts = np.arange(0, (S + 1) * n, n, dtype=np.int32)
+    d = torch_io.to_device(b)
+    qd = torch_io.storage_to_torch(q, "bf16", "cuda")
+    st = torch.from_numpy(starts).cuda()
+    out = torch.empty_like(qd)
+    stream = torch.cuda.current_stream()
+    f = lambda: P.prefill_attention(qd, d.k_pool, d.v_pool, d.block_tables, d.context_lens, st, b.scale, n,
+                                    out=out, stream=stream)
+    for _ in range(3):
+        f()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        f()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    keys = S * sum(L - n + j + 1 for j in range(n))          # (query token, key) pairs under the causal mask
+    flops = 4.0 * D * keys * Hq                               # QK^T and PV, 2 flops per multiply-add
+    tflops = flops / (ms * 1e-3) / 1e12
+    parity = None
+    if parity_seqs:
+        import oracle.pa_oracle as O
+        ref = O.prefill_attention(q, b.k_pool, b.v_pool, b.block_tables, b.context_lens, starts, b.scale, bs,
+                                  "bf16", seqs=list(parity_seqs))
+        got = O.upcast(torch_io.torch_to_storage(out, "bf16"), "bf16")
+        rows = np.concatenate([np.arange(starts[s], starts[s + 1]) for s in parity_seqs])
+        err = np.abs(got[rows] - ref[rows])
+        parity = {"max_abs_err": float(err.max()),
+                  "within_tolerance": bool((err <= 2e-2 + 1e-2 * np.abs(ref[rows])).all()),
+                  "checked": f"all outputs of sequences {list(parity_seqs)} vs the fp64 oracle"}
+    return {"workload": PREFILL_WORKLOAD, "ms": ms, "tflops": tflops, "flops_per_call": flops,
+            "roofline": {"bound": "mfma", "achieved": tflops, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": tflops / MFMA_BF16_PEAK_TFLOPS,
+                         "kernel": "pa_prefill_attention: prefill_kernel<BF16, 128, 4>"},
+            "parity": parity}
 
 
 def swap_leg(d, b, reps: int = 5, target_bytes: int = 1 << 30) -> dict:
@@ -297,6 +359,15 @@ def main():
         sys.exit(2)
     if args.calibrate_copy_mib:
         calibrate_copy(args.calibrate_copy_mib)
+        return
+    if args.prefill_only:
+        import torch
+        torch.cuda.set_device(0)
+        leg = prefill_leg(reps=args.steps, parity_seqs=() if args.no_cpu_baseline else (0, 9))
+        print(json.dumps({"metric": "prefill TFLOP/s (causal, bf16 matrix cores), 1 GPU", "value": leg["tflops"],
+                          "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "higher_is_better": True,
+                          "dtype": "bf16", "data": "synthetic", "config": {"workload": PREFILL_WORKLOAD},
+                          **leg}), flush=True)
         return
 
     import numpy as np
@@ -376,6 +447,7 @@ def main():
 
     bm_leg = block_manager_leg(b, max(args.steps, 10))
     swap = None if args.no_swap else swap_leg(d, b)
+    prefill = None if args.no_prefill else prefill_leg(parity_seqs=() if args.no_cpu_baseline else (0, 9))
 
     # parity of this run's output against the oracle run above (all sequences)
     parity = None
@@ -421,6 +493,7 @@ def main():
         "parity": parity,
         "block_manager": bm_leg,
         "swap": swap,
+        "prefill": prefill,
     }
     print(json.dumps(line), flush=True)
 

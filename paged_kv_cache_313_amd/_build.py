@@ -24,6 +24,11 @@ SOURCES = ["pa_api.cpp", "pa_block_manager.cpp", "pa_copy_kernels.hip", "pa_deco
 HEADERS = ["pa_common.hpp", "pa_launch.hpp"]
 ARCH = "gfx950"
 
+# Per-source additions.  The prefill kernel keeps its MFMA accumulators in
+# ordinary VGPRs: otherwise the compiler parks them in AGPRs and copies all of
+# them back and forth around the online-softmax rescale every key tile.
+SOURCE_FLAGS = {"pa_prefill_kernels.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
 COMPILE_FLAGS = [
     "-x", "hip", f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",
     "-Wall", "-Wno-unused-function",
@@ -58,7 +63,7 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     for src in SOURCES:
         obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
         objs.append(obj)
-        cmds.append([cc, *COMPILE_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        cmds.append([cc, *COMPILE_FLAGS, *SOURCE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj])
     with ThreadPoolExecutor(max_workers=max(1, min(jobs, len(cmds)))) as ex:
         logs = list(ex.map(_run, cmds))
     tmp = LIB_PATH + ".tmp"

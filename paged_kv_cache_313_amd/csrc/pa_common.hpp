@@ -174,8 +174,12 @@ __device__ __forceinline__ f32x4 mfma_16x16x32<F16>(u32x4 a, u32x4 b, f32x4 c) {
 
 // two fp32 values rounded (to nearest even) into one packed 16-bit pair
 template <class T> __device__ __forceinline__ uint32_t pack2(float lo, float hi);
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 template <> __device__ __forceinline__ uint32_t pack2<BF16>(float lo, float hi) {
-  return (uint32_t)f32_to_bf16_rne(lo) | ((uint32_t)f32_to_bf16_rne(hi) << 16);
+  // one v_cvt_pk_bf16_f32 on gfx950 (round to nearest even)
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 template <> __device__ __forceinline__ uint32_t pack2<F16>(float lo, float hi) {
   return (uint32_t)f32_to_f16_rne(lo) | ((uint32_t)f32_to_f16_rne(hi) << 16);

@@ -36,10 +36,30 @@ namespace pa {
 
 constexpr int kPfWaves = 4;
 constexpr int kPfThreads = kPfWaves * kWave;
-constexpr int kPfRows = kPfWaves * 16;   // query rows (token, head) per workgroup
-constexpr int kPfKeys = 32;              // keys per tile
+#ifndef PA_PREFILL_KEYS
+#define PA_PREFILL_KEYS 64
+#endif
+constexpr int kPfKeys = PA_PREFILL_KEYS;  // keys per tile (32 or 64)
+constexpr int kPfSub = kPfKeys / 16;     // 16-key score tiles per key tile
+static_assert(kPfKeys == 32 || kPfKeys == 64, "key tile");
 constexpr float kPfLazy = 8.f;
+// Row groups of 16 per wave: every K or V^T operand a wave reads from LDS
+// feeds NG matrix-core products, which keeps LDS traffic per product below
+// what the matrix cores consume (one 16x16x32 product needs a 1 KiB operand).
+#ifndef PA_PREFILL_GROUPS
+#define PA_PREFILL_GROUPS 2
+#endif
+// LDS operand reads issued this many reads ahead of the products that use
+// them (the compiler otherwise waits on each read right before its product)
+#ifndef PA_PREFILL_SCHED
+#define PA_PREFILL_SCHED 3
+#endif
+constexpr int kPfGroups = PA_PREFILL_GROUPS;
+constexpr int kPfRows = kPfWaves * 16 * kPfGroups;   // query rows (token, head) per workgroup
 
+// K is staged row-major.  V is staged transposed (row d holds the tile's keys
+// in order); a thread owns two consecutive keys of one 16-byte d-chunk, so it
+// writes a (key, key + 1) pair of each of its 8 d rows as one dword.
 template <int D>
 struct PfLayout {
   static constexpr int kRowB = D * 2 + 16;           // K row pitch in LDS (bytes), padded
@@ -47,15 +67,19 @@ struct PfLayout {
   static constexpr int kKBytes = kPfKeys * kRowB;
   static constexpr int kBufBytes = kKBytes + D * kVtB;
   static constexpr int CPR = D / 8;                  // 16-byte chunks per token row
-  static constexpr int NCH = kPfKeys * CPR / kPfThreads;   // chunks per thread per tile
-  static_assert(NCH * kPfThreads == kPfKeys * CPR, "tile split");
+  static constexpr int kPairs = kPfKeys / 2 * CPR;   // (key pair, d-chunk) units per tile
+  static constexpr bool kPartial = kPairs < kPfThreads;   // then threads >= kPairs load nothing
+  static constexpr int NPAIR = kPartial ? 1 : kPairs / kPfThreads;   // key pairs per thread per tile
+  static constexpr int NCH = 2 * NPAIR;              // chunks per thread per tile
+  static_assert(kPartial || NPAIR * kPfThreads == kPairs, "tile split");
 };
 
 template <class T, int D, int G>
 __global__ __launch_bounds__(kPfThreads) void prefill_kernel(PrefillArgs a, int block_size, int bs_shift) {
   using Lay = PfLayout<D>;
+  constexpr int NG = kPfGroups;
   constexpr int QB = kPfRows / G;          // query tokens per workgroup
-  constexpr int TPW = 16 / G;              // query tokens per wave
+  constexpr int TPW = 16 * NG / G;         // query tokens per wave
   constexpr int NKC = D / 32;              // k-chunks of the score MFMA
   constexpr int NDT = D / 16;              // 16-row d tiles of the output
   __shared__ __align__(16) char lds[2 * Lay::kBufBytes];
@@ -81,39 +105,55 @@ __global__ __launch_bounds__(kPfThreads) void prefill_kernel(PrefillArgs a, int 
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int c = lane & 15, gq = lane >> 4;
 
-  // this lane's query row (column c of the wave's MFMA tiles)
-  const int tq = qb * QB + wave * TPW + c / G;      // token index among the n new ones
-  const int hh = c % G;
-  const bool row_ok = tq < n;
-  const int pos = L - n + (row_ok ? tq : n - 1);
-  const int wave_last = L - n + min(qb * QB + (wave + 1) * TPW, n) - 1;   // wave's largest position
-  const int kend = L - n + min(qb * QB + QB, n);                          // keys the unit needs
-
-  u32x4 qop[NKC];
-  {
+  // this lane's query rows: column c of each of the wave's NG row groups;
+  // row r = 16 (NG wave + grp) + c of the workgroup is token r / G, head r % G
+  int tq[NG], pos[NG];
+  bool row_ok[NG];
+  u32x4 qop[NG][NKC];
+  const int hh = c % G;                  // the same head in every group (16 % G == 0)
+#pragma unroll
+  for (int grp = 0; grp < NG; ++grp) {
+    tq[grp] = qb * QB + (16 * (NG * wave + grp) + c) / G;
+    row_ok[grp] = tq[grp] < n;
+    pos[grp] = L - n + (row_ok[grp] ? tq[grp] : n - 1);
     const u32x4 z = {0u, 0u, 0u, 0u};
     const char* qrow = reinterpret_cast<const char*>(a.query) +
-                       (((size_t)(q0 + (row_ok ? tq : 0)) * a.num_q_heads + (size_t)g * G + hh) * D) * 2;
+                       (((size_t)(q0 + (row_ok[grp] ? tq[grp] : 0)) * a.num_q_heads + (size_t)g * G + hh) * D) * 2;
 #pragma unroll
-    for (int kc = 0; kc < NKC; ++kc) qop[kc] = row_ok ? ld16(qrow + (32 * kc + 8 * gq) * 2) : z;
+    for (int kc = 0; kc < NKC; ++kc) qop[grp][kc] = row_ok[grp] ? ld16(qrow + (32 * kc + 8 * gq) * 2) : z;
   }
+  const int wave_last = L - n + min(qb * QB + (wave + 1) * TPW, n) - 1;   // wave's largest position
+  const int kend = L - n + min(qb * QB + QB, n);                          // keys the unit needs
 
   const int32_t* trow = a.block_tables + (size_t)s * a.max_blocks_per_seq;
   const char* kpool = reinterpret_cast<const char*>(a.k_pool);
   const char* vpool = reinterpret_cast<const char*>(a.v_pool);
   const int bmask = block_size - 1;
 
+  // The table entries a tile needs are loaded one tile before its K/V, so
+  // the two dependent loads of a tile (entry, then data) overlap two tiles
+  // of compute.
   u32x4 kreg[Lay::NCH], vreg[Lay::NCH];
   bool vok[Lay::NCH];
+  int ids[Lay::NCH];
+  // chunk j of this thread: key pair jp = j / 2 (pairs dealt over the threads,
+  // d-chunk fastest so 16 lanes cover a row), key 2 (pair / CPR) + (j & 1)
+  auto chunk_key = [&](int j) { return 2 * (((j >> 1) * kPfThreads + tid) / Lay::CPR) + (j & 1); };
+  auto chunk_dch = [&](int j) { return ((j >> 1) * kPfThreads + tid) % Lay::CPR; };
+  const bool loader = !Lay::kPartial || tid < Lay::kPairs;
+  auto load_ids = [&](int t0) {
+    if (!loader) return;
+#pragma unroll
+    for (int j = 0; j < Lay::NCH; ++j) ids[j] = trow[min(t0 + chunk_key(j), L - 1) >> bs_shift];
+  };
   auto load_tile = [&](int t0) {
+    if (!loader) return;
 #pragma unroll
     for (int j = 0; j < Lay::NCH; ++j) {
-      const int ch = j * kPfThreads + tid;
-      const int key = ch / Lay::CPR, dch = ch % Lay::CPR;
+      const int key = chunk_key(j), dch = chunk_dch(j);
       const int t = t0 + key;
       const int tt = min(t, L - 1);
-      int blk = trow[tt >> bs_shift];
-      blk = ((unsigned)blk < (unsigned)a.num_blocks) ? blk : 0;
+      const int blk = ((unsigned)ids[j] < (unsigned)a.num_blocks) ? ids[j] : 0;
       const size_t off = ((((size_t)blk * a.num_kv_heads + g) * block_size + (tt & bmask)) * D + dch * 8) * 2;
       kreg[j] = ld16(kpool + off);
       vreg[j] = ld16(vpool + off);
@@ -121,103 +161,165 @@ __global__ __launch_bounds__(kPfThreads) void prefill_kernel(PrefillArgs a, int 
     }
   };
   auto store_tile = [&](int buf) {
+    if (!loader) return;
     char* kb = lds + buf * Lay::kBufBytes;
     char* vb = kb + Lay::kKBytes;
     const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int j = 0; j < Lay::NCH; ++j) {
-      const int ch = j * kPfThreads + tid;
-      const int key = ch / Lay::CPR, dch = ch % Lay::CPR;
-      *reinterpret_cast<u32x4*>(kb + key * Lay::kRowB + dch * 16) = kreg[j];
-      const u32x4 v = vok[j] ? vreg[j] : z;      // slots past the context may hold anything
+    for (int j = 0; j < Lay::NCH; ++j)
+      *reinterpret_cast<u32x4*>(kb + chunk_key(j) * Lay::kRowB + chunk_dch(j) * 16) = kreg[j];
+#pragma unroll
+    for (int jp = 0; jp < Lay::NPAIR; ++jp) {
+      const int key = chunk_key(2 * jp), dch = chunk_dch(2 * jp);   // keys key, key + 1
+      const u32x4 v0 = vok[2 * jp] ? vreg[2 * jp] : z;            // slots past the context
+      const u32x4 v1 = vok[2 * jp + 1] ? vreg[2 * jp + 1] : z;    // may hold anything
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const uint16_t x = (uint16_t)(v[e >> 1] >> ((e & 1) * 16));
-        *reinterpret_cast<uint16_t*>(vb + (dch * 8 + e) * Lay::kVtB + key * 2) = x;
+        // element e of both keys: low halves (even e) or high halves (odd e)
+        const uint32_t w = (e & 1) ? __builtin_amdgcn_perm(v1[e >> 1], v0[e >> 1], 0x07060302u)
+                                   : __builtin_amdgcn_perm(v1[e >> 1], v0[e >> 1], 0x05040100u);
+        *reinterpret_cast<uint32_t*>(vb + (dch * 8 + e) * Lay::kVtB + key * 2) = w;
       }
     }
   };
 
-  float m_run = kNegInf, l_run = 0.f;
-  f32x4 oacc[NDT];
+  float m_run[NG], l_run[NG];
+  f32x4 oacc[NG][NDT];
 #pragma unroll
-  for (int dt = 0; dt < NDT; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int grp = 0; grp < NG; ++grp) {
+    m_run[grp] = kNegInf;
+    l_run[grp] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) oacc[grp][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
 
   const int ntiles = (kend + kPfKeys - 1) / kPfKeys;
+  load_ids(0);
   load_tile(0);
   store_tile(0);
+  if (ntiles > 1) load_ids(kPfKeys);
   __syncthreads();
   for (int it = 0; it < ntiles; ++it) {
     const int t0 = it * kPfKeys;
     if (it + 1 < ntiles) load_tile(t0 + kPfKeys);
+    if (it + 2 < ntiles) load_ids(t0 + 2 * kPfKeys);
     if (t0 <= wave_last) {   // wave-uniform: some row of this wave sees a key of the tile
       const char* kb = lds + (it & 1) * Lay::kBufBytes;
       const char* vb = kb + Lay::kKBytes;
-      f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+      f32x4 st[NG][kPfSub];
+#pragma unroll
+      for (int grp = 0; grp < NG; ++grp)
+#pragma unroll
+        for (int sub = 0; sub < kPfSub; ++sub) st[grp][sub] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kc = 0; kc < NKC; ++kc) {
-        const u32x4 a0 = *reinterpret_cast<const u32x4*>(kb + c * Lay::kRowB + (32 * kc + 8 * gq) * 2);
-        const u32x4 a1 = *reinterpret_cast<const u32x4*>(kb + (16 + c) * Lay::kRowB + (32 * kc + 8 * gq) * 2);
-        s0 = mfma_16x16x32<T>(a0, qop[kc], s0);
-        s1 = mfma_16x16x32<T>(a1, qop[kc], s1);
+#pragma unroll
+        for (int sub = 0; sub < kPfSub; ++sub) {
+          const u32x4 ak =
+              *reinterpret_cast<const u32x4*>(kb + (16 * sub + c) * Lay::kRowB + (32 * kc + 8 * gq) * 2);
+#pragma unroll
+          for (int grp = 0; grp < NG; ++grp) st[grp][sub] = mfma_16x16x32<T>(ak, qop[grp][kc], st[grp][sub]);
+        }
       }
-      float sc[8];
+#if PA_PREFILL_SCHED > 0
+      // K operands PA_PREFILL_SCHED reads ahead of their products
+      __builtin_amdgcn_sched_group_barrier(0x100, PA_PREFILL_SCHED, 0);
+#pragma unroll
+      for (int r = 0; r < NKC * kPfSub; ++r) {
+        __builtin_amdgcn_sched_group_barrier(0x008, NG, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+#endif
+      // lane holds keys 16 sub + 4 gq + i; k-slot 8 gq + j of PV product h
+      // (keys [32 h, 32 h + 32)) means key 32 h + 4 gq + j (j < 4) or
+      // 32 h + 16 + 4 gq + j - 4
+      u32x4 pb[NG][kPfSub / 2];
       const int kt = t0 + 4 * gq;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        sc[i] = (kt + i <= pos) ? s0[i] * a.scale_log2 : kNegInf;
-        sc[4 + i] = (kt + 16 + i <= pos) ? s1[i] * a.scale_log2 : kNegInf;
+      for (int grp = 0; grp < NG; ++grp) {
+        float sc[4 * kPfSub];
+#pragma unroll
+        for (int sub = 0; sub < kPfSub; ++sub)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            sc[4 * sub + i] = (kt + 16 * sub + i <= pos[grp]) ? st[grp][sub][i] * a.scale_log2 : kNegInf;
+        float tmax = sc[0];
+#pragma unroll
+        for (int i = 1; i < 4 * kPfSub; ++i) tmax = fmaxf(tmax, sc[i]);
+        tmax = fmaxf(tmax, xor_lane<16>(tmax));
+        tmax = fmaxf(tmax, xor_lane<32>(tmax));
+        const bool grow = tmax > m_run[grp] + kPfLazy;    // always true on a row's first key
+        if (__any(grow)) {
+          const float m_new = grow ? tmax : m_run[grp];
+          const float alpha = grow ? fast_exp2(m_run[grp] - m_new) : 1.f;
+          m_run[grp] = m_new;
+          l_run[grp] *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt) oacc[grp][dt] *= alpha;
+        }
+        float p[4 * kPfSub];
+#pragma unroll
+        for (int i = 0; i < 4 * kPfSub; ++i) {
+          p[i] = sc[i] == kNegInf ? 0.f : fast_exp2(sc[i] - m_run[grp]);
+          l_run[grp] += p[i];
+        }
+#pragma unroll
+        for (int h = 0; h < kPfSub / 2; ++h) {
+          pb[grp][h][0] = pack2<T>(p[8 * h + 0], p[8 * h + 1]);
+          pb[grp][h][1] = pack2<T>(p[8 * h + 2], p[8 * h + 3]);
+          pb[grp][h][2] = pack2<T>(p[8 * h + 4], p[8 * h + 5]);
+          pb[grp][h][3] = pack2<T>(p[8 * h + 6], p[8 * h + 7]);
+        }
       }
-      float tmax = sc[0];
-#pragma unroll
-      for (int i = 1; i < 8; ++i) tmax = fmaxf(tmax, sc[i]);
-      tmax = fmaxf(tmax, xor_lane<16>(tmax));
-      tmax = fmaxf(tmax, xor_lane<32>(tmax));
-      const bool grow = tmax > m_run + kPfLazy;    // always true on a row's first key
-      if (__any(grow)) {
-        const float m_new = grow ? tmax : m_run;
-        const float alpha = grow ? fast_exp2(m_run - m_new) : 1.f;
-        m_run = m_new;
-        l_run *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) oacc[dt] *= alpha;
-      }
-      float p[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        p[i] = sc[i] == kNegInf ? 0.f : fast_exp2(sc[i] - m_run);
-        l_run += p[i];
-      }
-      u32x4 pb;
-      pb[0] = pack2<T>(p[0], p[1]);
-      pb[1] = pack2<T>(p[2], p[3]);
-      pb[2] = pack2<T>(p[4], p[5]);
-      pb[3] = pack2<T>(p[6], p[7]);
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
+      // V^T operands one step ahead of their products, so LDS latency
+      // overlaps the matrix cores instead of preceding each product
+      constexpr int NVS = NDT * (kPfSub / 2);
+      auto read_v = [&](int step) {
+        const int dt = step / (kPfSub / 2), h = step % (kPfSub / 2);
         const char* vrow = vb + (16 * dt + c) * Lay::kVtB;
-        const uint2 lo = *reinterpret_cast<const uint2*>(vrow + (4 * gq) * 2);
-        const uint2 hi = *reinterpret_cast<const uint2*>(vrow + (16 + 4 * gq) * 2);
-        const u32x4 av = {lo.x, lo.y, hi.x, hi.y};
-        oacc[dt] = mfma_16x16x32<T>(av, pb, oacc[dt]);
+        const uint2 lo = *reinterpret_cast<const uint2*>(vrow + (32 * h + 4 * gq) * 2);
+        const uint2 hi = *reinterpret_cast<const uint2*>(vrow + (32 * h + 16 + 4 * gq) * 2);
+        return u32x4{lo.x, lo.y, hi.x, hi.y};
+      };
+      u32x4 av = read_v(0);
+#pragma unroll
+      for (int step = 0; step < NVS; ++step) {
+        const u32x4 nxt = read_v(step + 1 < NVS ? step + 1 : step);
+        const int dt = step / (kPfSub / 2), h = step % (kPfSub / 2);
+#pragma unroll
+        for (int grp = 0; grp < NG; ++grp) oacc[grp][dt] = mfma_16x16x32<T>(av, pb[grp][h], oacc[grp][dt]);
+        av = nxt;
       }
+#if PA_PREFILL_SCHED > 0
+      // keep each V^T read PA_PREFILL_SCHED products ahead of its use
+      __builtin_amdgcn_sched_group_barrier(0x100, PA_PREFILL_SCHED, 0);
+#pragma unroll
+      for (int step = 0; step < NVS; ++step) {
+        __builtin_amdgcn_sched_group_barrier(0x008, NG, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+#endif
     }
     if (it + 1 < ntiles) store_tile((it + 1) & 1);   // the other buffer: free since the last barrier
     __syncthreads();
   }
 
-  l_run += xor_lane<16>(l_run);
-  l_run += xor_lane<32>(l_run);
-  if (!row_ok) return;
-  const float inv = 1.f / l_run;
-  char* orow = reinterpret_cast<char*>(a.out) +
-               (((size_t)(q0 + tq) * a.num_q_heads + (size_t)g * G + hh) * D) * 2;
 #pragma unroll
-  for (int dt = 0; dt < NDT; ++dt) {
-    uint2 w;
-    w.x = pack2<T>(oacc[dt][0] * inv, oacc[dt][1] * inv);
-    w.y = pack2<T>(oacc[dt][2] * inv, oacc[dt][3] * inv);
-    *reinterpret_cast<uint2*>(orow + (16 * dt + 4 * gq) * 2) = w;
+  for (int grp = 0; grp < NG; ++grp) {
+    float l = l_run[grp];
+    l += xor_lane<16>(l);
+    l += xor_lane<32>(l);
+    if (!row_ok[grp]) continue;
+    const float inv = 1.f / l;
+    char* orow = reinterpret_cast<char*>(a.out) +
+                 (((size_t)(q0 + tq[grp]) * a.num_q_heads + (size_t)g * G + hh) * D) * 2;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      uint2 w;
+      w.x = pack2<T>(oacc[grp][dt][0] * inv, oacc[grp][dt][1] * inv);
+      w.y = pack2<T>(oacc[grp][dt][2] * inv, oacc[grp][dt][3] * inv);
+      *reinterpret_cast<uint2*>(orow + (16 * dt + 4 * gq) * 2) = w;
+    }
   }
 }
 
