@@ -35,6 +35,9 @@ What it computes, and where the pages define it:
   causally over its whole paged context, shared prefix pages included
   (paged-KV analysis page, sections 3.2 and 4.1).  Token at position p reads
   tokens t <= p.  Written out as masked dense attention per (sequence, head).
+* Two-level tables -- large pages (aligned runs of H blocks) for a prompt,
+  small blocks for what follows (Cross-Paper Synthesis page, section 5):
+  expanded into a flat table, then the definitions above.
 * Swap out / swap in -- preemption evicts all blocks of a request to host
   memory and brings them back later (Cross-Paper Synthesis page, section 3);
   the host copy is block-first (vLLM entity page, key observations).  Byte
@@ -259,6 +262,48 @@ def prefill_attention(query, k_pool, v_pool, block_tables, context_lens, query_s
                 scores[np.arange(L)[None, :] > pos[:, None]] = -np.inf
                 out[q0:q1, h] = attention_weights(scores) @ values
     return out
+
+
+def expand_hier_tables(large_tables, num_large, small_tables, pages_per_large: int) -> np.ndarray:
+    """Two-level (hierarchical) block tables as one flat block table.
+
+    The pages propose two page granularities at once, like an OS's huge and
+    small pages: large pages where a sequence's prompt is written in one go
+    (fewer table entries), small blocks where it grows token by token (less
+    fragmentation) (Cross-Paper Synthesis page, section 5, the adaptive block
+    size item).  Reading: a large page is an aligned run of H =
+    pages_per_large consecutive blocks of the one pool, large page P covering
+    blocks [P H, P H + H).  Sequence s's first num_large[s] * H logical blocks
+    live in its large pages, the rest in its small blocks:
+        entry j = large_tables[s][j // H] * H + j % H      if j < num_large[s] * H
+                = small_tables[s][j - num_large[s] * H]    otherwise."""
+    large_tables = np.asarray(large_tables)
+    small_tables = np.asarray(small_tables)
+    S = small_tables.shape[0]
+    H = int(pages_per_large)
+    width = int(np.max(np.asarray(num_large))) * H + small_tables.shape[1] if S else 0
+    flat = np.full((S, width), -1, dtype=np.int64)
+    for s in range(S):
+        nl = int(num_large[s])
+        for j in range(nl * H):
+            flat[s, j] = int(large_tables[s, j // H]) * H + j % H
+        flat[s, nl * H:nl * H + small_tables.shape[1]] = small_tables[s]
+    return flat
+
+
+def decode_attention_hier(query, k_pool, v_pool, large_tables, num_large, small_tables, pages_per_large,
+                          context_lens, scale, block_size, dtype=None, seqs=None) -> np.ndarray:
+    """Decode attention through two-level tables: the flat expansion above,
+    then the same definition as :func:`decode_attention`."""
+    flat = expand_hier_tables(large_tables, num_large, small_tables, pages_per_large)
+    return decode_attention(query, k_pool, v_pool, flat, context_lens, scale, block_size, dtype, seqs=seqs)
+
+
+def prefill_attention_hier(query, k_pool, v_pool, large_tables, num_large, small_tables, pages_per_large,
+                           context_lens, query_start, scale, block_size, dtype=None, seqs=None) -> np.ndarray:
+    flat = expand_hier_tables(large_tables, num_large, small_tables, pages_per_large)
+    return prefill_attention(query, k_pool, v_pool, flat, context_lens, query_start, scale, block_size, dtype,
+                             seqs=seqs)
 
 
 def attend_partitioned(q_rows, keys, values, scale, partition_size: int) -> np.ndarray:

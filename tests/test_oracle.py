@@ -537,3 +537,42 @@ def test_prefill_planted_mistakes_are_caught():
     topleft = sc.copy(); topleft[np.arange(30)[None, :] > np.arange(8)[:, None]] = -np.inf
     assert not np.allclose(O.attention_weights(strict) @ vals, good[:, 0])
     assert not np.allclose(O.attention_weights(topleft) @ vals, good[:, 0])
+
+
+# -- two-level (large page + small block) tables --------------------------------
+
+def test_hier_tables_hand_example():
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "hier_tables.json")))
+    flat = O.expand_hier_tables(np.array(g["large_tables"]), g["num_large"], np.array(g["small_tables"]),
+                                g["pages_per_large"])
+    for s, want in enumerate(g["flat_prefixes"]):
+        assert flat[s, :len(want)].tolist() == want
+
+
+def test_hier_decode_reads_tokens_where_the_pages_put_them():
+    """Brute force: write each token's K/V at the physical place the two-level
+    rule gives (large page run, then small blocks), attend through the
+    hierarchical tables, and compare with plain attention over the logical
+    token sequence."""
+    rng = np.random.default_rng(21)
+    H, bs, D, NB = 2, 4, 8, 40
+    L = [19, 6]
+    nl = [2, 0]                                   # 2 large pages = 16 tokens for seq 0
+    large = np.array([[7, 3], [-1, -1]])          # blocks 14,15 and 6,7
+    small = np.array([[30, -1], [11, 25]])
+    kp = np.full((NB, 1, bs, D), np.nan, dtype=np.float32)
+    vp = np.full((NB, 1, bs, D), np.nan, dtype=np.float32)
+    keys = [rng.standard_normal((n, D)).astype(np.float32).astype(np.float64) for n in L]
+    vals = [rng.standard_normal((n, D)).astype(np.float32).astype(np.float64) for n in L]
+    for s in range(2):
+        for t in range(L[s]):
+            j, o = divmod(t, bs)
+            blk = large[s, j // H] * H + j % H if j < nl[s] * H else small[s, j - nl[s] * H]
+            kp[blk, 0, o] = keys[s][t]
+            vp[blk, 0, o] = vals[s][t]
+    q = rng.standard_normal((2, 1, D)).astype(np.float32)
+    out = O.decode_attention_hier(q, kp, vp, large, nl, small, H, np.array(L), 0.3, bs, "f32")
+    for s in range(2):
+        sc = keys[s] @ q[s, 0].astype(np.float64) * float(np.float32(0.3))
+        w = np.exp(sc - sc.max())
+        assert np.allclose(out[s, 0], (w @ vals[s]) / w.sum(), atol=1e-12, rtol=0)
