@@ -49,7 +49,9 @@ def parse_args():
     ap.add_argument("--config", type=int, default=3, choices=sorted(WORKLOADS))
     ap.add_argument("--block-size", type=int, default=16, help="block size of the long-context workload")
     ap.add_argument("--partition", type=int, default=None, help="partition size (default: library choice)")
-    ap.add_argument("--table-layout", default="shuffled", choices=["shuffled", "identity"])
+    ap.add_argument("--table-layout", default="shuffled", choices=["shuffled", "identity", "hier"],
+                    help="physical layout: shuffled blocks, identity (contiguous) tables, or two-level tables "
+                         "with the prompt in 256-token large pages")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-swap", action="store_true", help="skip the swap (preemption traffic) leg")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill leg")
@@ -73,14 +75,27 @@ def calibrate_copy(mib):
     print(json.dumps({"calibration_copy_bytes": n, "launches": 5}), flush=True)
 
 
+LARGE_PAGE_BLOCKS = 16   # two-level layout: 256-token large pages at bs 16
+
+
 def make_batch(args):
     from workloads import synth as W
     kw = {}
+    hier = args.table_layout == "hier"
     if args.config in (2, 3, 5):
-        kw["table_layout"] = args.table_layout
+        kw["table_layout"] = "shuffled" if hier else args.table_layout
     if args.config == 5:
-        return W.config5(block_size=args.block_size, **kw)
-    return W.CONFIGS[args.config](**kw)
+        b = W.config5(block_size=args.block_size, **kw)
+    else:
+        b = W.CONFIGS[args.config](**kw)
+    if hier:
+        if b.block_mapping is not None and len(b.block_mapping):
+            raise SystemExit("--table-layout hier: not for the copy-on-write workload")
+        # everything before the step's appended token is the prompt: large pages
+        hb, large, nl = W.to_hierarchical(b, LARGE_PAGE_BLOCKS, b.context_lens - 1, seed=313009)
+        hb.meta["hier"] = (large, nl, LARGE_PAGE_BLOCKS)
+        return hb
+    return b
 
 
 # ----------------------------------------------------------------------------- CPU oracle leg
@@ -117,6 +132,10 @@ def cpu_baseline(b, min_seconds):
     import oracle.pa_oracle as O
     global _CPU_BATCH
     cores = max(1, min(len(os.sched_getaffinity(0)), 16))
+    if "hier" in b.meta:     # the oracle reads two-level tables through their flat expansion
+        import dataclasses
+        large, nl, H = b.meta["hier"]
+        b = dataclasses.replace(b, block_tables=O.expand_hier_tables(large, nl, b.block_tables, H))
     # pools after the step (oracle copies + appends); the timed loop redoes them
     k, v = b.k_pool, b.v_pool
     if b.block_mapping is not None and len(b.block_mapping):
@@ -160,7 +179,13 @@ def algorithmic_bytes(b):
     L = b.context_lens.astype(np.int64)
     kv = b.kv_bytes()
     qo = 2 * b.num_seqs * b.num_q_heads * b.head_dim * b.elt_bytes
-    tbl = int((-(-L // b.block_size)).sum()) * 4 + b.num_seqs * 4
+    nblk = -(-L // b.block_size)
+    if "hier" in b.meta:       # large-page entries, small entries and the large-page counts
+        _, nl, H = b.meta["hier"]
+        nl = nl.astype(np.int64)
+        tbl = int((nl + nblk - nl * H).sum()) * 4 + b.num_seqs * 8
+    else:
+        tbl = int(nblk.sum()) * 4 + b.num_seqs * 4
     return kv + qo + tbl, kv
 
 
@@ -401,6 +426,10 @@ def main():
     out = torch.empty_like(d.query)
     stream = torch.cuda.current_stream(dev)
     has_copy = b.block_mapping is not None and len(b.block_mapping) > 0
+    hier = None
+    if "hier" in b.meta:
+        large, nl, H = b.meta["hier"]
+        hier = (torch.from_numpy(large).to(dev), torch.from_numpy(nl).to(dev), H)
     has_append = b.new_key is not None
 
     ev = {"dec0": [], "dec1": [], "app0": [], "app1": [], "cp0": [], "cp1": []}
@@ -420,8 +449,13 @@ def main():
                 e = torch.cuda.Event(enable_timing=True); e.record(stream); ev["app1"].append(e)
         if record:
             e = torch.cuda.Event(enable_timing=True); e.record(stream); ev["dec0"].append(e)
-        P.decode_attention(d.query, d.k_pool, d.v_pool, d.block_tables, d.context_lens, b.scale,
-                           b.max_context_len, part, out=out, workspace=ws, stream=stream)
+        if hier:
+            P.decode_attention_hier(d.query, d.k_pool, d.v_pool, d.block_tables, hier[0], hier[1], hier[2],
+                                    d.context_lens, b.scale, b.max_context_len, part, out=out, workspace=ws,
+                                    stream=stream)
+        else:
+            P.decode_attention(d.query, d.k_pool, d.v_pool, d.block_tables, d.context_lens, b.scale,
+                               b.max_context_len, part, out=out, workspace=ws, stream=stream)
         if record:
             e = torch.cuda.Event(enable_timing=True); e.record(stream); ev["dec1"].append(e)
 

@@ -210,6 +210,46 @@ pa_status pa_prefill_attention(void* out, const void* query, const void* k_pool,
                                int32_t max_query_len, float scale, pa_dtype dtype, void* stream);
 
 /*
+ * pa_decode_attention_hier / pa_prefill_attention_hier -- the same operations
+ * as pa_decode_attention / pa_prefill_attention over two-level tables.
+ *
+ * Two page granularities at once, like an OS's huge and small pages: large
+ * pages where a prompt is written in one go (fewer table entries), small
+ * blocks where a sequence grows token by token (less fragmentation)
+ * (Cross-Paper Synthesis page, section 5, the adaptive block size item).  A
+ * large page is an aligned run of H = pages_per_large consecutive blocks of
+ * the same pools, large page P covering blocks [P H, P H + H).  Sequence s's
+ * logical block j (tokens [j bs, (j + 1) bs)) is
+ *     large_tables[s][j / H] * H + j % H    for j < num_large[s] * H,
+ *     small_tables[s][j - num_large[s] * H] otherwise.
+ *
+ *   small_tables   DEVICE int32 [num_seqs][max_small_per_seq]
+ *   large_tables   DEVICE int32 [num_seqs][max_large_per_seq] (large-page ids)
+ *   num_large      DEVICE int32 [num_seqs], clamped to [0, max_large_per_seq]
+ *   pages_per_large H, a power of two in [1, 1024]
+ * Lengths are clamped to (num_large[s] * H + max_small_per_seq) * block_size.
+ * All other arguments, the workspace and the errors are those of the flat
+ * calls.
+ */
+pa_status pa_decode_attention_hier(void* out, const void* query, const void* k_pool, const void* v_pool,
+                                   const int32_t* small_tables, const int32_t* large_tables,
+                                   const int32_t* num_large, const int32_t* context_lens, int32_t num_seqs,
+                                   int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                   int32_t block_size, int32_t max_small_per_seq, int32_t max_large_per_seq,
+                                   int32_t pages_per_large, int32_t num_blocks, int32_t max_context_len,
+                                   float scale, int32_t partition_size, pa_dtype dtype, void* workspace,
+                                   size_t workspace_bytes, void* stream);
+
+pa_status pa_prefill_attention_hier(void* out, const void* query, const void* k_pool, const void* v_pool,
+                                    const int32_t* small_tables, const int32_t* large_tables,
+                                    const int32_t* num_large, const int32_t* context_lens,
+                                    const int32_t* query_start, int32_t num_seqs, int32_t num_tokens,
+                                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                    int32_t block_size, int32_t max_small_per_seq, int32_t max_large_per_seq,
+                                    int32_t pages_per_large, int32_t num_blocks, int32_t max_query_len,
+                                    float scale, pa_dtype dtype, void* stream);
+
+/*
  * pa_block_copy -- copy-on-write block duplication, all pairs in one launch.
  *
  * Shared blocks (parallel samples, beams, common prompts) are reference

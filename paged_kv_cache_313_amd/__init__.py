@@ -18,7 +18,8 @@ from . import _lib
 from ._lib import PA_PARTITION_BALANCED, PagedKVError, load  # noqa: F401
 from .block_manager import BlockManager  # noqa: F401
 
-__all__ = ["kv_append", "block_copy", "decode_attention", "prefill_attention", "decode_workspace_bytes",
+__all__ = ["kv_append", "block_copy", "decode_attention", "prefill_attention", "decode_attention_hier",
+           "prefill_attention_hier", "decode_workspace_bytes",
            "choose_partition", "swap_out", "swap_in", "swap_buffer", "PagedKVError", "load",
            "PA_PARTITION_BALANCED", "BlockManager"]
 
@@ -220,4 +221,78 @@ def prefill_attention(query: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.T
                                   Hq, Hkv, D, bs, block_tables.shape[1], NB, int(max_query_len), float(scale),
                                   _dtype_code(query), _stream(query, stream))
     _lib.check("pa_prefill_attention", st)
+    return out
+
+
+def _hier_args(small_tables, large_tables, num_large, S):
+    for t, name in ((small_tables, "small_tables"), (large_tables, "large_tables"), (num_large, "num_large")):
+        if t.dtype != torch.int32:
+            raise TypeError(f"{name} must be int32")
+    if (small_tables.dim() != 2 or large_tables.dim() != 2 or small_tables.shape[0] != S
+            or large_tables.shape[0] != S or num_large.numel() != S):
+        raise ValueError("small_tables [S, MS], large_tables [S, ML] and num_large [S] expected")
+
+
+def decode_attention_hier(query, k_pool, v_pool, small_tables, large_tables, num_large, pages_per_large: int,
+                          context_lens, scale: float, max_context_len: int, partition_size: Optional[int] = None,
+                          out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                          stream=None) -> torch.Tensor:
+    """decode_attention over two-level tables: a sequence's first
+    num_large[s] * H logical blocks are its large pages (large page P = blocks
+    [P H, P H + H) of the pools), the rest its small blocks."""
+    lib = load()
+    S, Hq, D = query.shape
+    NB, Hkv, bs, D2 = k_pool.shape
+    if D2 != D or v_pool.shape != k_pool.shape:
+        raise ValueError("head_dim mismatch between query and pools")
+    _hier_args(small_tables, large_tables, num_large, S)
+    if context_lens.dtype != torch.int32 or context_lens.numel() != S:
+        raise ValueError("context_lens must be int32 [S]")
+    if not (query.dtype == k_pool.dtype == v_pool.dtype):
+        raise TypeError("query and pools must share a dtype")
+    if partition_size is None:
+        partition_size = choose_partition(S, Hkv, max_context_len, bs)
+    if out is None:
+        out = torch.empty_like(query)
+    need = decode_workspace_bytes(S, Hq, Hkv, D, max_context_len, partition_size)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=query.device)
+    ws_ptr = _dev(workspace, "workspace") if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib.pa_decode_attention_hier(_dev(out, "out"), _dev(query, "query"), _dev(k_pool, "k_pool"),
+                                      _dev(v_pool, "v_pool"), _dev(small_tables, "small_tables"),
+                                      _dev(large_tables, "large_tables"), _dev(num_large, "num_large"),
+                                      _dev(context_lens, "context_lens"), S, Hq, Hkv, D, bs, small_tables.shape[1],
+                                      large_tables.shape[1], int(pages_per_large), NB, int(max_context_len),
+                                      float(scale), int(partition_size), _dtype_code(query), ws_ptr, ws_bytes,
+                                      _stream(query, stream))
+    _lib.check("pa_decode_attention_hier", st)
+    return out
+
+
+def prefill_attention_hier(query, k_pool, v_pool, small_tables, large_tables, num_large, pages_per_large: int,
+                           context_lens, query_start, scale: float, max_query_len: int,
+                           out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """prefill_attention over two-level tables (see decode_attention_hier)."""
+    lib = load()
+    T, Hq, D = query.shape
+    NB, Hkv, bs, D2 = k_pool.shape
+    S = context_lens.numel()
+    if D2 != D or v_pool.shape != k_pool.shape:
+        raise ValueError("head_dim mismatch between query and pools")
+    _hier_args(small_tables, large_tables, num_large, S)
+    if context_lens.dtype != torch.int32 or query_start.dtype != torch.int32 or query_start.numel() != S + 1:
+        raise ValueError("context_lens int32 [S] and query_start int32 [S + 1] expected")
+    if not (query.dtype == k_pool.dtype == v_pool.dtype):
+        raise TypeError("query and pools must share a dtype")
+    if out is None:
+        out = torch.empty_like(query)
+    st = lib.pa_prefill_attention_hier(_dev(out, "out"), _dev(query, "query"), _dev(k_pool, "k_pool"),
+                                       _dev(v_pool, "v_pool"), _dev(small_tables, "small_tables"),
+                                       _dev(large_tables, "large_tables"), _dev(num_large, "num_large"),
+                                       _dev(context_lens, "context_lens"), _dev(query_start, "query_start"), S, T,
+                                       Hq, Hkv, D, bs, small_tables.shape[1], large_tables.shape[1],
+                                       int(pages_per_large), NB, int(max_query_len), float(scale),
+                                       _dtype_code(query), _stream(query, stream))
+    _lib.check("pa_prefill_attention_hier", st)
     return out

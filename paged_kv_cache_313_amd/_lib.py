@@ -31,6 +31,12 @@ SIGNATURES = {
                                      _c_size, _vp]),
     "pa_prefill_attention": (_c_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_i32, _c_i32, _c_i32, _c_i32,
                                       _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_f32, _c_i32, _vp]),
+    "pa_decode_attention_hier": (_c_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_i32, _c_i32, _c_i32,
+                                          _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_f32,
+                                          _c_i32, _c_i32, _vp, _c_size, _vp]),
+    "pa_prefill_attention_hier": (_c_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_i32, _c_i32, _c_i32,
+                                           _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
+                                           _c_f32, _c_i32, _vp]),
     "pa_block_copy": (_c_i32, [_vp, _vp, _vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _vp]),
     "pa_swap_out": (_c_i32, [_vp, _vp, _vp, _c_i32, _vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _vp]),
     "pa_swap_in": (_c_i32, [_vp, _vp, _vp, _vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _vp]),

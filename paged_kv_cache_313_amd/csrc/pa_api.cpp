@@ -181,14 +181,34 @@ PA_EXPORT pa_status pa_swap_in(const void* host_src, void* k_pool, void* v_pool,
                    block_size, head_dim, num_blocks, dtype, stream);
 }
 
-PA_EXPORT pa_status pa_prefill_attention(void* out, const void* query, const void* k_pool,
-                                         const void* v_pool, const int32_t* block_tables,
-                                         const int32_t* context_lens, const int32_t* query_start,
-                                         int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads,
-                                         int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
-                                         int32_t max_blocks_per_seq, int32_t num_blocks,
-                                         int32_t max_query_len, float scale, pa_dtype dtype,
-                                         void* stream) {
+// Two-level tables: the large-page arguments of the *_hier entry points.
+struct HierTables {
+  const int32_t* large_tables = nullptr;
+  const int32_t* num_large = nullptr;
+  int32_t max_large_per_seq = 0;
+  int32_t shift = 0;
+};
+
+// Host checks of the large-page arguments; fills h.shift.
+static pa_status check_hier(HierTables& h, int32_t pages_per_large, int32_t max_blocks_per_seq,
+                            int32_t block_size) {
+  if (!h.large_tables || !h.num_large) return PA_ERR_NULL;
+  if (h.max_large_per_seq < 1 || pages_per_large < 1 || pages_per_large > 1024 ||
+      (pages_per_large & (pages_per_large - 1)) != 0)
+    return PA_ERR_SHAPE;
+  while ((1 << h.shift) < pages_per_large) ++h.shift;
+  const int64_t tokens = ((int64_t)h.max_large_per_seq * pages_per_large + max_blocks_per_seq) * block_size;
+  if (tokens > INT32_MAX) return PA_ERR_SHAPE;
+  return PA_OK;
+}
+
+static pa_status prefill_impl(void* out, const void* query, const void* k_pool, const void* v_pool,
+                              const int32_t* block_tables, const int32_t* context_lens,
+                              const int32_t* query_start, int32_t num_seqs, int32_t num_tokens,
+                              int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                              int32_t block_size, int32_t max_blocks_per_seq, int32_t num_blocks,
+                              int32_t max_query_len, float scale, pa_dtype dtype, void* stream,
+                              const HierTables& hier) {
   if (!dtype_ok(dtype) || dtype == PA_F32) return PA_ERR_DTYPE;
   if (!block_size_ok(block_size)) return PA_ERR_BLOCK_SIZE;
   if (num_seqs < 0 || num_tokens < 0 || num_q_heads < 1 || num_kv_heads < 1 || !head_dim_ok(head_dim) ||
@@ -218,8 +238,48 @@ PA_EXPORT pa_status pa_prefill_attention(void* out, const void* query, const voi
   a.num_tokens = num_tokens;
   a.max_query_len = max_query_len;
   a.scale_log2 = scale * pa::kLog2e;
+  a.large_tables = hier.large_tables;
+  a.num_large = hier.num_large;
+  a.max_large_per_seq = hier.max_large_per_seq;
+  a.large_shift = hier.shift;
   return hip_status(pa::launch_prefill(a, elem_of(dtype), head_dim, block_size, group,
                                        reinterpret_cast<hipStream_t>(stream)));
+}
+
+PA_EXPORT pa_status pa_prefill_attention(void* out, const void* query, const void* k_pool,
+                                         const void* v_pool, const int32_t* block_tables,
+                                         const int32_t* context_lens, const int32_t* query_start,
+                                         int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads,
+                                         int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                         int32_t max_blocks_per_seq, int32_t num_blocks,
+                                         int32_t max_query_len, float scale, pa_dtype dtype,
+                                         void* stream) {
+  return prefill_impl(out, query, k_pool, v_pool, block_tables, context_lens, query_start, num_seqs,
+                      num_tokens, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                      num_blocks, max_query_len, scale, dtype, stream, HierTables{});
+}
+
+PA_EXPORT pa_status pa_prefill_attention_hier(void* out, const void* query, const void* k_pool,
+                                              const void* v_pool, const int32_t* small_tables,
+                                              const int32_t* large_tables, const int32_t* num_large,
+                                              const int32_t* context_lens, const int32_t* query_start,
+                                              int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads,
+                                              int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                              int32_t max_small_per_seq, int32_t max_large_per_seq,
+                                              int32_t pages_per_large, int32_t num_blocks,
+                                              int32_t max_query_len, float scale, pa_dtype dtype,
+                                              void* stream) {
+  if (!dtype_ok(dtype) || dtype == PA_F32) return PA_ERR_DTYPE;
+  if (!block_size_ok(block_size)) return PA_ERR_BLOCK_SIZE;
+  if (max_small_per_seq < 1) return PA_ERR_SHAPE;
+  HierTables h{large_tables, num_large, max_large_per_seq, 0};
+  if (num_seqs > 0 && num_tokens > 0 && max_query_len > 0) {
+    const pa_status st = check_hier(h, pages_per_large, max_small_per_seq, block_size);
+    if (st != PA_OK) return st;
+  }
+  return prefill_impl(out, query, k_pool, v_pool, small_tables, context_lens, query_start, num_seqs,
+                      num_tokens, num_q_heads, num_kv_heads, head_dim, block_size, max_small_per_seq,
+                      num_blocks, max_query_len, scale, dtype, stream, h);
 }
 
 PA_EXPORT size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
@@ -246,15 +306,13 @@ PA_EXPORT int32_t pa_decode_choose_partition(int32_t num_seqs, int32_t num_kv_he
   return PA_PARTITION_BALANCED;
 }
 
-PA_EXPORT pa_status pa_decode_attention(void* out, const void* query, const void* k_pool,
-                                        const void* v_pool, const int32_t* block_tables,
-                                        const int32_t* context_lens, int32_t num_seqs,
-                                        int32_t num_q_heads, int32_t num_kv_heads,
-                                        int32_t head_dim, int32_t block_size,
-                                        int32_t max_blocks_per_seq, int32_t num_blocks,
-                                        int32_t max_context_len, float scale,
-                                        int32_t partition_size, pa_dtype dtype, void* workspace,
-                                        size_t workspace_bytes, void* stream) {
+static pa_status decode_impl(void* out, const void* query, const void* k_pool, const void* v_pool,
+                             const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+                             int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                             int32_t block_size, int32_t max_blocks_per_seq, int32_t num_blocks,
+                             int32_t max_context_len, float scale, int32_t partition_size, pa_dtype dtype,
+                             void* workspace, size_t workspace_bytes, void* stream,
+                             const HierTables& hier) {
   if (!dtype_ok(dtype)) return PA_ERR_DTYPE;
   if (!block_size_ok(block_size)) return PA_ERR_BLOCK_SIZE;
   if (num_seqs < 0 || num_q_heads < 1 || num_kv_heads < 1 || !head_dim_ok(head_dim) ||
@@ -318,6 +376,47 @@ PA_EXPORT pa_status pa_decode_attention(void* out, const void* query, const void
     a.ws_l = a.ws_m + rows;
     a.ws_o = a.ws_l + rows;
   }
+  a.large_tables = hier.large_tables;
+  a.num_large = hier.num_large;
+  a.max_large_per_seq = hier.max_large_per_seq;
+  a.large_shift = hier.shift;
   return hip_status(pa::launch_decode(a, elem_of(dtype), head_dim, block_size, group,
                                       reinterpret_cast<hipStream_t>(stream)));
+}
+
+PA_EXPORT pa_status pa_decode_attention(void* out, const void* query, const void* k_pool,
+                                        const void* v_pool, const int32_t* block_tables,
+                                        const int32_t* context_lens, int32_t num_seqs,
+                                        int32_t num_q_heads, int32_t num_kv_heads,
+                                        int32_t head_dim, int32_t block_size,
+                                        int32_t max_blocks_per_seq, int32_t num_blocks,
+                                        int32_t max_context_len, float scale,
+                                        int32_t partition_size, pa_dtype dtype, void* workspace,
+                                        size_t workspace_bytes, void* stream) {
+  return decode_impl(out, query, k_pool, v_pool, block_tables, context_lens, num_seqs, num_q_heads,
+                     num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks, max_context_len,
+                     scale, partition_size, dtype, workspace, workspace_bytes, stream, HierTables{});
+}
+
+PA_EXPORT pa_status pa_decode_attention_hier(void* out, const void* query, const void* k_pool,
+                                             const void* v_pool, const int32_t* small_tables,
+                                             const int32_t* large_tables, const int32_t* num_large,
+                                             const int32_t* context_lens, int32_t num_seqs,
+                                             int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                             int32_t block_size, int32_t max_small_per_seq,
+                                             int32_t max_large_per_seq, int32_t pages_per_large,
+                                             int32_t num_blocks, int32_t max_context_len, float scale,
+                                             int32_t partition_size, pa_dtype dtype, void* workspace,
+                                             size_t workspace_bytes, void* stream) {
+  if (!dtype_ok(dtype)) return PA_ERR_DTYPE;
+  if (!block_size_ok(block_size)) return PA_ERR_BLOCK_SIZE;
+  if (max_small_per_seq < 1) return PA_ERR_SHAPE;
+  HierTables h{large_tables, num_large, max_large_per_seq, 0};
+  if (num_seqs > 0) {
+    const pa_status st = check_hier(h, pages_per_large, max_small_per_seq, block_size);
+    if (st != PA_OK) return st;
+  }
+  return decode_impl(out, query, k_pool, v_pool, small_tables, context_lens, num_seqs, num_q_heads,
+                     num_kv_heads, head_dim, block_size, max_small_per_seq, num_blocks, max_context_len,
+                     scale, partition_size, dtype, workspace, workspace_bytes, stream, h);
 }

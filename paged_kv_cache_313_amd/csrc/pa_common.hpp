@@ -248,6 +248,11 @@ struct DecodeArgs {
   int32_t head_chunks;        // head groups per sequence (Hkv on the MFMA path)
   int32_t mode;               // kModeUnit or kModeBalanced
   float scale_log2;           // scale * log2(e)
+  // two-level tables (nullptr: block_tables is the whole table)
+  const int32_t* large_tables;  // [S, max_large_per_seq] large-page ids
+  const int32_t* num_large;     // [S] large pages in use
+  int32_t max_large_per_seq;
+  int32_t large_shift;          // log2(blocks per large page)
 };
 
 // Arguments of the prefill kernel.
@@ -265,11 +270,49 @@ struct PrefillArgs {
   int32_t max_query_len;        // host bound of query_start[s+1] - query_start[s]
   int32_t qblocks;              // query blocks per (sequence, KV head) in the grid
   float scale_log2;             // scale * log2(e)
+  const int32_t* large_tables;  // two-level tables, as in DecodeArgs (nullptr: flat)
+  const int32_t* num_large;
+  int32_t max_large_per_seq;
+  int32_t large_shift;
 };
+
+// One sequence's block table, flat or two-level.  In the two-level form a
+// large page P is the aligned run of blocks [P << shift, (P + 1) << shift);
+// logical blocks [0, nl_blocks) sit in the sequence's large pages, the rest in
+// its small-block row.  entry() is unchecked: callers clamp ids into the pool.
+struct TableView {
+  const int32_t* small;
+  const int32_t* large;
+  int32_t nl_blocks;
+  int32_t shift;
+  int32_t capacity;    // logical blocks the tables can describe
+  __device__ __forceinline__ int entry(int j) const {
+    if (j < nl_blocks) return (large[j >> shift] << shift) + (j & ((1 << shift) - 1));
+    return small[j - nl_blocks];
+  }
+};
+
+template <class Args>
+__device__ __forceinline__ TableView table_view(const Args& a, int s) {
+  TableView v;
+  v.small = a.block_tables + (size_t)s * a.max_blocks_per_seq;
+  v.large = nullptr;
+  v.nl_blocks = 0;
+  v.shift = 0;
+  if (a.large_tables) {
+    int nl = a.num_large[s];
+    nl = nl < 0 ? 0 : (nl > a.max_large_per_seq ? a.max_large_per_seq : nl);
+    v.large = a.large_tables + (size_t)s * a.max_large_per_seq;
+    v.shift = a.large_shift;
+    v.nl_blocks = nl << a.large_shift;
+  }
+  v.capacity = v.nl_blocks + a.max_blocks_per_seq;
+  return v;
+}
 
 __device__ __forceinline__ int clamp_len(const DecodeArgs& a, int s, int block_size) {
   int L = a.context_lens[s];
-  const int cap_tbl = a.max_blocks_per_seq * block_size;
+  const int cap_tbl = table_view(a, s).capacity * block_size;
   L = L < 0 ? 0 : L;
   L = L > cap_tbl ? cap_tbl : L;
   L = L > a.max_context_len ? a.max_context_len : L;

@@ -47,10 +47,10 @@ constexpr int kRing = 2;
 // LDS window (ids clamped into the pool: memory-safe on bad tables).  LDS
 // operations of one wave complete in order; the wait makes the entries
 // visible to every lane before the wave reads them.
-__device__ __forceinline__ void stage_table_wave(int32_t* tbl, const int32_t* row, int first, int count,
+__device__ __forceinline__ void stage_table_wave(int32_t* tbl, const TableView& row, int first, int count,
                                                  int num_blocks, int lane) {
   for (int i = lane; i < count; i += kWave) {
-    const int e = row[first + i];
+    const int e = row.entry(first + i);
     tbl[i] = ((unsigned)e < (unsigned)num_blocks) ? e : 0;
   }
   __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
@@ -203,7 +203,7 @@ struct ValuCore {
     const char* kbase = reinterpret_cast<const char*>(a.k_pool) + (size_t)g * BS * ROWB;
     const char* vbase = reinterpret_cast<const char*>(a.v_pool) + (size_t)g * BS * ROWB;
     const size_t blk_stride = (size_t)a.num_kv_heads * BS * ROWB;
-    const int32_t* trow = a.block_tables + (size_t)s * a.max_blocks_per_seq;
+    const TableView trow = table_view(a, s);
     // lane's row within the tile's block region, and which block (block_size 8)
     const uint32_t lane_off = (uint32_t)((BS >= 16 ? tt : (tt & 7)) * ROWB + qp * 16);
     const bool hi_blk = BS < 16 && tt >= 8;
@@ -382,7 +382,7 @@ struct MfmaCore {
     const char* kbase = reinterpret_cast<const char*>(a.k_pool) + (size_t)g * BS * ROWB;
     const char* vbase = reinterpret_cast<const char*>(a.v_pool) + (size_t)g * BS * ROWB;
     const size_t blk_stride = (size_t)a.num_kv_heads * BS * ROWB;
-    const int32_t* trow = a.block_tables + (size_t)s * a.max_blocks_per_seq;
+    const TableView trow = table_view(a, s);
     // K: token w of the tile, chunk 4 i + gr (i = instruction);
     // V: token 4 gr + w / CPR + 16 j / CPR, chunk w % CPR (j = instruction)
     const int tv0 = 4 * gr + w / CPR;

@@ -97,7 +97,8 @@ __global__ __launch_bounds__(kPfThreads) void prefill_kernel(PrefillArgs a, int 
   // new tokens leave the unit idle (and those rows unwritten)
   const int q0 = a.query_start[s];
   const int n = a.query_start[s + 1] - q0;
-  const int L = min(a.context_lens[s], a.max_blocks_per_seq * block_size);
+  const TableView trow = table_view(a, s);
+  const int L = min(a.context_lens[s], trow.capacity * block_size);
   if (q0 < 0 || n <= 0 || n > a.num_tokens - q0 || qb * QB >= n || n > L) return;
 
   const int tid = threadIdx.x;
@@ -125,7 +126,6 @@ __global__ __launch_bounds__(kPfThreads) void prefill_kernel(PrefillArgs a, int 
   const int wave_last = L - n + min(qb * QB + (wave + 1) * TPW, n) - 1;   // wave's largest position
   const int kend = L - n + min(qb * QB + QB, n);                          // keys the unit needs
 
-  const int32_t* trow = a.block_tables + (size_t)s * a.max_blocks_per_seq;
   const char* kpool = reinterpret_cast<const char*>(a.k_pool);
   const char* vpool = reinterpret_cast<const char*>(a.v_pool);
   const int bmask = block_size - 1;
@@ -144,7 +144,7 @@ __global__ __launch_bounds__(kPfThreads) void prefill_kernel(PrefillArgs a, int 
   auto load_ids = [&](int t0) {
     if (!loader) return;
 #pragma unroll
-    for (int j = 0; j < Lay::NCH; ++j) ids[j] = trow[min(t0 + chunk_key(j), L - 1) >> bs_shift];
+    for (int j = 0; j < Lay::NCH; ++j) ids[j] = trow.entry(min(t0 + chunk_key(j), L - 1) >> bs_shift);
   };
   auto load_tile = [&](int t0) {
     if (!loader) return;

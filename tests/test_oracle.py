@@ -576,3 +576,31 @@ def test_hier_decode_reads_tokens_where_the_pages_put_them():
         sc = keys[s] @ q[s, 0].astype(np.float64) * float(np.float32(0.3))
         w = np.exp(sc - sc.max())
         assert np.allclose(out[s, 0], (w @ vals[s]) / w.sum(), atol=1e-12, rtol=0)
+
+
+def test_hierarchical_layout_keeps_logical_content():
+    """The two-level layout generator moves blocks, not tokens: gathering each
+    sequence through the expanded two-level tables returns the same K/V rows as
+    the flat batch, and unused blocks stay poisoned."""
+    b = W.make_decode_batch(4, num_seqs=5, num_q_heads=4, num_kv_heads=2, head_dim=16, dtype="bf16", block_size=8,
+                            context_lens=[1, 64, 65, 200, 513], append=True)
+    hb, large, nl = W.to_hierarchical(b, 4, prompt_tokens=[1, 64, 40, 199, 512], seed=2)
+    assert nl.tolist() == [0, 2, 1, 6, 16]
+    flat = O.expand_hier_tables(large, nl, hb.block_tables, 4)
+    for s in range(b.num_seqs):
+        L = int(b.context_lens[s])
+        for g in range(2):
+            old_k = O.gather_tokens(b.k_pool, b.block_tables[s], L, 8, g)
+            new_k = O.gather_tokens(hb.k_pool, flat[s], L, 8, g)
+            assert old_k.tobytes() == new_k.tobytes()
+    used = set(int(x) for x in flat[flat >= 0])
+    spare = [i for i in range(hb.num_blocks) if i not in used]
+    assert np.isnan(O.upcast(hb.k_pool[spare], "bf16")).all()
+    # append slots follow their blocks
+    ko, vo = b.k_pool.copy(), b.v_pool.copy()
+    O.kv_append(ko, vo, b.new_key, b.new_value, b.slot_mapping, 8)
+    kn, vn = hb.k_pool.copy(), hb.v_pool.copy()
+    O.kv_append(kn, vn, hb.new_key, hb.new_value, hb.slot_mapping, 8)
+    for s in range(b.num_seqs):
+        L = int(b.context_lens[s])
+        assert O.gather_tokens(ko, b.block_tables[s], L, 8, 1).tobytes() == O.gather_tokens(kn, flat[s], L, 8, 1).tobytes()

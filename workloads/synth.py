@@ -404,3 +404,63 @@ def config5(block_size=16, num_seqs=16, lo=32768, hi=131072, **kw) -> Batch:
 
 
 CONFIGS = {1: config1, 2: config2, 3: config3, 4: config4, 5: config5}
+
+
+S_HIER = 5   # stream id of the two-level layout's placement draws
+
+
+def to_hierarchical(b: Batch, pages_per_large: int, prompt_tokens, seed: int = 0):
+    """The same logical content as ``b`` laid out with two-level tables.
+
+    Sequence s keeps its first ``prompt_tokens[s] // (H * bs)`` full large
+    pages' worth of tokens in large pages -- aligned runs of H = pages_per_large
+    blocks placed at random aligned positions of the pool -- and the rest of
+    its blocks as small blocks at random free positions.  Block contents are
+    copied over, unused blocks stay poisoned and any append slots are moved
+    with their blocks.  Returns (batch, large_tables, num_large): the batch's
+    block_tables are the small tables."""
+    H, bs, S = int(pages_per_large), b.block_size, b.num_seqs
+    lens = b.context_lens.astype(np.int64)
+    nblk = -(-lens // bs)
+    nl = np.array([min(int(prompt_tokens[s]), int(lens[s])) // (H * bs) for s in range(S)], dtype=np.int64)
+    n_small = nblk - nl * H
+    nlp_total = int(nl.sum())
+    need = nlp_total * H + int(n_small.sum())
+    nb = max(b.num_blocks, -(-need // H) * H + H)
+    rng = child_rng(seed, S_HIER)
+    slots_lp = rng.permutation(nb // H)[:nlp_total]              # aligned large-page positions
+    used = np.zeros(nb, dtype=bool)
+    for P in slots_lp:
+        used[P * H:(P + 1) * H] = True
+    free_small = rng.permutation(np.flatnonzero(~used))[:int(n_small.sum())]
+    large = np.full((S, max(1, int(nl.max()) if S else 1)), -1, dtype=np.int32)
+    small = np.full((S, max(1, int(n_small.max()) if S else 1)), -1, dtype=np.int32)
+    newphys = {}
+    kl = ks = 0
+    for s in range(S):
+        large[s, :nl[s]] = slots_lp[kl:kl + nl[s]]
+        kl += int(nl[s])
+        small[s, :n_small[s]] = free_small[ks:ks + n_small[s]]
+        ks += int(n_small[s])
+        for j in range(int(nblk[s])):
+            new = int(large[s, j // H]) * H + j % H if j < nl[s] * H else int(small[s, j - nl[s] * H])
+            newphys[int(b.block_tables[s, j])] = new
+    old_ids = np.fromiter(newphys.keys(), dtype=np.int64)
+    new_ids = np.fromiter(newphys.values(), dtype=np.int64)
+    k_pool = poison_array((nb,) + b.k_pool.shape[1:], b.dtype)
+    v_pool = poison_array((nb,) + b.v_pool.shape[1:], b.dtype)
+    k_pool[new_ids] = b.k_pool[old_ids]
+    v_pool[new_ids] = b.v_pool[old_ids]
+    slot_mapping = None
+    if b.slot_mapping is not None:
+        sm = b.slot_mapping.astype(np.int64)
+        blk, off = sm // bs, sm % bs
+        remap = np.array([newphys.get(int(x), -1) for x in blk], dtype=np.int64)
+        slot_mapping = np.where((sm >= 0) & (remap >= 0), remap * bs + off, -1).astype(np.int64)
+    hb = Batch(name=b.name + f"_hier{H}", dtype=b.dtype, num_seqs=S, num_q_heads=b.num_q_heads,
+               num_kv_heads=b.num_kv_heads, head_dim=b.head_dim, block_size=bs, num_blocks=nb, scale=b.scale,
+               query=b.query, k_pool=k_pool, v_pool=v_pool, block_tables=small, context_lens=b.context_lens,
+               partition_size=b.partition_size, new_key=b.new_key, new_value=b.new_value,
+               slot_mapping=slot_mapping, block_mapping=None,
+               meta={**b.meta, "pages_per_large": H, "num_large_pages": nlp_total})
+    return hb, large, nl.astype(np.int32)
