@@ -375,6 +375,29 @@ def swap_leg(d, b, reps: int = 5, target_bytes: int = 1 << 30) -> dict:
                     "plain = one contiguous torch copy of the same bytes"}
 
 
+def cold_decode_leg(decode_call, stream, reps: int = 10, evict_bytes: int = 1 << 30) -> dict:
+    """Decode time with nothing of the batch left in the caches: before each
+    timed call a 1 GiB scratch buffer is overwritten (it evicts the 256 MB
+    MALL and every L2), then the call alone is timed with HIP events."""
+    import numpy as np
+    import torch
+
+    scratch = torch.empty(evict_bytes, dtype=torch.uint8, device="cuda")
+    ms = []
+    for i in range(reps + 1):
+        scratch.fill_(i & 0xFF)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        decode_call()
+        e1.record(stream)
+        e1.synchronize()
+        ms.append(e0.elapsed_time(e1))
+    del scratch
+    return {"decode_ms_median": float(np.median(ms[1:])), "reps": reps,
+            "what": "median of per-call HIP-event times, each call after a 1 GiB scratch write"}
+
+
 def main():
     args = parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -479,6 +502,18 @@ def main():
     alg_bytes, kv_bytes = algorithmic_bytes(b)
     achieved = alg_bytes / (dec_ms * 1e-3) / 1e9
 
+    def decode_only():
+        if hier:
+            P.decode_attention_hier(d.query, d.k_pool, d.v_pool, d.block_tables, hier[0], hier[1], hier[2],
+                                    d.context_lens, b.scale, b.max_context_len, part, out=out, workspace=ws,
+                                    stream=stream)
+        else:
+            P.decode_attention(d.query, d.k_pool, d.v_pool, d.block_tables, d.context_lens, b.scale,
+                               b.max_context_len, part, out=out, workspace=ws, stream=stream)
+
+    cold = cold_decode_leg(decode_only, stream)
+    cold["kv_read_gbps"] = kv_bytes / (cold["decode_ms_median"] * 1e-3) / 1e9
+    cold["pct_of_hbm_peak"] = 100.0 * alg_bytes / (cold["decode_ms_median"] * 1e-3) / 1e9 / HBM_PEAK_GBPS
     bm_leg = block_manager_leg(b, max(args.steps, 10))
     swap = None if args.no_swap else swap_leg(d, b)
     prefill = None if args.no_prefill else prefill_leg(parity_seqs=() if args.no_cpu_baseline else (0, 9))
@@ -525,6 +560,7 @@ def main():
                      "algorithmic_bytes_per_launch": alg_bytes},
         "cpu_baseline": cpu,
         "parity": parity,
+        "decode_cold_cache": cold,
         "block_manager": bm_leg,
         "swap": swap,
         "prefill": prefill,

@@ -54,6 +54,15 @@ Readings where the pages are silent:
   blocks as it held (lowest first, all-or-nothing) and returns them in table
   order; the caller copies the host data into them.  Blocks it shared before
   come back as private copies.  Utilisation counts resident sequences only.
+* Large pages (Cross-Paper Synthesis page, section 5, the adaptive block size
+  item): append_prompt_large(seq, n, H) writes an empty sequence's prompt of n
+  tokens with its first n // (H * block_size) full large pages' worth of
+  tokens in large pages -- for each, the lowest aligned run of H free blocks
+  [P H, P H + H) -- and the rest as append_slots would place them.  The
+  sequence's table still lists every block; its first num_large * H entries
+  are the large pages' blocks, which block_tables_hier reports as large-page
+  ids.  Large pages are always full, so no later write copies one; a swap-in
+  brings the sequence back with small blocks only.
 """
 
 from __future__ import annotations
@@ -102,7 +111,7 @@ class BlockManager:
         p = self._seq(parent)
         sid = self.next_id
         self.next_id += 1
-        self.seqs[sid] = {"table": list(p["table"]), "len": p["len"]}
+        self.seqs[sid] = {"table": list(p["table"]), "len": p["len"], "nl": p.get("nl", 0), "H": p.get("H")}
         for b in p["table"]:
             self.ref[b] += 1
         return sid
@@ -153,6 +162,61 @@ class BlockManager:
         b = heapq.heappop(self.free)
         self.ref[b] = 1
         return b
+
+    def _take_run(self, H: int) -> int:
+        """Lowest aligned run of H free blocks; returns its large-page id."""
+        free = set(self.free)
+        for P in range(self.num_blocks // H):
+            if all(b in free for b in range(P * H, P * H + H)):
+                for b in range(P * H, P * H + H):
+                    self.ref[b] = 1
+                self.free = [b for b in self.free if not (P * H <= b < P * H + H)]
+                heapq.heapify(self.free)
+                return P
+        raise OutOfBlocks()
+
+    def append_prompt_large(self, sid: int, n: int, H: int):
+        """Slots of an empty sequence's n prompt tokens, full large pages first."""
+        s = self._seq(sid)
+        if s["len"] != 0 or n < 0 or H < 1:
+            raise ValueError("prompt into an empty sequence only")
+        nl = n // (H * self.block_size)
+        saved = (copy.deepcopy(self.seqs), list(self.ref), list(self.free))
+        try:
+            pages = [self._take_run(H) for _ in range(nl)]
+        except OutOfBlocks:
+            self.seqs, self.ref, self.free = saved
+            raise
+        s["table"] = [P * H + i for P in pages for i in range(H)]
+        s["len"] = nl * H * self.block_size
+        s["nl"], s["H"] = nl, H
+        slots = []
+        for P in pages:
+            slots += list(range(P * H * self.block_size, (P + 1) * H * self.block_size))
+        try:
+            rest, pairs = self.append_slots([sid], [n - s["len"]])
+        except OutOfBlocks:
+            self.seqs, self.ref, self.free = saved
+            raise
+        assert pairs == []
+        return slots + rest
+
+    def block_tables_hier(self, seqs, H: int, max_large: int, max_small: int):
+        """(large ids, num_large, small tables, lengths); sequences written
+        without large pages (or with another H) report num_large = 0."""
+        large, nls, small, lens = [], [], [], []
+        for sid in seqs:
+            s = self._seq(sid)
+            nl = s.get("nl", 0) if s.get("H") == H else 0
+            lp = [s["table"][k * H] // H for k in range(nl)]
+            sm = s["table"][nl * H:]
+            if nl > max_large or len(sm) > max_small:
+                raise ValueError("table widths too small")
+            large.append(lp + [-1] * (max_large - nl))
+            nls.append(nl)
+            small.append(sm + [-1] * (max_small - len(sm)))
+            lens.append(s["len"])
+        return large, nls, small, lens
 
     def append_slots(self, seqs, counts):
         """Returns (slots, cow_pairs): one slot per new token in batch order,

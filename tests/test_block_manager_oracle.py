@@ -46,6 +46,17 @@ class World:
         del self.hist[sid]
         self.host.pop(sid, None)
 
+    def prompt_large(self, sid, n, H):
+        slots = self.bm.append_prompt_large(sid, n, H)
+        assert len(slots) == n and len(set(slots)) == n
+        for sl in slots:
+            tok = self.next_token
+            self.next_token += 1
+            b, o = divmod(sl, self.bm.block_size)
+            self.pool[b, o] = tok
+            self.hist[sid].append(tok)
+        return slots
+
     def swap_out(self, sid):
         ids = self.bm.swap_out(sid)
         self.host[sid] = self.pool[ids].copy()       # before anything reuses the blocks
@@ -95,19 +106,29 @@ class World:
                 count[b] += 1
             got = [int(self.pool[s["table"][t // bm.block_size], t % bm.block_size]) for t in range(len(h))]
             assert got == h, f"sequence {sid} reads back other tokens"
+            nl, H = s.get("nl", 0), s.get("H")
+            for k in range(nl):                    # large pages: aligned runs, always full
+                run = s["table"][k * H:(k + 1) * H]
+                assert run[0] % H == 0 and run == list(range(run[0], run[0] + H))
+            assert s["len"] >= nl * (H or 0) * bm.block_size
         assert count == bm.ref, "reference counts differ from table membership"
         assert sorted(bm.free) == [b for b in range(bm.num_blocks) if count[b] == 0]
         assert set(bm.seqs) | set(bm.swapped) == set(self.hist)
         assert not set(bm.seqs) & set(bm.swapped)
 
 
-def random_ops(world, rng, steps, max_batch=6, max_tokens=40, swaps=True):
+def random_ops(world, rng, steps, max_batch=6, max_tokens=40, swaps=True, large_pages=0):
     for _ in range(steps):
         live = sorted(s for s in world.hist if s not in world.host)
         out = sorted(world.host)
         r = rng.random()
         if not live or r < 0.15:
-            world.add()
+            sid = world.add()
+            if large_pages and rng.random() < 0.5:
+                try:
+                    world.prompt_large(sid, rng.randint(0, 3 * large_pages * world.bm.block_size), large_pages)
+                except OutOfBlocks:
+                    pass
         elif r < 0.30:
             world.fork(rng.choice(live))
         elif r < 0.40 and len(live) > 1:
@@ -309,3 +330,49 @@ def test_swap_round_trip_and_errors():
     world.check()
     world.free(a)                                 # a swapped sequence can be dropped
     world.check()
+
+
+@pytest.mark.parametrize("seed", range(8))
+@pytest.mark.parametrize("bs,H", [(1, 4), (4, 2), (2, 8)])
+def test_random_histories_with_large_pages(seed, bs, H):
+    world = World(BlockManager(num_blocks=96, block_size=bs))
+    random_ops(world, random.Random(100 + seed), 150, large_pages=H)
+
+
+def test_large_pages_expand_to_the_flat_table():
+    """block_tables_hier, expanded by the pool oracle's two-level rule, is the
+    flat table; an aligned run is skipped while any of its blocks is taken."""
+    import oracle.pa_oracle as O
+    bm = BlockManager(64, 4)
+    a = bm.add_sequence()
+    bm.append_slots([a], [5])                       # blocks 0, 1: runs of 8 start at 8
+    b = bm.add_sequence()
+    slots = bm.append_prompt_large(b, 2 * 8 * 4 + 6, 8)
+    assert slots[0] == 8 * 4 and bm.seqs[b]["table"][:16] == list(range(8, 24))
+    assert bm.seqs[b]["table"][16:] == [2, 3]       # the rest: lowest free small blocks
+    large, nl, small, lens = bm.block_tables_hier([a, b], 8, 2, 3)
+    assert nl == [0, 2] and large[1] == [1, 2] and lens == [5, 70]
+    flat = O.expand_hier_tables(np.array(large), nl, np.array(small), 8)
+    for i, sid in enumerate([a, b]):
+        t = bm.seqs[sid]["table"]
+        assert flat[i, :len(t)].tolist() == t
+    with pytest.raises(ValueError):
+        bm.append_prompt_large(a, 40, 8)             # only into an empty sequence
+
+
+class UnalignedLargeBM(BlockManager):
+    def _take_run(self, H):
+        got = [self._take() for _ in range(H)]        # lowest free blocks, not an aligned run
+        return got[0] // H
+
+
+def test_unaligned_large_pages_are_caught():
+    caught = False
+    for seed in range(10):
+        world = World(UnalignedLargeBM(num_blocks=96, block_size=2))
+        try:
+            random_ops(world, random.Random(seed), 200, large_pages=4)
+        except AssertionError:
+            caught = True
+            break
+    assert caught
