@@ -99,6 +99,34 @@ pa_status pa_bm_block_tables(const pa_block_manager* bm, const int64_t* seq_ids,
                              int32_t max_blocks_per_seq, int32_t* block_tables,
                              int32_t* context_lens);
 
+/* Prompt in large pages (Cross-Paper Synthesis page, section 5, the adaptive
+ * block size item: huge pages where a prompt is written in one go).  Sequence
+ * seq_id must be resident and empty (else PA_ERR_SHAPE).  Its first
+ * floor(num_tokens / (pages_per_large * block_size)) large pages' worth of
+ * tokens go to large pages -- each the lowest aligned run of pages_per_large
+ * free blocks [P H, P H + H) -- and the remaining tokens to small blocks as
+ * pa_bm_append_slots would place them.  slot_mapping (HOST int64
+ * [slot_capacity]) receives num_tokens slots in token order.  pages_per_large
+ * is a power of two in [1, 1024].  All-or-nothing: PA_ERR_NO_BLOCKS (no free
+ * aligned run, or too few blocks) or PA_ERR_CAPACITY leave it empty.  Large
+ * pages are always full, so no later append copies one; they are shared by
+ * forks and returned block by block on free; a swap-in brings the sequence
+ * back in small blocks. */
+pa_status pa_bm_append_prompt_large(pa_block_manager* bm, int64_t seq_id, int32_t num_tokens,
+                                    int32_t pages_per_large, int64_t* slot_mapping, int64_t slot_capacity);
+
+/* Two-level tables of a batch, in the layout pa_decode_attention_hier reads:
+ * large_tables HOST int32 [num_seqs][max_large_per_seq] (large-page ids,
+ * -1 past the last), num_large HOST int32 [num_seqs], small_tables HOST int32
+ * [num_seqs][max_small_per_seq] (-1 past the last), context_lens HOST int32
+ * [num_seqs].  A sequence without large pages of this pages_per_large reports
+ * num_large = 0 and all its blocks as small ones.  PA_ERR_SEQUENCE for an id
+ * not resident, PA_ERR_CAPACITY if a row does not fit. */
+pa_status pa_bm_block_tables_hier(const pa_block_manager* bm, const int64_t* seq_ids, int32_t num_seqs,
+                                  int32_t pages_per_large, int32_t max_large_per_seq, int32_t max_small_per_seq,
+                                  int32_t* large_tables, int32_t* num_large, int32_t* small_tables,
+                                  int32_t* context_lens);
+
 /* Preemption, out: the blocks of resident sequence seq_id in table order go
  * to block_ids (HOST int32 [capacity]; *num_ids receives the count), each
  * loses the sequence's reference (blocks left with none become free), and

@@ -50,6 +50,8 @@ SIGNATURES = {
     "pa_bm_append_slots": (_c_i32, [_vp, _vp, _vp, _c_i32, _vp, _c_i64, _vp, _c_i32,
                                     ctypes.POINTER(_c_i32)]),
     "pa_bm_block_tables": (_c_i32, [_vp, _vp, _c_i32, _c_i32, _vp, _vp]),
+    "pa_bm_append_prompt_large": (_c_i32, [_vp, _c_i64, _c_i32, _c_i32, _vp, _c_i64]),
+    "pa_bm_block_tables_hier": (_c_i32, [_vp, _vp, _c_i32, _c_i32, _c_i32, _c_i32, _vp, _vp, _vp, _vp]),
     "pa_bm_swap_out": (_c_i32, [_vp, _c_i64, _vp, _c_i32, ctypes.POINTER(_c_i32)]),
     "pa_bm_swap_in": (_c_i32, [_vp, _c_i64, _vp, _c_i32, ctypes.POINTER(_c_i32)]),
     "pa_bm_num_free_blocks": (_c_i32, [_vp]),

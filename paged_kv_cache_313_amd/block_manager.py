@@ -83,6 +83,14 @@ class BlockManager:
                                                 slots.size, _ptr(pairs), ids.size, ctypes.byref(n)))
         return slots, pairs[: n.value].copy()
 
+    def append_prompt_large(self, seq_id: int, num_tokens: int, pages_per_large: int) -> np.ndarray:
+        """Slots of an empty sequence's prompt, full large pages first."""
+        slots = np.empty(max(int(num_tokens), 0), dtype=np.int64)
+        _lib.check("pa_bm_append_prompt_large",
+                   self._lib.pa_bm_append_prompt_large(self._h, int(seq_id), int(num_tokens), int(pages_per_large),
+                                                       _ptr(slots), slots.size))
+        return slots
+
     # -- preemption ------------------------------------------------------------
     def _ids_call(self, fn: str, seq_id: int) -> np.ndarray:
         cap = max(1, -(-self.length(seq_id) // self.block_size))
@@ -109,6 +117,20 @@ class BlockManager:
                    self._lib.pa_bm_block_tables(self._h, _ptr(ids), ids.size, max_blocks_per_seq,
                                                 _ptr(tables), _ptr(lens)))
         return tables, lens
+
+    def block_tables_hier(self, seq_ids, pages_per_large: int, max_large_per_seq: int, max_small_per_seq: int):
+        """(large_tables, num_large, small_tables, context_lens) for the
+        two-level decode and prefill calls."""
+        ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
+        large = np.empty((ids.size, max_large_per_seq), dtype=np.int32)
+        nl = np.empty(ids.size, dtype=np.int32)
+        small = np.empty((ids.size, max_small_per_seq), dtype=np.int32)
+        lens = np.empty(ids.size, dtype=np.int32)
+        _lib.check("pa_bm_block_tables_hier",
+                   self._lib.pa_bm_block_tables_hier(self._h, _ptr(ids), ids.size, int(pages_per_large),
+                                                     max_large_per_seq, max_small_per_seq, _ptr(large), _ptr(nl),
+                                                     _ptr(small), _ptr(lens)))
+        return large, nl, small, lens
 
     def num_free_blocks(self) -> int:
         return int(self._lib.pa_bm_num_free_blocks(self._h))

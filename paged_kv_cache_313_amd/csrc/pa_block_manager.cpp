@@ -62,6 +62,28 @@ class FreeBitmap {
     }
     --count_;
   }
+  // Lowest aligned run of h free blocks (h a power of two); returns its
+  // first block or -1.  A linear scan of the block bitmap: large pages are
+  // taken once per prompt.
+  int32_t find_run(int32_t h) const {
+    if (h <= 64) {
+      const uint64_t m = h == 64 ? ~0ull : ((1ull << h) - 1);
+      for (size_t i = 0; i < l0_.size(); ++i) {
+        const uint64_t w = l0_[i];
+        if (!w) continue;
+        for (int off = 0; off < 64; off += h)
+          if (((w >> off) & m) == m && (int64_t)i * 64 + off + h <= n_) return (int32_t)(i * 64 + off);
+      }
+      return -1;
+    }
+    const size_t words = (size_t)h / 64;
+    for (size_t i = 0; i + words <= l0_.size(); i += words) {
+      size_t k = 0;
+      while (k < words && l0_[i + k] == ~0ull) ++k;
+      if (k == words && (int64_t)(i + words) * 64 <= n_) return (int32_t)(i * 64);
+    }
+    return -1;
+  }
   void put(int32_t b) {
     const size_t i0 = (size_t)b >> 6, i1 = i0 >> 6;
     l0_[i0] |= 1ull << (b & 63);
@@ -76,8 +98,10 @@ class FreeBitmap {
 };
 
 struct Sequence {
-  std::vector<int32_t> table;
+  std::vector<int32_t> table;   // every block, large pages' blocks first
   int64_t len = 0;
+  int32_t num_large = 0;        // large pages at the start of the table
+  int32_t large_h = 0;          // their size in blocks
 };
 
 struct SwappedOut {
@@ -267,6 +291,101 @@ PA_EXPORT pa_status pa_bm_append_slots(pa_block_manager* bm, const int64_t* seq_
   }
   bm->log.clear();
   *num_pairs = pairs;
+  return PA_OK;
+}
+
+PA_EXPORT pa_status pa_bm_append_prompt_large(pa_block_manager* bm, int64_t seq_id, int32_t num_tokens,
+                                              int32_t pages_per_large, int64_t* slot_mapping,
+                                              int64_t slot_capacity) {
+  if (!bm) return PA_ERR_NULL;
+  if (num_tokens < 0 || pages_per_large < 1 || pages_per_large > 1024 ||
+      (pages_per_large & (pages_per_large - 1)) != 0)
+    return PA_ERR_SHAPE;
+  auto it = bm->seqs.find(seq_id);
+  if (it == bm->seqs.end()) return PA_ERR_SEQUENCE;
+  Sequence& s = it->second;
+  if (s.len != 0 || !s.table.empty()) return PA_ERR_SHAPE;
+  if (slot_capacity < num_tokens) return PA_ERR_CAPACITY;
+  if (num_tokens > 0 && !slot_mapping) return PA_ERR_NULL;
+  const int32_t H = pages_per_large, bs = bm->block_size;
+  const int64_t page_tokens = (int64_t)H * bs;
+  const int32_t nl = (int32_t)(num_tokens / page_tokens);
+  try {
+    bm->log.clear();
+    bm->log.reserve(1 + (size_t)nl * H * 2);
+    s.table.reserve((size_t)nl * H + (size_t)((num_tokens - nl * page_tokens + bs - 1) / bs));
+  } catch (...) {
+    return PA_ERR_CAPACITY;
+  }
+  bm->log.push_back({Undo::kLen, 0, 0, &s, s.len});
+  for (int32_t k = 0; k < nl; ++k) {
+    const int32_t first = bm->free.find_run(H);
+    if (first < 0) {
+      bm->rollback();
+      return PA_ERR_NO_BLOCKS;
+    }
+    for (int32_t i = 0; i < H; ++i) {
+      bm->free.clear(first + i);
+      bm->ref[first + i] = 1;
+      ++bm->blocks_in_use;
+      bm->log.push_back({Undo::kTake, first + i, 0, nullptr, 0});
+      s.table.push_back(first + i);
+      bm->log.push_back({Undo::kTablePush, 0, 0, &s, 0});
+    }
+  }
+  for (int64_t t = 0; t < (int64_t)nl * page_tokens; ++t)
+    slot_mapping[t] = (int64_t)s.table[t / bs] * bs + t % bs;
+  s.len = (int64_t)nl * page_tokens;
+  // the rest goes where an append puts it; that call rolls back its own part
+  const int64_t sid = seq_id;
+  const int32_t rest = (int32_t)(num_tokens - s.len);
+  int32_t pairs = 0;
+  std::vector<Undo> mine;
+  mine.swap(bm->log);
+  const pa_status st = pa_bm_append_slots(bm, &sid, &rest, 1, slot_mapping + s.len, slot_capacity - s.len,
+                                          nullptr, 0, &pairs);
+  mine.swap(bm->log);
+  if (st != PA_OK) {
+    bm->rollback();
+    return st;
+  }
+  bm->log.clear();
+  s.num_large = nl;
+  s.large_h = nl > 0 ? H : 0;
+  return PA_OK;
+}
+
+PA_EXPORT pa_status pa_bm_block_tables_hier(const pa_block_manager* bm, const int64_t* seq_ids,
+                                            int32_t num_seqs, int32_t pages_per_large,
+                                            int32_t max_large_per_seq, int32_t max_small_per_seq,
+                                            int32_t* large_tables, int32_t* num_large, int32_t* small_tables,
+                                            int32_t* context_lens) {
+  if (!bm) return PA_ERR_NULL;
+  if (num_seqs < 0 || max_large_per_seq < 0 || max_small_per_seq < 0 || pages_per_large < 1) return PA_ERR_SHAPE;
+  if (num_seqs == 0) return PA_OK;
+  if (!seq_ids || !num_large || !small_tables || !context_lens || (max_large_per_seq > 0 && !large_tables))
+    return PA_ERR_NULL;
+  for (int32_t i = 0; i < num_seqs; ++i) {
+    auto it = bm->seqs.find(seq_ids[i]);
+    if (it == bm->seqs.end()) return PA_ERR_SEQUENCE;
+    const Sequence& s = it->second;
+    const int32_t nl = s.large_h == pages_per_large ? s.num_large : 0;
+    if (nl > max_large_per_seq || (int64_t)s.table.size() - (int64_t)nl * pages_per_large > max_small_per_seq ||
+        s.len > INT32_MAX)
+      return PA_ERR_CAPACITY;
+  }
+  for (int32_t i = 0; i < num_seqs; ++i) {
+    const Sequence& s = bm->seqs.find(seq_ids[i])->second;
+    const int32_t nl = s.large_h == pages_per_large ? s.num_large : 0;
+    int32_t* lrow = large_tables + (size_t)i * max_large_per_seq;
+    for (int32_t k = 0; k < max_large_per_seq; ++k)
+      lrow[k] = k < nl ? s.table[(size_t)k * pages_per_large] / pages_per_large : -1;
+    int32_t* srow = small_tables + (size_t)i * max_small_per_seq;
+    const size_t off = (size_t)nl * pages_per_large, n = s.table.size() - off;
+    for (size_t j = 0; j < (size_t)max_small_per_seq; ++j) srow[j] = j < n ? s.table[off + j] : -1;
+    num_large[i] = nl;
+    context_lens[i] = (int32_t)s.len;
+  }
   return PA_OK;
 }
 

@@ -85,9 +85,10 @@ __global__ __launch_bounds__(kPfThreads) void prefill_kernel(PrefillArgs a, int 
   __shared__ __align__(16) char lds[2 * Lay::kBufBytes];
 
   // unit: (sequence, KV head, query block), query block fastest, dealt to
-  // XCDs in runs so that one sequence's blocks share an L2
+  // XCDs in runs so that one sequence's blocks share an L2; the last query
+  // block of a sequence (the most keys under the causal mask) goes first
   const uint32_t u = xcd_unit(blockIdx.x, gridDim.x);
-  const int qb = (int)(u % (uint32_t)a.qblocks);
+  const int qb = a.qblocks - 1 - (int)(u % (uint32_t)a.qblocks);
   const int sg = (int)(u / (uint32_t)a.qblocks);
   const int g = sg % a.num_kv_heads;
   const int s = sg / a.num_kv_heads;

@@ -24,10 +24,16 @@ def built():
     P.load()
 
 
-def same_state(nat, ref):
+def same_state(nat, ref, large_pages=0):
     for sid in ref.swapped:
         assert nat.length(sid) == ref.length(sid)
     live = sorted(ref.seqs)
+    if live and large_pages:
+        ml = max(1, max(ref.seqs[s].get("nl", 0) for s in live))
+        ms = max(1, max(len(ref.seqs[s]["table"]) for s in live))
+        got = nat.block_tables_hier(live, large_pages, ml, ms)
+        want = ref.block_tables_hier(live, large_pages, ml, ms)
+        assert [g.tolist() for g in got] == [list(w) for w in want]
     if live:
         mb = max(1, max(len(ref.seqs[s]["table"]) for s in live))
         t_ref, l_ref = ref.block_tables(live, mb)
@@ -38,7 +44,7 @@ def same_state(nat, ref):
     assert nat.utilisation() == ref.utilisation()
 
 
-def run_history(seed, num_blocks, bs, steps, max_batch=8, max_tokens=50):
+def run_history(seed, num_blocks, bs, steps, max_batch=8, max_tokens=50, large_pages=0):
     rng = random.Random(seed)
     nat, ref = P.BlockManager(num_blocks, bs), RefBM(num_blocks, bs)
     n_fail = 0
@@ -47,7 +53,20 @@ def run_history(seed, num_blocks, bs, steps, max_batch=8, max_tokens=50):
         out = sorted(ref.swapped)
         r = rng.random()
         if not live or r < 0.15:
-            assert nat.add_sequence() == ref.add_sequence()
+            sid = nat.add_sequence()
+            assert ref.add_sequence() == sid
+            if large_pages and rng.random() < 0.5:
+                n = rng.randint(0, 3 * large_pages * bs)
+                try:
+                    want = ref.append_prompt_large(sid, n, large_pages)
+                except OutOfBlocks:
+                    want = None
+                if want is None:
+                    with pytest.raises(P.PagedKVError) as e:
+                        nat.append_prompt_large(sid, n, large_pages)
+                    assert e.value.status == NO_BLOCKS
+                else:
+                    assert nat.append_prompt_large(sid, n, large_pages).tolist() == want
         elif r < 0.30:
             p = rng.choice(live)
             assert nat.fork(p) == ref.fork(p)
@@ -88,7 +107,7 @@ def run_history(seed, num_blocks, bs, steps, max_batch=8, max_tokens=50):
                 slots, pairs = nat.append_slots(seqs, counts)
                 assert slots.tolist() == want[0]
                 assert [tuple(p) for p in pairs.tolist()] == want[1]
-        same_state(nat, ref)
+        same_state(nat, ref, large_pages)
     return n_fail
 
 
@@ -214,3 +233,26 @@ def test_swapped_sequence_errors_and_round_trip():
     with pytest.raises(P.PagedKVError) as e:
         bm.length(b)
     assert e.value.status == BAD_SEQ
+
+
+@pytest.mark.parametrize("seed", range(6))
+@pytest.mark.parametrize("num_blocks,bs,H", [(96, 2, 4), (130, 4, 8), (300, 1, 64)])
+def test_large_pages_match_reference(seed, num_blocks, bs, H):
+    run_history(seed, num_blocks, bs, 160, large_pages=H)
+
+
+def test_large_page_runs_span_words():
+    """Runs longer than one 64-block bitmap word, and the lowest aligned run
+    after scattered small allocations."""
+    bm = P.BlockManager(1024, 16)
+    a = bm.add_sequence()
+    bm.append_slots([a], [16 * 3])                    # blocks 0..2
+    b = bm.add_sequence()
+    slots = bm.append_prompt_large(b, 128 * 16 + 5, 128)
+    assert slots[0] == 128 * 16                       # run [128, 256): [0, 128) is broken by a's blocks
+    large, nl, small, lens = bm.block_tables_hier([a, b], 128, 1, 3)
+    assert nl.tolist() == [0, 1] and large[1].tolist() == [1] and small[1].tolist() == [3, -1, -1]
+    c = bm.add_sequence()
+    with pytest.raises(P.PagedKVError) as e:
+        bm.append_prompt_large(c, 8 * 128 * 16, 128)   # 8 more runs do not exist
+    assert e.value.status == NO_BLOCKS and bm.length(c) == 0

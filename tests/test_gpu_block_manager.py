@@ -94,3 +94,82 @@ def test_manager_driven_decode_steps(bs, partition):
     torch.cuda.synchronize()
     assert torch_io.torch_to_storage(k_dev, DT).tobytes() == k_host.tobytes()
     assert torch_io.torch_to_storage(v_dev, DT).tobytes() == v_host.tobytes()
+
+
+def test_manager_large_pages_drive_hier_calls():
+    """Prompts written in large pages by the native manager (aligned runs of
+    8 blocks), then a prefill of their last tokens and decode steps with forks
+    and copy-on-write in the small-block tail, through the two-level calls;
+    pools bit for bit and attention against the oracle."""
+    rng = np.random.default_rng(99)
+    NB, Hkv, G, D, bs, H = 256, 2, 4, 128, 16, 8
+    Hq = Hkv * G
+    scale = W.default_scale(D)
+    nat, ref = P.BlockManager(NB, bs), RefBM(NB, bs)
+    k_host = W.poison_array((NB, Hkv, bs, D), DT)
+    v_host = W.poison_array((NB, Hkv, bs, D), DT)
+    k_dev = torch_io.storage_to_torch(k_host, DT, "cuda")
+    v_dev = torch_io.storage_to_torch(v_host, DT, "cuda")
+
+    def write(slots):
+        n = len(slots)
+        key, val = draw(rng, (n, Hkv, D)), draw(rng, (n, Hkv, D))
+        P.kv_append(torch_io.storage_to_torch(key, DT, "cuda"), torch_io.storage_to_torch(val, DT, "cuda"),
+                    k_dev, v_dev, torch.from_numpy(np.asarray(slots, dtype=np.int64)).cuda())
+        O.kv_append(k_host, v_host, key, val, np.asarray(slots, dtype=np.int64), bs)
+
+    def tables(seqs):
+        ml = max(1, max(ref.seqs[s].get("nl", 0) for s in seqs))
+        ms = max(1, max(len(ref.seqs[s]["table"]) for s in seqs))
+        got = nat.block_tables_hier(seqs, H, ml, ms)
+        want = ref.block_tables_hier(seqs, H, ml, ms)
+        assert [g.tolist() for g in got] == [list(w) for w in want]
+        return got
+
+    prompts = [300, 129, 40]                        # 2, 1 and 0 large pages of 128 tokens
+    seqs = []
+    for n in prompts:
+        s = nat.add_sequence()
+        assert ref.add_sequence() == s
+        slots = nat.append_prompt_large(s, n, H)
+        assert slots.tolist() == ref.append_prompt_large(s, n, H)
+        write(slots)
+        seqs.append(s)
+    # prefill of each prompt's last 20 tokens (already written)
+    large, nl, small, lens = tables(seqs)
+    news = [20, 20, 20]
+    starts = np.concatenate([[0], np.cumsum(news)]).astype(np.int32)
+    q = draw(rng, (int(starts[-1]), Hq, D))
+    note("manager large pages: prefill")
+    out = P.prefill_attention_hier(torch_io.storage_to_torch(q, DT, "cuda"), k_dev, v_dev, torch.from_numpy(small).cuda(),
+                                   torch.from_numpy(large).cuda(), torch.from_numpy(nl).cuda(), H,
+                                   torch.from_numpy(lens).cuda(), torch.from_numpy(starts).cuda(), scale, 20)
+    torch.cuda.synchronize()
+    want = O.prefill_attention_hier(q, k_host, v_host, large, nl, small, H, lens, starts, scale, bs, DT)
+    check_close(gpu_out_f64(out, DT), want, DT, "prefill through manager large pages", ulps=2,
+                extra=2.0 ** -7 * np.abs(want).max())
+    # forks and decode steps: copy-on-write in the small tail
+    live = list(seqs)
+    for s in seqs:
+        c = nat.fork(s)
+        assert ref.fork(s) == c
+        live.append(c)
+    for t in range(6):
+        slots, pairs = nat.append_slots(live, [1] * len(live))
+        want_s, want_p = ref.append_slots(live, [1] * len(live))
+        assert slots.tolist() == want_s and [tuple(p) for p in pairs.tolist()] == want_p
+        if len(pairs):
+            P.block_copy(k_dev, v_dev, torch.from_numpy(pairs).cuda())
+            O.block_copy(k_host, v_host, pairs)
+        write(slots)
+        large, nl, small, lens = tables(live)
+        q = draw(rng, (len(live), Hq, D))
+        note(f"manager large pages: decode step {t}")
+        out = P.decode_attention_hier(torch_io.storage_to_torch(q, DT, "cuda"), k_dev, v_dev,
+                                      torch.from_numpy(small).cuda(), torch.from_numpy(large).cuda(),
+                                      torch.from_numpy(nl).cuda(), H, torch.from_numpy(lens).cuda(), scale,
+                                      int(lens.max()), -1)
+        torch.cuda.synchronize()
+        want = O.decode_attention_hier(q, k_host, v_host, large, nl, small, H, lens, scale, bs, DT)
+        check_close(gpu_out_f64(out, DT), want, DT, f"decode step {t}")
+    assert torch_io.torch_to_storage(k_dev, DT).tobytes() == k_host.tobytes()
