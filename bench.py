@@ -55,6 +55,7 @@ def parse_args():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-swap", action="store_true", help="skip the swap (preemption traffic) leg")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill leg")
+    ap.add_argument("--eager", action="store_true", help="time eager launches instead of HIP-graph replays")
     ap.add_argument("--prefill-only", action="store_true",
                     help="only time pa_prefill_attention on the chunked-prefill workload and print its line")
     ap.add_argument("--cpu-seconds", type=float, default=8.0, help="minimum wall time of the oracle timing")
@@ -377,15 +378,17 @@ def swap_leg(d, b, reps: int = 5, target_bytes: int = 1 << 30) -> dict:
 
 def cold_decode_leg(decode_call, stream, reps: int = 10, evict_bytes: int = 1 << 30) -> dict:
     """Decode time with nothing of the batch left in the caches: before each
-    timed call a 1 GiB scratch buffer is overwritten (it evicts the 256 MB
-    MALL and every L2), then the call alone is timed with HIP events."""
+    timed call a 1 GiB scratch buffer is read through (it evicts the 256 MB
+    MALL and every L2 with clean lines, so no write-back competes with the
+    call), then the call alone is timed with HIP events."""
     import numpy as np
     import torch
 
-    scratch = torch.empty(evict_bytes, dtype=torch.uint8, device="cuda")
+    scratch = torch.ones(evict_bytes // 4, dtype=torch.int32, device="cuda")
+    sink = torch.empty((), dtype=torch.int64, device="cuda")
     ms = []
     for i in range(reps + 1):
-        scratch.fill_(i & 0xFF)
+        torch.sum(scratch, dim=0, dtype=torch.int64, out=sink)
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record(stream)
@@ -393,9 +396,9 @@ def cold_decode_leg(decode_call, stream, reps: int = 10, evict_bytes: int = 1 <<
         e1.record(stream)
         e1.synchronize()
         ms.append(e0.elapsed_time(e1))
-    del scratch
+    del scratch, sink
     return {"decode_ms_median": float(np.median(ms[1:])), "reps": reps,
-            "what": "median of per-call HIP-event times, each call after a 1 GiB scratch write"}
+            "what": "median of per-call HIP-event times, each call after reading a 1 GiB scratch buffer"}
 
 
 def main():
@@ -455,61 +458,92 @@ def main():
         hier = (torch.from_numpy(large).to(dev), torch.from_numpy(nl).to(dev), H)
     has_append = b.new_key is not None
 
-    ev = {"dec0": [], "dec1": [], "app0": [], "app1": [], "cp0": [], "cp1": []}
+    def copy_only(st):
+        P.block_copy(d.k_pool, d.v_pool, d.block_mapping, stream=st)
 
-    def step(record):
-        if has_copy:
-            if record:
-                e = torch.cuda.Event(enable_timing=True); e.record(stream); ev["cp0"].append(e)
-            P.block_copy(d.k_pool, d.v_pool, d.block_mapping, stream=stream)
-            if record:
-                e = torch.cuda.Event(enable_timing=True); e.record(stream); ev["cp1"].append(e)
-        if has_append:
-            if record:
-                e = torch.cuda.Event(enable_timing=True); e.record(stream); ev["app0"].append(e)
-            P.kv_append(d.new_key, d.new_value, d.k_pool, d.v_pool, d.slot_mapping, stream=stream)
-            if record:
-                e = torch.cuda.Event(enable_timing=True); e.record(stream); ev["app1"].append(e)
-        if record:
-            e = torch.cuda.Event(enable_timing=True); e.record(stream); ev["dec0"].append(e)
+    def append_only(st):
+        P.kv_append(d.new_key, d.new_value, d.k_pool, d.v_pool, d.slot_mapping, stream=st)
+
+    def decode_only(st=None):
+        st = stream if st is None else st
         if hier:
             P.decode_attention_hier(d.query, d.k_pool, d.v_pool, d.block_tables, hier[0], hier[1], hier[2],
                                     d.context_lens, b.scale, b.max_context_len, part, out=out, workspace=ws,
-                                    stream=stream)
+                                    stream=st)
         else:
             P.decode_attention(d.query, d.k_pool, d.v_pool, d.block_tables, d.context_lens, b.scale,
-                               b.max_context_len, part, out=out, workspace=ws, stream=stream)
-        if record:
-            e = torch.cuda.Event(enable_timing=True); e.record(stream); ev["dec1"].append(e)
+                               b.max_context_len, part, out=out, workspace=ws, stream=st)
 
+    parts = ([copy_only] if has_copy else []) + ([append_only] if has_append else []) + [decode_only]
+
+    def step_fn(st):
+        for f in parts:
+            f(st)
+
+    def events_ms(run, n):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(n):
+            run()
+        e1.record(stream)
+        e1.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    # The timed region is one HIP graph holding the K steps back to back (and
+    # one per call kind, K calls each, for the per-call times): a single
+    # launch, so host stalls cannot starve the GPU and no per-launch cost is
+    # counted K times.  The library allocates, synchronises and clears
+    # nothing, so its calls capture as they are.  Eager launches are the
+    # fallback (--eager forces them).
     for _ in range(args.warmup):
-        step(False)
+        step_fn(stream)
     torch.cuda.synchronize()
-    print(f"[bench] warmup done ({args.warmup} steps), timing {args.steps} steps", file=sys.stderr, flush=True)
+    K = args.steps
+    graphs = None
+    if not args.eager:
+        try:
+            def capture(fn):
+                g = torch.cuda.CUDAGraph()
+                cs = torch.cuda.Stream()
+                cs.wait_stream(stream)
+                with torch.cuda.graph(g, stream=cs):
+                    for _ in range(K):
+                        fn(cs)
+                stream.wait_stream(cs)
+                return g
+            graphs = {"step": capture(step_fn), "decode": capture(decode_only)}
+            if has_append:
+                graphs["append"] = capture(append_only)
+            if has_copy:
+                graphs["copy"] = capture(copy_only)
+            graphs["step"].replay()   # warm the graph itself
+            torch.cuda.synchronize()
+        except Exception as exc:   # fall back to eager launches
+            print(f"[bench] graph capture failed ({exc}); timing eager launches", file=sys.stderr, flush=True)
+            graphs = None
+            torch.cuda.synchronize()
+    timing = f"one HIP graph of {K} steps" if graphs else "eager launches"
+    print(f"[bench] warmup done ({args.warmup} steps), timing {K} steps ({timing})", file=sys.stderr, flush=True)
+
+    def k_calls(kind, fn):
+        if graphs:
+            return graphs[kind].replay
+        return lambda: [fn(stream) for _ in range(K)]
+
+    run_steps = k_calls("step", step_fn)
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step(True)
+    run_steps()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) / args.steps * 1e3
-
-    def mean_ms(a, z):
-        return float(np.mean([x.elapsed_time(y) for x, y in zip(ev[a], ev[z])])) if ev[a] else None
-
-    dec_ms = mean_ms("dec0", "dec1")
-    app_ms = mean_ms("app0", "app1")
-    cp_ms = mean_ms("cp0", "cp1")
+    ms_per_step = (t1 - t0) / K * 1e3
+    # per-call times: K back-to-back calls of one kind, HIP events on the stream
+    dec_ms = events_ms(k_calls("decode", decode_only), 1) / K
+    app_ms = events_ms(k_calls("append", append_only), 1) / K if has_append else None
+    cp_ms = events_ms(k_calls("copy", copy_only), 1) / K if has_copy else None
     alg_bytes, kv_bytes = algorithmic_bytes(b)
     achieved = alg_bytes / (dec_ms * 1e-3) / 1e9
-
-    def decode_only():
-        if hier:
-            P.decode_attention_hier(d.query, d.k_pool, d.v_pool, d.block_tables, hier[0], hier[1], hier[2],
-                                    d.context_lens, b.scale, b.max_context_len, part, out=out, workspace=ws,
-                                    stream=stream)
-        else:
-            P.decode_attention(d.query, d.k_pool, d.v_pool, d.block_tables, d.context_lens, b.scale,
-                               b.max_context_len, part, out=out, workspace=ws, stream=stream)
 
     cold = cold_decode_leg(decode_only, stream)
     cold["kv_read_gbps"] = kv_bytes / (cold["decode_ms_median"] * 1e-3) / 1e9
@@ -550,6 +584,7 @@ def main():
         "config": cfg,
         "kv_read_gbps": kv_bytes / (dec_ms * 1e-3) / 1e9,
         "pct_of_hbm_peak": 100.0 * achieved / HBM_PEAK_GBPS,
+        "timing": timing,
         "decode_ms": dec_ms,
         "append_ms": app_ms,
         "block_copy_ms": cp_ms,
