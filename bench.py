@@ -538,10 +538,13 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) / K * 1e3
-    # per-call times: K back-to-back calls of one kind, HIP events on the stream
-    dec_ms = events_ms(k_calls("decode", decode_only), 1) / K
-    app_ms = events_ms(k_calls("append", append_only), 1) / K if has_append else None
+    # per-call times: K back-to-back calls of one kind, HIP events on the
+    # stream, in step order (copies, appends, decode) so that the pools end in
+    # the state a step leaves: a copy's source may be a block that an append
+    # of the same step writes in place
     cp_ms = events_ms(k_calls("copy", copy_only), 1) / K if has_copy else None
+    app_ms = events_ms(k_calls("append", append_only), 1) / K if has_append else None
+    dec_ms = events_ms(k_calls("decode", decode_only), 1) / K
     alg_bytes, kv_bytes = algorithmic_bytes(b)
     achieved = alg_bytes / (dec_ms * 1e-3) / 1e9
 
@@ -551,6 +554,9 @@ def main():
     bm_leg = block_manager_leg(b, max(args.steps, 10))
     swap = None if args.no_swap else swap_leg(d, b)
     prefill = None if args.no_prefill else prefill_leg(parity_seqs=() if args.no_cpu_baseline else (0, 9))
+
+    step_fn(stream)          # one whole step last: the output the parity check reads
+    torch.cuda.synchronize()
 
     # parity of this run's output against the oracle run above (all sequences)
     parity = None
