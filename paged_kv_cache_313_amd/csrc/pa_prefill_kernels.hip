@@ -34,7 +34,10 @@
 
 namespace pa {
 
-constexpr int kPfWaves = 4;
+#ifndef PA_PREFILL_WAVES
+#define PA_PREFILL_WAVES 4
+#endif
+constexpr int kPfWaves = PA_PREFILL_WAVES;
 constexpr int kPfThreads = kPfWaves * kWave;
 #ifndef PA_PREFILL_KEYS
 #define PA_PREFILL_KEYS 64
@@ -57,9 +60,14 @@ constexpr float kPfLazy = 8.f;
 constexpr int kPfGroups = PA_PREFILL_GROUPS;
 constexpr int kPfRows = kPfWaves * 16 * kPfGroups;   // query rows (token, head) per workgroup
 
-// K is staged row-major.  V is staged transposed (row d holds the tile's keys
-// in order); a thread owns two consecutive keys of one 16-byte d-chunk, so it
-// writes a (key, key + 1) pair of each of its 8 d rows as one dword.
+// K is staged row-major.  V is staged transposed (row d holds the tile's
+// keys); a thread owns two consecutive keys of one 16-byte d-chunk, so it
+// writes a (key, key + 1) pair of each of its 8 d rows as one dword.  The 16
+// lanes that write one key pair hit rows 8 apart, which the row pitch alone
+// maps onto 4 of the 64 banks; so row r keeps key pair p at dword
+// p ^ vt_swizzle(r), spreading those lanes over every bank.  The swizzle is a
+// multiple of 4, so the two pairs a reader takes together stay adjacent.
+__device__ __forceinline__ int vt_swizzle(int row) { return 4 * ((row >> 5) & 3); }
 template <int D>
 struct PfLayout {
   static constexpr int kRowB = D * 2 + 16;           // K row pitch in LDS (bytes), padded
@@ -179,7 +187,8 @@ __global__ __launch_bounds__(kPfThreads) void prefill_kernel(PrefillArgs a, int 
         // element e of both keys: low halves (even e) or high halves (odd e)
         const uint32_t w = (e & 1) ? __builtin_amdgcn_perm(v1[e >> 1], v0[e >> 1], 0x07060302u)
                                    : __builtin_amdgcn_perm(v1[e >> 1], v0[e >> 1], 0x05040100u);
-        *reinterpret_cast<uint32_t*>(vb + (dch * 8 + e) * Lay::kVtB + key * 2) = w;
+        const int row = dch * 8 + e;
+        *reinterpret_cast<uint32_t*>(vb + row * Lay::kVtB + (((key >> 1) ^ vt_swizzle(row)) << 2)) = w;
       }
     }
   };
@@ -275,18 +284,23 @@ __global__ __launch_bounds__(kPfThreads) void prefill_kernel(PrefillArgs a, int 
       // V^T operands one step ahead of their products, so LDS latency
       // overlaps the matrix cores instead of preceding each product
       constexpr int NVS = NDT * (kPfSub / 2);
+      // step = h NDT + dt: consecutive products accumulate into different d
+      // tiles, so a product's dependence on the same tile's previous one is
+      // NDT products back (the matrix-core latency stays covered)
       auto read_v = [&](int step) {
-        const int dt = step / (kPfSub / 2), h = step % (kPfSub / 2);
-        const char* vrow = vb + (16 * dt + c) * Lay::kVtB;
-        const uint2 lo = *reinterpret_cast<const uint2*>(vrow + (32 * h + 4 * gq) * 2);
-        const uint2 hi = *reinterpret_cast<const uint2*>(vrow + (32 * h + 16 + 4 * gq) * 2);
+        const int h = step / NDT, dt = step % NDT;
+        const int row = 16 * dt + c;
+        const char* vrow = vb + row * Lay::kVtB;
+        const int sw = vt_swizzle(row);
+        const uint2 lo = *reinterpret_cast<const uint2*>(vrow + (((16 * h + 2 * gq) ^ sw) << 2));
+        const uint2 hi = *reinterpret_cast<const uint2*>(vrow + (((16 * h + 8 + 2 * gq) ^ sw) << 2));
         return u32x4{lo.x, lo.y, hi.x, hi.y};
       };
       u32x4 av = read_v(0);
 #pragma unroll
       for (int step = 0; step < NVS; ++step) {
         const u32x4 nxt = read_v(step + 1 < NVS ? step + 1 : step);
-        const int dt = step / (kPfSub / 2), h = step % (kPfSub / 2);
+        const int h = step / NDT, dt = step % NDT;
 #pragma unroll
         for (int grp = 0; grp < NG; ++grp) oacc[grp][dt] = mfma_16x16x32<T>(av, pb[grp][h], oacc[grp][dt]);
         av = nxt;
