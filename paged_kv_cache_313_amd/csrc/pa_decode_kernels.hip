@@ -57,6 +57,27 @@ __device__ __forceinline__ void stage_table_wave(int32_t* tbl, const TableView& 
   __builtin_amdgcn_wave_barrier();
 }
 
+// The table window a wave last staged: consecutive segments of a wave are
+// mostly the same sequence under another KV head and need the same entries,
+// so a window that still covers the next one is reused (one dependent global
+// round trip less per segment start).
+struct TblCache {
+  int s = -1, first = 0, count = 0;
+};
+
+// Entries [fblk, fblk + nent) of sequence s, staged unless the cached window
+// holds them; returns the LDS address of entry fblk.
+__device__ __forceinline__ int32_t* staged_window(int32_t* tbl, TblCache& tc, const TableView& row, int s,
+                                                  int fblk, int nent, int num_blocks, int lane) {
+  if (!(tc.s == s && tc.first <= fblk && fblk + nent <= tc.first + tc.count)) {
+    stage_table_wave(tbl, row, fblk, nent, num_blocks, lane);
+    tc.s = s;
+    tc.first = fblk;
+    tc.count = nent;
+  }
+  return tbl + (fblk - tc.first);
+}
+
 // Walk tiles 0 .. ntiles-1 keeping the next NB-1 tiles' K/V loads in flight
 // while the current one is computed.  The loop runs over NB tiles at a time
 // with a ring of NB buffers and has a single exit, so that no path (not even
@@ -176,8 +197,8 @@ struct ValuCore {
 
   // q heads h0 .. h0+H-1 of sequence s over tokens [tok0, tok1), run by one
   // wave; tbl is the wave's LDS window.
-  __device__ static void run(const DecodeArgs& a, int32_t* tbl, int s, int h0, int tok0, int tok1,
-                             const Dest& dst) {
+  __device__ static void run(const DecodeArgs& a, int32_t* tbl_lds, TblCache& tc, int s, int h0, int tok0,
+                             int tok1, const Dest& dst) {
     const int lane = threadIdx.x & (kWave - 1);
     const int G = a.num_q_heads / a.num_kv_heads;
     const int g = h0 / G;
@@ -215,7 +236,7 @@ struct ValuCore {
       const int off0 = wb - fblk * BS;
       const int we = min((fblk + kTblWin) * BS, tok1);
       const int nent = (we - 1) / BS - fblk + 1;
-      stage_table_wave(tbl, trow, fblk, nent, a.num_blocks, lane);
+      const int32_t* tbl = staged_window(tbl_lds, tc, trow, s, fblk, nent, a.num_blocks, lane);
 
       auto load = [&](int ti, ValuBuf<NL>& buf) {
         size_t lo, hi;
@@ -359,8 +380,8 @@ struct MfmaCore {
 
   // the G q heads h0 .. h0+G-1 (KV head h0 / G) of sequence s over tokens
   // [tok0, tok1), run by one wave; tbl is the wave's LDS window.
-  __device__ static void run(const DecodeArgs& a, int32_t* tbl, int s, int h0, int tok0, int tok1,
-                             const Dest& dst) {
+  __device__ static void run(const DecodeArgs& a, int32_t* tbl_lds, TblCache& tc, int s, int h0, int tok0,
+                             int tok1, const Dest& dst) {
     const int lane = threadIdx.x & (kWave - 1);
     const int gr = lane >> 4, w = lane & 15;
     const int g = h0 / G;
@@ -396,7 +417,7 @@ struct MfmaCore {
       const int off0 = wb - fblk * BS;
       const int we = min((fblk + kTblWin) * BS, tok1);
       const int nent = (we - 1) / BS - fblk + 1;
-      stage_table_wave(tbl, trow, fblk, nent, a.num_blocks, lane);
+      const int32_t* tbl = staged_window(tbl_lds, tc, trow, s, fblk, nent, a.num_blocks, lane);
 
       auto load = [&](int ti, MfmaBuf<NQK, NVI>& buf) {
         size_t lo, hi;
@@ -537,19 +558,30 @@ __global__ __launch_bounds__(NW * kWave) void decode_unit_kernel(DecodeArgs a, i
   // partial rows: (s, h, p) -> ((s * Hq + h) * NP + p)
   const Dest dst{!a.split || L <= P, ((size_t)s * a.num_q_heads + h0) * a.num_parts + p,
                  (size_t)a.num_parts};
-  Core::run(a, s_tbl[wave], s, h0, t0, t1, dst);
+  TblCache tc;
+  Core::run(a, s_tbl[wave], tc, s, h0, t0, t1, dst);
 }
 
 // ============================================================================
-// Balanced-mode kernel.  Flattened space: sequence s owns tiles
-// [C cum[s], C cum[s+1]) (C head groups of ceil(L_s / 16) tiles each, head
-// group major).  Of ntot tiles, wave w of W takes [w ntot / W, (w+1) ntot / W).
-// A (sequence, head group) wholly inside the range is written directly; the
-// first and the last segment of the range, when they are pieces of a larger
-// one, go to partial slots 2w and 2w+1 (H rows each).  Each XCD gets a
-// contiguous run of waves (so samples sharing a prompt's blocks meet in one
-// L2); workgroup 0 also stores cum for the merge.
+// Balanced-mode kernel.  Flattened space: each (sequence, head group) with
+// nt = ceil(L_s / 16) > 0 tiles costs X + nt units -- X for starting a
+// segment (its query, its first tiles' latency, its epilogue), then its
+// tiles -- so sequence s owns [C cum[s], C cum[s+1]) with cum the prefix of
+// C (X + nt) and head groups major.  Of ntot units, wave w of W takes
+// [w ntot / W, (w+1) ntot / W): waves whose range holds many short segments
+// get fewer tiles, and all finish together.  A (sequence, head group) whose
+// tiles all fall in one range is written directly; the first and the last
+// segment of a range, when they are pieces of a larger one, go to partial
+// slots 2w and 2w+1 (H rows each).  Each XCD gets a contiguous run of waves
+// (so samples sharing a prompt's blocks meet in one L2); workgroup 0 also
+// stores cum for the merge.
 // ============================================================================
+#ifndef PA_SEG_COST
+#define PA_SEG_COST 3
+#endif
+// Segment start cost in tiles: on a Llama-3-8B-shaped batch, equal-byte runs
+// at 1K and 8K tokens per sequence put a segment start at about 3 tiles.
+constexpr int kSegCost = PA_SEG_COST;
 __device__ __forceinline__ int64_t range_start(int64_t w, int64_t ntot, int64_t W) {
   return w * ntot / W;
 }
@@ -565,7 +597,8 @@ __device__ __forceinline__ uint32_t xcd_contiguous(uint32_t b, uint32_t n) {
 template <int NT>
 __device__ __forceinline__ void tile_prefix(const DecodeArgs& a, int block_size, int32_t* s_cum,
                                             int32_t* s_part) {
-  // s_cum[s] = sum_{s' < s} ceil(L_s' / 16), s = 0..S, by a block-wide scan
+  // s_cum[s] = sum_{s' < s} cost(s'), cost = X + ceil(L / 16) (0 for an
+  // empty sequence), s = 0..S, by a block-wide scan
   const int S = a.num_seqs;
   const int per = (S + NT - 1) / NT;
   const int lo = threadIdx.x * per, hi = min(lo + per, S);
@@ -573,7 +606,7 @@ __device__ __forceinline__ void tile_prefix(const DecodeArgs& a, int block_size,
   for (int s = lo; s < hi; ++s) {
     const int nt = (clamp_len(a, s, block_size) + kTile - 1) / kTile;
     s_cum[s] = sum;   // local exclusive prefix, offset below
-    sum += nt;
+    sum += nt > 0 ? nt + kSegCost : 0;
   }
   s_part[threadIdx.x] = sum;
   __syncthreads();
@@ -602,6 +635,11 @@ __global__ __launch_bounds__(NW * kWave) void decode_balanced_kernel(DecodeArgs 
   tile_prefix<NW * kWave>(a, block_size, s_cum, s_part);
   if (blockIdx.x == 0)
     for (int s = threadIdx.x; s <= S; s += NW * kWave) a.ws_cum[s] = s_cum[s];
+  // sequences with no tile own no range: their rows are zeros, written here
+  for (int s = blockIdx.x; s < S; s += gridDim.x)
+    if (s_cum[s + 1] == s_cum[s])
+      for (int idx = threadIdx.x; idx < a.num_q_heads * D; idx += NW * kWave)
+        store_elem<T>(a.out, (size_t)s * a.num_q_heads * D + idx, 0.f);
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int64_t W = (int64_t)gridDim.x * NW;
@@ -618,30 +656,35 @@ __global__ __launch_bounds__(NW * kWave) void decode_balanced_kernel(DecodeArgs 
     if ((int64_t)C * s_cum[mid] <= f) lo = mid; else hi = mid - 1;
   }
   int s = lo;
-  int nt = s_cum[s + 1] - s_cum[s];
+  int ntc = s_cum[s + 1] - s_cum[s];        // cost of one head group of s: X + nt
   const int64_t rel = f - (int64_t)C * s_cum[s];
-  int c = (int)(rel / nt);
-  int t = (int)(rel - (int64_t)c * nt);
+  int c = (int)(rel / ntc);
+  int u = (int)(rel - (int64_t)c * ntc);    // position within that cost
   bool first = true;
+  TblCache tc;
   while (f < fb) {
-    const int n = (int)min((int64_t)(nt - t), fb - f);
-    const int L = clamp_len(a, s, block_size);
-    const int tok0 = t * kTile, tok1 = min((t + n) * kTile, L);
-    const size_t slot = 2 * (size_t)w + (first ? 0 : 1);
-    const Dest dst{t == 0 && t + n == nt, slot * H, 1};
-    Core::run(a, s_tbl[wave], s, c * H, tok0, tok1, dst);
-    first = false;
+    const int n = (int)min((int64_t)(ntc - u), fb - f);
+    const int nt = ntc - kSegCost;
+    const int t0 = max(u - kSegCost, 0), t1 = min(u + n - kSegCost, nt);
+    if (t1 > t0) {   // the range holds real tiles of this head group
+      const int L = clamp_len(a, s, block_size);
+      const int tok0 = t0 * kTile, tok1 = min(t1 * kTile, L);
+      const size_t slot = 2 * (size_t)w + (first ? 0 : 1);
+      const Dest dst{t0 == 0 && t1 == nt, slot * H, 1};
+      Core::run(a, s_tbl[wave], tc, s, c * H, tok0, tok1, dst);
+      first = false;
+    }
     f += n;
-    t += n;
-    if (t == nt && f < fb) {  // next head group, or the next sequence with tiles
-      t = 0;
+    u += n;
+    if (u == ntc && f < fb) {  // next head group, or the next sequence with tiles
+      u = 0;
       if (++c == C) {
         c = 0;
         do {
           ++s;
         } while (s_cum[s + 1] == s_cum[s]);
       }
-      nt = s_cum[s + 1] - s_cum[s];
+      ntc = s_cum[s + 1] - s_cum[s];
     }
   }
 }
@@ -711,17 +754,43 @@ __global__ __launch_bounds__(kWave) void decode_merge_parts_kernel(DecodeArgs a,
   for (int e = 0; e < EPL; ++e) store_elem<T>(a.out, (size_t)row * D + e * kWave + lane, num[e] / den);
 }
 
-// Balanced mode, per (sequence, head group): the waves that shared its tile
-// range [A, B) are w_lo .. w_hi (w_lo: the last wave whose range starts at or
-// before A); wave w left its piece in slot 2w + (its range starts at or after
-// A ? 0 : 1), and waves with an empty range (more waves than tiles) wrote
-// nothing.  One workgroup per (sequence, head group), one wave per head: lane
-// p holds piece p (64 at a time) for the max and the sum, then all lanes walk
-// the pieces with slot and weight read from lane j (loads unrolled by 8),
-// each accumulating D/64 outputs.  Lanes without a piece point at w_lo's
-// piece (always written in this call) with weight 0, so nothing left in the
-// workspace by an earlier call is read.  Empty sequences get zeros.
+// Balanced mode: the head groups whose tiles were split between waves are
+// found from the wave boundaries.  Boundary w (1 <= w < W, at position
+// b = range_start(w) of the flattened space) merges the head group whose
+// tiles [A, B) it is the first to split: A < b < B and wave w - 1 holds A.
+// Head groups written whole need nothing, so the launch is sized by the
+// boundaries, however many sequences there are.  The waves that shared [A, B)
+// are w_lo = w - 1 .. w_hi; wave w left its piece in slot 2w + (its range
+// starts at or after the head group's cost start A0 = A - X ? 0 : 1), and
+// waves with an empty range wrote nothing.  Per head, lane p holds piece p
+// (64 at a time) for the max and the sum, then all lanes walk the pieces with
+// slot and weight read from lane j (loads unrolled by 8), each accumulating
+// D/64 outputs.  Lanes without a piece point at w_lo's piece (always written
+// in this call) with weight 0, so nothing left in the workspace by an earlier
+// call is read.
 constexpr int kMergeWaves = 4;
+// The H heads of a boundary's head group go to min(H, 4) waves of one
+// workgroup (each taking every min(H, 4)-th head), and a workgroup serves
+// 4 / min(H, 4) boundaries.
+template <int H>
+constexpr int kMergeHeadWaves = H < kMergeWaves ? H : kMergeWaves;
+template <int H>
+constexpr int kMergeBoundaries = kMergeWaves / kMergeHeadWaves<H>;
+
+// The last s in [0, S) with C cum[s] <= x (cum non-decreasing, cum[0] = 0 <=
+// x): two rounds of a 64-lane ballot for S <= 4096, from global memory.
+__device__ __forceinline__ int find_seq(const int32_t* cum, int S, int C, int64_t x, int lane) {
+  int base = 0, span = S;
+  while (span > 1) {
+    const int step = (span + kWave - 1) / kWave;
+    const int idx = base + lane * step;
+    const bool le = lane * step < span && (int64_t)C * cum[idx] <= x;
+    const int last = __popcll(__ballot(le)) - 1;   // the true lanes are a prefix
+    base += last * step;
+    span = min(step, span - last * step);
+  }
+  return base;
+}
 
 template <class T, int D, int H>
 __global__ __launch_bounds__(kMergeWaves * kWave) void decode_merge_balanced_kernel(DecodeArgs a,
@@ -729,31 +798,32 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void decode_merge_balanced_ker
                                                                                    int nwaves) {
   constexpr int EPL = D / kWave;
   const int C = a.head_chunks;
-  const int s = blockIdx.x / C, c = blockIdx.x - (blockIdx.x / C) * C;
   const int lane = threadIdx.x & (kWave - 1);
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int L = clamp_len(a, s, block_size);
-  const int nt = (L + kTile - 1) / kTile;
-  const size_t orow = (size_t)s * a.num_q_heads + (size_t)c * H;
-  if (nt == 0) {
-    for (int idx = threadIdx.x; idx < H * D; idx += kMergeWaves * kWave)
-      store_elem<T>(a.out, orow * D + idx, 0.f);
-    return;
-  }
   const int64_t W = nwaves;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  if (wave / kMergeHeadWaves<H> >= kMergeBoundaries<H>) return;
+  const int64_t w = (int64_t)blockIdx.x * kMergeBoundaries<H> + wave / kMergeHeadWaves<H>;
+  if (w < 1 || w >= W) return;
   const int64_t ntot = (int64_t)C * a.ws_cum[a.num_seqs];
-  const int64_t A = (int64_t)C * a.ws_cum[s] + (int64_t)c * nt, B = A + nt;
-  const int64_t w_lo = ((A + 1) * W - 1) / ntot, w_hi = (B * W - 1) / ntot;
-  if (w_lo == w_hi) return;                 // one wave wrote it directly
+  const int64_t b = range_start(w, ntot, W);
+  if (b <= 0 || b >= ntot) return;
+  const int s = __builtin_amdgcn_readfirstlane(find_seq(a.ws_cum, a.num_seqs, C, b - 1, lane));
+  const int ntc = a.ws_cum[s + 1] - a.ws_cum[s];
+  const int c = (int)((b - 1 - (int64_t)C * a.ws_cum[s]) / ntc);
+  const int64_t A0 = (int64_t)C * a.ws_cum[s] + (int64_t)c * ntc;
+  const int64_t A = A0 + kSegCost, B = A0 + ntc;
+  if (!(A < b && b < B && range_start(w - 1, ntot, W) <= A)) return;
+  const size_t orow = (size_t)s * a.num_q_heads + (size_t)c * H;
+  const int64_t w_lo = w - 1, w_hi = (B * W - 1) / ntot;
   const int k = (int)(w_hi - w_lo + 1);
-  const int slot_lo = (int)(2 * w_lo + (range_start(w_lo, ntot, W) >= A ? 0 : 1));
+  const int slot_lo = (int)(2 * w_lo + (range_start(w_lo, ntot, W) >= A0 ? 0 : 1));
   auto piece_slot = [&](int p, bool& ok) {
     const int64_t w = w_lo + p;
     const int64_t ws = range_start(w, ntot, W);
     ok = p < k && ws != range_start(w + 1, ntot, W);
-    return ok ? (int)(2 * w + (ws >= A ? 0 : 1)) : slot_lo;
+    return ok ? (int)(2 * w + (ws >= A0 ? 0 : 1)) : slot_lo;
   };
-  for (int hh = wave; hh < H; hh += kMergeWaves) {
+  for (int hh = wave % kMergeHeadWaves<H>; hh < H; hh += kMergeHeadWaves<H>) {
     float M = kNegInf;
     for (int p0 = 0; p0 < k; p0 += kWave) {
       bool ok;
@@ -826,8 +896,10 @@ static hipError_t run_core(const DecodeArgs& a, int bs, hipStream_t st) {
     hipLaunchKernelGGL(kern, dim3(nwg), dim3(NW * kWave), 0, st, a, bs);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((decode_merge_balanced_kernel<T, D, H>), dim3((uint32_t)a.num_seqs * a.head_chunks),
-                       dim3(kMergeWaves * kWave), 0, st, a, bs, nwg * NW);
+    const uint32_t waves = (uint32_t)nwg * NW;
+    constexpr uint32_t BPW = kMergeBoundaries<H>;
+    hipLaunchKernelGGL((decode_merge_balanced_kernel<T, D, H>), dim3((waves + BPW - 1) / BPW),
+                       dim3(kMergeWaves * kWave), 0, st, a, bs, (int)waves);
     return hipGetLastError();
   }
   const uint64_t units = (uint64_t)a.num_seqs * a.head_chunks * a.num_parts;

@@ -1,12 +1,16 @@
 """The balanced split's bookkeeping, checked on the CPU: every tile of every
-(sequence, head group) is processed by exactly one workgroup, every piece that
-a workgroup writes to a partial slot is read back by the merge exactly once,
-and the merge never reads a slot that no workgroup wrote.
+(sequence, head group) is processed by exactly one wave, every piece that a
+wave writes to a partial slot is read back by the merge exactly once, and the
+merge never reads a slot that no wave wrote.
 
 The walk below mirrors the index arithmetic of decode_balanced_kernel and
-decode_merge_balanced_kernel (tile prefix sums, range w*ntot/W, slot 2w or
-2w+1, the merge's w_lo/w_hi and skip of empty ranges); it is a model of the
-schedule, the kernels themselves are checked against the oracle on the GPU."""
+decode_merge_balanced_kernel: each (sequence, head group) with tiles costs X
+virtual units (a segment start) followed by its nt tiles in the flattened
+space, wave w of W takes [w ntot / W, (w+1) ntot / W), its first real segment
+goes to slot 2w and its last to 2w+1, and the merge finds the waves w_lo..w_hi
+that hold the real tiles and skips those with empty ranges.  It is a model of
+the schedule; the kernels themselves are checked against the oracle on the
+GPU."""
 
 import random
 
@@ -15,12 +19,12 @@ import pytest
 TILE = 16
 
 
-def walk(lens, C, W):
+def walk(lens, C, W, X=0):
     S = len(lens)
     nts = [-(-L // TILE) for L in lens]
     cum = [0]
     for n in nts:
-        cum.append(cum[-1] + n)
+        cum.append(cum[-1] + (n + X if n else 0))
     ntot = C * cum[S]
     written, direct, seen = {}, set(), {}
     for w in range(W):
@@ -35,39 +39,67 @@ def walk(lens, C, W):
             else:
                 hi = mid - 1
         s = lo
-        nt = cum[s + 1] - cum[s]
+        ntc = cum[s + 1] - cum[s]
         rel = f - C * cum[s]
-        c, t = rel // nt, rel % nt
+        c, u = rel // ntc, rel % ntc
         first = True
         while f < fb:
-            n = min(nt - t, fb - f)
-            for tt in range(t, t + n):
-                assert (s, c, tt) not in seen
-                seen[(s, c, tt)] = w
-            if t == 0 and t + n == nt:
-                direct.add((s, c))
-            else:
-                slot = 2 * w + (0 if first else 1)
-                assert slot not in written
-                written[slot] = (s, c, t, t + n)
-            first = False
+            n = min(ntc - u, fb - f)
+            nt = ntc - X
+            t0, t1 = max(u - X, 0), min(u + n - X, nt)
+            if t1 > t0:
+                for tt in range(t0, t1):
+                    assert (s, c, tt) not in seen
+                    seen[(s, c, tt)] = w
+                if t0 == 0 and t1 == nt:
+                    direct.add((s, c))
+                else:
+                    slot = 2 * w + (0 if first else 1)
+                    assert slot not in written
+                    written[slot] = (s, c, t0, t1)
+                first = False
             f += n
-            t += n
-            if t == nt and f < fb:
-                t, c = 0, c + 1
+            u += n
+            if u == ntc and f < fb:
+                u, c = 0, c + 1
                 if c == C:
                     c, s = 0, s + 1
                     while cum[s + 1] == cum[s]:
                         s += 1
-                nt = cum[s + 1] - cum[s]
-    assert len(seen) == ntot
+                ntc = cum[s + 1] - cum[s]
+    assert len(seen) == C * sum(nts)
+    # the merge over wave boundaries: boundary w (1 <= w < W) merges the head
+    # group whose tiles it is the first to split
+    merged = {}
+    for w in range(1, W):
+        b = w * ntot // W
+        if b == 0 or b >= ntot:
+            continue
+        lo, hi = 0, S - 1
+        while lo < hi:
+            mid = (lo + hi + 1) >> 1
+            if C * cum[mid] <= b - 1:
+                lo = mid
+            else:
+                hi = mid - 1
+        s = lo
+        ntc = cum[s + 1] - cum[s]
+        c = (b - 1 - C * cum[s]) // ntc
+        A = C * cum[s] + c * ntc + X
+        B = A + ntc - X
+        if A < b < B and (w - 1) * ntot // W <= A:
+            assert (s, c) not in merged
+            merged[(s, c)] = w
+    split = {(s, c) for s in range(S) for c in range(C) if nts[s] and (s, c) not in direct}
+    assert set(merged) == split
     read = set()
     for s in range(S):
         for c in range(C):
             nt = nts[s]
             if nt == 0:
                 continue
-            A = C * cum[s] + c * nt
+            A0 = C * cum[s] + c * (nt + X)        # the unit's cost start
+            A = A0 + X                             # its first real tile
             B = A + nt
             w_lo, w_hi = ((A + 1) * W - 1) // ntot, (B * W - 1) // ntot
             if w_lo == w_hi:
@@ -79,7 +111,7 @@ def walk(lens, C, W):
                 ws = w * ntot // W
                 if ws == (w + 1) * ntot // W:
                     continue
-                slot = 2 * w + (0 if ws >= A else 1)
+                slot = 2 * w + (0 if ws >= A0 else 1)
                 assert written.get(slot, (None, None))[:2] == (s, c)
                 read.add(slot)
                 covered += written[slot][3] - written[slot][2]
@@ -96,8 +128,9 @@ def cases():
     return [c for c in out if sum(c) > 0]
 
 
+@pytest.mark.parametrize("X", [0, 1, 3, 8])
 @pytest.mark.parametrize("lens", cases())
-def test_balanced_schedule_covers_each_tile_once(lens):
+def test_balanced_schedule_covers_each_tile_once(lens, X):
     for C in (1, 2, 8):
         for W in list(range(1, 70)) + [255, 256, 512, 768, 2048]:
-            walk(lens, C, W)
+            walk(lens, C, W, X)
