@@ -60,18 +60,27 @@ constexpr float kPfLazy = 8.f;
 constexpr int kPfGroups = PA_PREFILL_GROUPS;
 constexpr int kPfRows = kPfWaves * 16 * kPfGroups;   // query rows (token, head) per workgroup
 
-// K is staged row-major.  V is staged transposed (row d holds the tile's
-// keys); a thread owns two consecutive keys of one 16-byte d-chunk, so it
-// writes a (key, key + 1) pair of each of its 8 d rows as one dword.  The 16
-// lanes that write one key pair hit rows 8 apart, which the row pitch alone
-// maps onto 4 of the 64 banks; so row r keeps key pair p at dword
-// p ^ vt_swizzle(r), spreading those lanes over every bank.  The swizzle is a
-// multiple of 4, so the two pairs a reader takes together stay adjacent.
-__device__ __forceinline__ int vt_swizzle(int row) { return 4 * ((row >> 5) & 3); }
+// K is staged row-major.  V is staged transposed: row d of a tile holds its
+// key pairs as dwords (the d-th elements of keys 2p and 2p + 1).  The pairs
+// sit in the order the matrix-core operand takes them: dword 4 (4 h + gq) +
+// slot holds pair 16 h + 2 gq + (slot & 1) + 8 (slot >> 1), i.e. keys
+// 4 gq .. 4 gq + 3 and 16 + 4 gq .. 16 + 4 gq + 3 of half h, so lane (c, gq)
+// reads its 8 keys of a row as one aligned 16-byte load.  A thread owns one
+// such pair position of one 16-byte d-chunk and writes the pair to each of
+// its 8 d rows as one dword.  The 64 lanes of a write instruction cover 16
+// d-chunks (rows 8 apart, which the 144-byte row pitch maps onto 2 bank
+// groups) and 4 consecutive positions, so row r keeps position x at
+// x ^ vt_swizzle(r), which spreads those lanes over all 64 banks.  The swizzle
+// is a multiple of 4, so each lane's 16-byte group stays whole.
+__device__ __forceinline__ int vt_swizzle(int row) { return 4 * ((row >> 4) & (kPfKeys / 8 - 1)); }
+// pair (within the tile) stored at position x
+__device__ __forceinline__ int vt_pair(int x) {
+  return 16 * (x >> 4) + 2 * ((x >> 2) & 3) + (x & 1) + 8 * ((x >> 1) & 1);
+}
 template <int D>
 struct PfLayout {
   static constexpr int kRowB = D * 2 + 16;           // K row pitch in LDS (bytes), padded
-  static constexpr int kVtB = kPfKeys * 2 + 8;       // V^T row pitch in LDS (bytes), padded
+  static constexpr int kVtB = kPfKeys * 2 + 16;      // V^T row pitch in LDS (bytes), padded, 16-byte aligned
   static constexpr int kKBytes = kPfKeys * kRowB;
   static constexpr int kBufBytes = kKBytes + D * kVtB;
   static constexpr int CPR = D / 8;                  // 16-byte chunks per token row
@@ -80,7 +89,19 @@ struct PfLayout {
   static constexpr int NPAIR = kPartial ? 1 : kPairs / kPfThreads;   // key pairs per thread per tile
   static constexpr int NCH = 2 * NPAIR;              // chunks per thread per tile
   static_assert(kPartial || NPAIR * kPfThreads == kPairs, "tile split");
+  static_assert(kRowB % 16 == 0 && kVtB % 16 == 0 && kBufBytes % 16 == 0, "16-byte LDS rows");
 };
+
+// max over the 4 lanes of a query row (c, c + 16, c + 32, c + 48): the row
+// swaps exchange 16-lane rows and 32-lane halves without the LDS crossbar
+__device__ __forceinline__ float row_max4(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto r16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  x = fmaxf(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
+  const uint32_t v = __float_as_uint(x);
+  const auto r32 = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return fmaxf(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
+}
 
 template <class T, int D, int G>
 __global__ __launch_bounds__(kPfThreads) void prefill_kernel(PrefillArgs a, int block_size, int bs_shift) {
@@ -117,6 +138,11 @@ __global__ __launch_bounds__(kPfThreads) void prefill_kernel(PrefillArgs a, int 
 
   // this lane's query rows: column c of each of the wave's NG row groups;
   // row r = 16 (NG wave + grp) + c of the workgroup is token r / G, head r % G
+  // A negative scale goes into Q (flipping the sign bits is exact), so the
+  // kernel scales by sp > 0; a zero scale becomes the smallest normal float,
+  // which keeps -inf * sp = -inf for masked scores and changes no weight.
+  const uint32_t qneg = a.scale_log2 < 0.f ? 0x80008000u : 0u;
+  const float sp = fmaxf(fabsf(a.scale_log2), 1.17549435e-38f);
   int tq[NG], pos[NG];
   bool row_ok[NG];
   u32x4 qop[NG][NKC];
@@ -130,7 +156,11 @@ __global__ __launch_bounds__(kPfThreads) void prefill_kernel(PrefillArgs a, int 
     const char* qrow = reinterpret_cast<const char*>(a.query) +
                        (((size_t)(q0 + (row_ok[grp] ? tq[grp] : 0)) * a.num_q_heads + (size_t)g * G + hh) * D) * 2;
 #pragma unroll
-    for (int kc = 0; kc < NKC; ++kc) qop[grp][kc] = row_ok[grp] ? ld16(qrow + (32 * kc + 8 * gq) * 2) : z;
+    for (int kc = 0; kc < NKC; ++kc) {
+      qop[grp][kc] = row_ok[grp] ? ld16(qrow + (32 * kc + 8 * gq) * 2) : z;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) qop[grp][kc][e] ^= qneg;
+    }
   }
   const int wave_last = L - n + min(qb * QB + (wave + 1) * TPW, n) - 1;   // wave's largest position
   const int kend = L - n + min(qb * QB + QB, n);                          // keys the unit needs
@@ -139,74 +169,92 @@ __global__ __launch_bounds__(kPfThreads) void prefill_kernel(PrefillArgs a, int 
   const char* vpool = reinterpret_cast<const char*>(a.v_pool);
   const int bmask = block_size - 1;
 
-  // The table entries a tile needs are loaded one tile before its K/V, so
-  // the two dependent loads of a tile (entry, then data) overlap two tiles
-  // of compute.
+  // A key pair (t, t + 1) with t even lies in one block (block sizes are
+  // even), so a thread looks up one table entry and computes one address per
+  // pair.  Pairs at or past the context's end are read from its last pair:
+  // in bounds, and masked below.  The entries a tile needs are loaded one
+  // tile before its K/V, so the two dependent loads of a tile (entry, then
+  // data) overlap two tiles of compute.
+  const int last_pair = (L - 1) & ~1;
+  int ids[Lay::NPAIR];
   u32x4 kreg[Lay::NCH], vreg[Lay::NCH];
-  bool vok[Lay::NCH];
-  int ids[Lay::NCH];
-  // chunk j of this thread: key pair jp = j / 2 (pairs dealt over the threads,
-  // d-chunk fastest so 16 lanes cover a row), key 2 (pair / CPR) + (j & 1)
-  auto chunk_key = [&](int j) { return 2 * (((j >> 1) * kPfThreads + tid) / Lay::CPR) + (j & 1); };
-  auto chunk_dch = [&](int j) { return ((j >> 1) * kPfThreads + tid) % Lay::CPR; };
+  // unit jp of this thread: V^T pair position x (d-chunk fastest, so 16
+  // lanes cover a token row) holding the key pair vt_pair(x)
+  auto pair_pos = [&](int jp) { return (jp * kPfThreads + tid) / Lay::CPR; };
+  auto pair_key = [&](int jp) { return 2 * vt_pair(pair_pos(jp)); };
+  auto pair_dch = [&](int jp) { return (jp * kPfThreads + tid) % Lay::CPR; };
   const bool loader = !Lay::kPartial || tid < Lay::kPairs;
   auto load_ids = [&](int t0) {
     if (!loader) return;
 #pragma unroll
-    for (int j = 0; j < Lay::NCH; ++j) ids[j] = trow.entry(min(t0 + chunk_key(j), L - 1) >> bs_shift);
+    for (int jp = 0; jp < Lay::NPAIR; ++jp) ids[jp] = trow.entry(min(t0 + pair_key(jp), last_pair) >> bs_shift);
   };
   auto load_tile = [&](int t0) {
     if (!loader) return;
 #pragma unroll
-    for (int j = 0; j < Lay::NCH; ++j) {
-      const int key = chunk_key(j), dch = chunk_dch(j);
-      const int t = t0 + key;
-      const int tt = min(t, L - 1);
-      const int blk = ((unsigned)ids[j] < (unsigned)a.num_blocks) ? ids[j] : 0;
-      const size_t off = ((((size_t)blk * a.num_kv_heads + g) * block_size + (tt & bmask)) * D + dch * 8) * 2;
-      kreg[j] = ld16(kpool + off);
-      vreg[j] = ld16(vpool + off);
-      vok[j] = t < L;
+    for (int jp = 0; jp < Lay::NPAIR; ++jp) {
+      const int te = min(t0 + pair_key(jp), last_pair);
+      const int blk = ((unsigned)ids[jp] < (unsigned)a.num_blocks) ? ids[jp] : 0;
+      const size_t off =
+          ((((size_t)blk * a.num_kv_heads + g) * block_size + (te & bmask)) * D + pair_dch(jp) * 8) * 2;
+      kreg[2 * jp] = ld16(kpool + off);
+      kreg[2 * jp + 1] = ld16(kpool + off + D * 2);
+      vreg[2 * jp] = ld16(vpool + off);
+      vreg[2 * jp + 1] = ld16(vpool + off + D * 2);
     }
   };
-  auto store_tile = [&](int buf) {
+  // Keys at or past L (only in the tile that holds the context's end) get
+  // V = 0: their slots may hold anything, and a zero weight times a NaN is NaN.
+  auto store_tile = [&](int buf, int t0) {
     if (!loader) return;
     char* kb = lds + buf * Lay::kBufBytes;
     char* vb = kb + Lay::kKBytes;
-    const u32x4 z = {0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int j = 0; j < Lay::NCH; ++j)
-      *reinterpret_cast<u32x4*>(kb + chunk_key(j) * Lay::kRowB + chunk_dch(j) * 16) = kreg[j];
+    const bool tail = t0 + kPfKeys > L;   // uniform
 #pragma unroll
     for (int jp = 0; jp < Lay::NPAIR; ++jp) {
-      const int key = chunk_key(2 * jp), dch = chunk_dch(2 * jp);   // keys key, key + 1
-      const u32x4 v0 = vok[2 * jp] ? vreg[2 * jp] : z;            // slots past the context
-      const u32x4 v1 = vok[2 * jp + 1] ? vreg[2 * jp + 1] : z;    // may hold anything
+      const int key = pair_key(jp), dch = pair_dch(jp);
+      *reinterpret_cast<u32x4*>(kb + key * Lay::kRowB + dch * 16) = kreg[2 * jp];
+      *reinterpret_cast<u32x4*>(kb + (key + 1) * Lay::kRowB + dch * 16) = kreg[2 * jp + 1];
+      u32x4 v0 = vreg[2 * jp], v1 = vreg[2 * jp + 1];
+      if (tail) {
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        v0 = t0 + key < L ? v0 : z;
+        v1 = t0 + key + 1 < L ? v1 : z;
+      }
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         // element e of both keys: low halves (even e) or high halves (odd e)
         const uint32_t w = (e & 1) ? __builtin_amdgcn_perm(v1[e >> 1], v0[e >> 1], 0x07060302u)
                                    : __builtin_amdgcn_perm(v1[e >> 1], v0[e >> 1], 0x05040100u);
         const int row = dch * 8 + e;
-        *reinterpret_cast<uint32_t*>(vb + row * Lay::kVtB + (((key >> 1) ^ vt_swizzle(row)) << 2)) = w;
+        *reinterpret_cast<uint32_t*>(vb + row * Lay::kVtB + ((pair_pos(jp) ^ vt_swizzle(row)) << 2)) = w;
       }
     }
   };
 
-  float m_run[NG], l_run[NG];
-  f32x4 oacc[NG][NDT];
+  // Row sums come from the matrix cores: a 16 x 32 operand of ones times the
+  // rounded P^T gives every row of the product the sum of P over the keys,
+  // so lane l holds its query row's sum in each of its 4 accumulators, and
+  // the sum is of the same rounded weights that multiply V.
+  float m_run[NG];
+  f32x4 oacc[NG][NDT], lacc[NG];
 #pragma unroll
   for (int grp = 0; grp < NG; ++grp) {
     m_run[grp] = kNegInf;
-    l_run[grp] = 0.f;
+    lacc[grp] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) oacc[grp][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
+  const uint32_t one2 = pack2<T>(1.f, 1.f);
+  const u32x4 ones = {one2, one2, one2, one2};
+  // the wave's smallest position: a tile whose keys all lie at or below it
+  // is seen whole by every row of the wave and needs no causal mask
+  const int wave_first = L - n + min(qb * QB + wave * TPW, n - 1);
 
   const int ntiles = (kend + kPfKeys - 1) / kPfKeys;
   load_ids(0);
   load_tile(0);
-  store_tile(0);
+  store_tile(0, 0);
   if (ntiles > 1) load_ids(kPfKeys);
   __syncthreads();
   for (int it = 0; it < ntiles; ++it) {
@@ -242,7 +290,10 @@ __global__ __launch_bounds__(kPfThreads) void prefill_kernel(PrefillArgs a, int 
 #endif
       // lane holds keys 16 sub + 4 gq + i; k-slot 8 gq + j of PV product h
       // (keys [32 h, 32 h + 32)) means key 32 h + 4 gq + j (j < 4) or
-      // 32 h + 16 + 4 gq + j - 4
+      // 32 h + 16 + 4 gq + j - 4.  Scores stay raw (scale > 0 after the sign
+      // went into Q); the scale enters the max once and each exponent as one
+      // fused multiply-add.
+      const bool diag = t0 + kPfKeys - 1 > wave_first;   // wave-uniform
       u32x4 pb[NG][kPfSub / 2];
       const int kt = t0 + 4 * gq;
 #pragma unroll
@@ -251,28 +302,37 @@ __global__ __launch_bounds__(kPfThreads) void prefill_kernel(PrefillArgs a, int 
 #pragma unroll
         for (int sub = 0; sub < kPfSub; ++sub)
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            sc[4 * sub + i] = (kt + 16 * sub + i <= pos[grp]) ? st[grp][sub][i] * a.scale_log2 : kNegInf;
+          for (int i = 0; i < 4; ++i) sc[4 * sub + i] = st[grp][sub][i];
+        if (diag) {
+#pragma unroll
+          for (int sub = 0; sub < kPfSub; ++sub)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              sc[4 * sub + i] = (kt + 16 * sub + i <= pos[grp]) ? sc[4 * sub + i] : kNegInf;
+        }
         float tmax = sc[0];
 #pragma unroll
         for (int i = 1; i < 4 * kPfSub; ++i) tmax = fmaxf(tmax, sc[i]);
-        tmax = fmaxf(tmax, xor_lane<16>(tmax));
-        tmax = fmaxf(tmax, xor_lane<32>(tmax));
-        const bool grow = tmax > m_run[grp] + kPfLazy;    // always true on a row's first key
-        if (__any(grow)) {
-          const float m_new = grow ? tmax : m_run[grp];
+        tmax *= sp;   // -inf stays -inf
+        // The 4 lanes of a row share m_run, and it moves only when a score of
+        // the row exceeds it by more than 2^kPfLazy, so each lane tests its own
+        // scores and the row-wide max is formed only when some lane asks.
+        // Every row sees key 0 in the first tile (so m_run is finite after it,
+        // and a masked score's exponent is -inf, giving 0).
+        if (__any(tmax > m_run[grp] + kPfLazy)) {
+          const float rmax = row_max4(tmax);
+          const bool grow = rmax > m_run[grp] + kPfLazy;   // the same in the row's 4 lanes
+          const float m_new = grow ? rmax : m_run[grp];
           const float alpha = grow ? fast_exp2(m_run[grp] - m_new) : 1.f;
           m_run[grp] = m_new;
-          l_run[grp] *= alpha;
+          lacc[grp] *= alpha;
 #pragma unroll
           for (int dt = 0; dt < NDT; ++dt) oacc[grp][dt] *= alpha;
         }
+        const float nm = -m_run[grp];
         float p[4 * kPfSub];
 #pragma unroll
-        for (int i = 0; i < 4 * kPfSub; ++i) {
-          p[i] = sc[i] == kNegInf ? 0.f : fast_exp2(sc[i] - m_run[grp]);
-          l_run[grp] += p[i];
-        }
+        for (int i = 0; i < 4 * kPfSub; ++i) p[i] = fast_exp2(fmaf(sc[i], sp, nm));
 #pragma unroll
         for (int h = 0; h < kPfSub / 2; ++h) {
           pb[grp][h][0] = pack2<T>(p[8 * h + 0], p[8 * h + 1]);
@@ -284,19 +344,25 @@ __global__ __launch_bounds__(kPfThreads) void prefill_kernel(PrefillArgs a, int 
       // V^T operands one step ahead of their products, so LDS latency
       // overlaps the matrix cores instead of preceding each product
       constexpr int NVS = NDT * (kPfSub / 2);
+      // row 16 dt + c of V^T (c < 16) has swizzle sw = vt_swizzle(16 dt), and
+      // lane (c, gq) of half h reads dwords (16 h + 4 gq) ^ sw .. + 3 =
+      // 16 (h ^ sw / 16) + 4 (gq ^ (sw / 4) % 4) .. + 3: the row base, a
+      // constant and one of four lane offsets
+      const char* vlane = vb + c * Lay::kVtB;
+      auto read_v = [&](int step) {
+        const int h = step / NDT, dt = step % NDT;
+        const int sw = vt_swizzle(16 * dt);
+        const char* src = vlane + 16 * dt * Lay::kVtB + 64 * (h ^ (sw >> 4)) + 16 * (gq ^ ((sw >> 2) & 3));
+        return *reinterpret_cast<const u32x4*>(src);
+      };
+      u32x4 av = read_v(0);
+#pragma unroll
+      for (int grp = 0; grp < NG; ++grp)
+#pragma unroll
+        for (int h = 0; h < kPfSub / 2; ++h) lacc[grp] = mfma_16x16x32<T>(ones, pb[grp][h], lacc[grp]);
       // step = h NDT + dt: consecutive products accumulate into different d
       // tiles, so a product's dependence on the same tile's previous one is
       // NDT products back (the matrix-core latency stays covered)
-      auto read_v = [&](int step) {
-        const int h = step / NDT, dt = step % NDT;
-        const int row = 16 * dt + c;
-        const char* vrow = vb + row * Lay::kVtB;
-        const int sw = vt_swizzle(row);
-        const uint2 lo = *reinterpret_cast<const uint2*>(vrow + (((16 * h + 2 * gq) ^ sw) << 2));
-        const uint2 hi = *reinterpret_cast<const uint2*>(vrow + (((16 * h + 8 + 2 * gq) ^ sw) << 2));
-        return u32x4{lo.x, lo.y, hi.x, hi.y};
-      };
-      u32x4 av = read_v(0);
 #pragma unroll
       for (int step = 0; step < NVS; ++step) {
         const u32x4 nxt = read_v(step + 1 < NVS ? step + 1 : step);
@@ -308,6 +374,7 @@ __global__ __launch_bounds__(kPfThreads) void prefill_kernel(PrefillArgs a, int 
 #if PA_PREFILL_SCHED > 0
       // keep each V^T read PA_PREFILL_SCHED products ahead of its use
       __builtin_amdgcn_sched_group_barrier(0x100, PA_PREFILL_SCHED, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, NG * (kPfSub / 2), 0);
 #pragma unroll
       for (int step = 0; step < NVS; ++step) {
         __builtin_amdgcn_sched_group_barrier(0x008, NG, 0);
@@ -315,17 +382,14 @@ __global__ __launch_bounds__(kPfThreads) void prefill_kernel(PrefillArgs a, int 
       }
 #endif
     }
-    if (it + 1 < ntiles) store_tile((it + 1) & 1);   // the other buffer: free since the last barrier
+    if (it + 1 < ntiles) store_tile((it + 1) & 1, t0 + kPfKeys);   // the other buffer: free since the last barrier
     __syncthreads();
   }
 
 #pragma unroll
   for (int grp = 0; grp < NG; ++grp) {
-    float l = l_run[grp];
-    l += xor_lane<16>(l);
-    l += xor_lane<32>(l);
     if (!row_ok[grp]) continue;
-    const float inv = 1.f / l;
+    const float inv = 1.f / lacc[grp][0];
     char* orow = reinterpret_cast<char*>(a.out) +
                  (((size_t)(q0 + tq[grp]) * a.num_q_heads + (size_t)g * G + hh) * D) * 2;
 #pragma unroll
