@@ -24,10 +24,13 @@ MANT = {"f16": 10, "bf16": 7}
 
 def p_rounding(q, b, starts, seqs=None):
     """Allowance for rounding the probabilities to the input type before the
-    product with V: each weight carries a relative error of at most half an
-    ulp, 2^-(m+1), so the output moves by at most 2^-(m+1) sum_t w_t |v_t| /
-    sum_t w_t -- the oracle over |V| gives that weighted mean exactly.  Twice
-    that, for the accumulated fp32 rounding of the sums."""
+    products with V and with the ones that form the row sums: each weight
+    carries a relative error of at most half an ulp, u = 2^-(m+1), and the
+    normaliser is the sum of the same rounded weights, so each normalised
+    weight is off by at most 2u / (1 - u) relatively and the output by at most
+    that times sum_t w_t |v_t| / sum_t w_t -- the oracle over |V| gives that
+    weighted mean exactly.  2^-m covers 2u / (1 - u) up to a term of order u^2,
+    which the 2-ulp part of the bound absorbs."""
     kabs = b.k_pool
     vabs = W.to_storage(np.abs(O.upcast(b.v_pool, b.dtype)).astype(np.float32), b.dtype)
     mean = O.prefill_attention(q, kabs, vabs, b.block_tables, b.context_lens, starts, b.scale, b.block_size,
