@@ -41,7 +41,10 @@ constexpr float kLazy = 8.f;
 // Tiles in flight per wave (tile_loop's ring): the current one and the next.
 // Rings of 3 and 4 (8 KiB tiles, fewer resident waves for their registers)
 // streamed no faster on the GQA batches.
-constexpr int kRing = 2;
+#ifndef PA_TILE_RING
+#define PA_TILE_RING 2
+#endif
+constexpr int kRing = PA_TILE_RING;
 
 // Stage table entries [first, first+count) of one sequence into this wave's
 // LDS window (ids clamped into the pool: memory-safe on bad tables).  LDS
@@ -181,6 +184,12 @@ struct ValuBuf {
   u32x4 k[NL], v[NL];
 };
 
+// Resident workgroups per CU of the VALU core's balanced grid (0: as many as
+// its resources allow, 3 for MHA fp16).  One was 2.6 % faster than three on
+// the OPT-13B-shaped MHA batch: fewer, longer ranges pay fewer segment starts.
+#ifndef PA_VALU_WG_PER_CU
+#define PA_VALU_WG_PER_CU 1
+#endif
 template <class T, int D, int BS, int H>
 struct ValuCore {
   static constexpr int EB = T::bytes;
@@ -189,7 +198,7 @@ struct ValuCore {
   static constexpr int NE = 16 / EB;      // elements per 16 bytes
   static constexpr int DPL = NL * NE;     // elements per lane (= D / 4)
   static constexpr int HEADS = H;
-  static constexpr int kBalancedWgPerCu = 0;  // as many as stay resident
+  static constexpr int kBalancedWgPerCu = PA_VALU_WG_PER_CU;
   static_assert(DPL * 4 == D, "layout");
   static_assert(kTblWin * BS % kTile == 0, "window");
   // bytes a tile's buffer resource spans: its 16 rows (8 per block at block_size 8)
