@@ -401,6 +401,33 @@ def cold_decode_leg(decode_call, stream, reps: int = 10, evict_bytes: int = 1 <<
             "what": "median of per-call HIP-event times, each call after reading a 1 GiB scratch buffer"}
 
 
+def achievable_read_leg(stream, nbytes: int = 4 << 30, reps: int = 10) -> dict:
+    """The box's achievable HBM read bandwidth: pa_stream_read sweeping a
+    4 GiB buffer (16 times the MALL), reps back-to-back calls timed with HIP
+    events on the stream, after two untimed ones."""
+    import torch
+
+    import paged_kv_cache_313_amd as P
+
+    buf = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
+    partials = torch.empty(P._lib.PA_STREAM_READ_PARTIALS, dtype=torch.int32, device="cuda")
+    with torch.cuda.stream(stream):
+        for _ in range(2):
+            P.stream_read(buf, partials)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            P.stream_read(buf, partials)
+        e1.record(stream)
+    e1.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del buf, partials
+    return {"gbps": nbytes / (ms * 1e-3) / 1e9, "bytes": nbytes, "ms": ms, "reps": reps,
+            "what": "pa_stream_read: each workgroup sweeps a contiguous range of a 4 GiB buffer in 16-byte "
+                    "loads, 8 in flight per thread; decode_frac_of_achievable = roofline.achieved / gbps"}
+
+
 def main():
     args = parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -551,6 +578,8 @@ def main():
     cold = cold_decode_leg(decode_only, stream)
     cold["kv_read_gbps"] = kv_bytes / (cold["decode_ms_median"] * 1e-3) / 1e9
     cold["pct_of_hbm_peak"] = 100.0 * alg_bytes / (cold["decode_ms_median"] * 1e-3) / 1e9 / HBM_PEAK_GBPS
+    stream_leg = achievable_read_leg(stream)
+    stream_leg["decode_frac_of_achievable"] = achieved / stream_leg["gbps"]
     bm_leg = block_manager_leg(b, max(args.steps, 10))
     swap = None if args.no_swap else swap_leg(d, b)
     prefill = None if args.no_prefill else prefill_leg(parity_seqs=() if args.no_cpu_baseline else (0, 9))
@@ -602,6 +631,7 @@ def main():
         "cpu_baseline": cpu,
         "parity": parity,
         "decode_cold_cache": cold,
+        "achievable_read": stream_leg,
         "block_manager": bm_leg,
         "swap": swap,
         "prefill": prefill,

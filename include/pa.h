@@ -308,6 +308,21 @@ pa_status pa_swap_in(const void* host_src, void* k_pool, void* v_pool, const int
                      int32_t num_ids, int32_t num_kv_heads, int32_t block_size, int32_t head_dim,
                      int32_t num_blocks, pa_dtype dtype, void* stream);
 
+/*
+ * pa_stream_read -- measurement aid, not a step of the method: the
+ * achievable HBM read bandwidth that the decode kernel's streaming is judged
+ * against (a plain sweep has no table, softmax or output).
+ *   buf       DEVICE, 16-byte aligned (PA_ERR_ALIGN), read once
+ *   bytes     a multiple of 16 (PA_ERR_SHAPE); 0 is a no-op returning PA_OK
+ *   partials  DEVICE uint32 [PA_STREAM_READ_PARTIALS], caller-owned; receives
+ *             one XOR of 32-bit words per workgroup, and the XOR of all
+ *             partials is the XOR of every 32-bit word of the buffer (so the
+ *             result can be checked and no load can be skipped)
+ * Asynchronous on `stream`; allocates nothing.
+ */
+#define PA_STREAM_READ_PARTIALS 16384
+pa_status pa_stream_read(const void* buf, uint64_t bytes, uint32_t* partials, void* stream);
+
 /* Static, human-readable name of a status code.  HOST only. */
 const char* pa_status_string(pa_status status);
 

@@ -20,7 +20,7 @@ from .block_manager import BlockManager  # noqa: F401
 
 __all__ = ["kv_append", "block_copy", "decode_attention", "prefill_attention", "decode_attention_hier",
            "prefill_attention_hier", "decode_workspace_bytes",
-           "choose_partition", "swap_out", "swap_in", "swap_buffer", "PagedKVError", "load",
+           "choose_partition", "swap_out", "swap_in", "swap_buffer", "stream_read", "PagedKVError", "load",
            "PA_PARTITION_BALANCED", "BlockManager"]
 
 _DTYPES = {torch.float32: _lib.PA_F32, torch.float16: _lib.PA_F16, torch.bfloat16: _lib.PA_BF16}
@@ -132,6 +132,21 @@ def swap_in(host: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor, bloc
                         _dev(block_ids, "block_ids"), n, Hkv, bs, D, NB, _dtype_code(k_pool),
                         _stream(k_pool, stream))
     _lib.check("pa_swap_in", st)
+
+
+def stream_read(buf: torch.Tensor, partials: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Measurement aid: read every byte of the contiguous device tensor
+    ``buf`` once (pa_stream_read) and return the device uint32-valued int32
+    tensor of per-workgroup XOR partials [PA_STREAM_READ_PARTIALS]."""
+    lib = load()
+    nbytes = buf.numel() * buf.element_size()
+    if partials is None:
+        partials = torch.empty(_lib.PA_STREAM_READ_PARTIALS, dtype=torch.int32, device=buf.device)
+    if partials.dtype != torch.int32 or partials.numel() < _lib.PA_STREAM_READ_PARTIALS:
+        raise ValueError(f"partials must be int32 with at least {_lib.PA_STREAM_READ_PARTIALS} entries")
+    st = lib.pa_stream_read(_dev(buf, "buf"), nbytes, _dev(partials, "partials"), _stream(buf, stream))
+    _lib.check("pa_stream_read", st)
+    return partials
 
 
 def decode_workspace_bytes(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int,

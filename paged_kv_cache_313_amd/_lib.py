@@ -11,6 +11,7 @@ LIB_PATH = os.path.join(HERE, "libpagedkv.so")
 
 PA_OK = 0
 PA_F32, PA_F16, PA_BF16 = 0, 1, 2
+PA_STREAM_READ_PARTIALS = 16384   # include/pa.h
 PA_PARTITION_BALANCED = -1
 STATUS_NAMES = {0: "PA_OK", 1: "PA_ERR_NULL", 2: "PA_ERR_SHAPE", 3: "PA_ERR_BLOCK_SIZE",
                 4: "PA_ERR_DTYPE", 5: "PA_ERR_PARTITION", 6: "PA_ERR_WORKSPACE", 7: "PA_ERR_HIP",
@@ -40,6 +41,7 @@ SIGNATURES = {
     "pa_block_copy": (_c_i32, [_vp, _vp, _vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _vp]),
     "pa_swap_out": (_c_i32, [_vp, _vp, _vp, _c_i32, _vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _vp]),
     "pa_swap_in": (_c_i32, [_vp, _vp, _vp, _vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _vp]),
+    "pa_stream_read": (_c_i32, [_vp, ctypes.c_uint64, _vp, _vp]),
     "pa_status_string": (ctypes.c_char_p, [_c_i32]),
     # include/pa_block_manager.h (host only)
     "pa_bm_create": (_c_i32, [_c_i32, _c_i32, ctypes.POINTER(_vp)]),

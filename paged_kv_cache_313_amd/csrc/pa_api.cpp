@@ -181,6 +181,15 @@ PA_EXPORT pa_status pa_swap_in(const void* host_src, void* k_pool, void* v_pool,
                    block_size, head_dim, num_blocks, dtype, stream);
 }
 
+PA_EXPORT pa_status pa_stream_read(const void* buf, uint64_t bytes, uint32_t* partials, void* stream) {
+  if (bytes == 0) return PA_OK;
+  if (!buf || !partials) return PA_ERR_NULL;
+  if (bytes % 16 != 0) return PA_ERR_SHAPE;
+  if (!aligned16(buf)) return PA_ERR_ALIGN;
+  return hip_status(pa::launch_stream_read(buf, bytes, partials, PA_STREAM_READ_PARTIALS,
+                                           reinterpret_cast<hipStream_t>(stream)));
+}
+
 // Two-level tables: the large-page arguments of the *_hier entry points.
 struct HierTables {
   const int32_t* large_tables = nullptr;

@@ -29,6 +29,11 @@ hipError_t launch_block_copy(void* k_pool, void* v_pool, const int32_t* block_ma
 // max_wg in all; cached per kernel/device.
 hipError_t balanced_grid(const void* kernel, int block_threads, int max_per_cu, int max_wg, int* nwg);
 
+// Streaming read of bytes (a multiple of 16) at buf, one XOR partial per
+// workgroup into partials[0 .. num_partials).
+hipError_t launch_stream_read(const void* buf, uint64_t bytes, uint32_t* partials, int32_t num_partials,
+                              hipStream_t stream);
+
 // Decode: the segment kernel of the chosen mode plus, when results are split,
 // its merge kernel.  f16/bf16 with group size 2..16 run the MFMA core, all
 // other cases the VALU core.

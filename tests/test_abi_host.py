@@ -182,3 +182,16 @@ def test_swap_binding_refuses_pageable_host_memory(lib):
     host = torch.empty(16)
     with pytest.raises(ValueError):
         P._swap_args(torch.empty(4, 1, 16, 64), torch.empty(4, 1, 16, 64), torch.zeros(1, dtype=torch.int32), host)
+
+
+@pytest.mark.parametrize("buf,nbytes,partials,status", [
+    (A, 0, None, 0), (None, 0, None, 0), (None, 64, A, 1), (A, 64, None, 1), (A, 17, B, 2), (A + 8, 64, B, 8),
+])
+def test_stream_read_argument_checks(lib, buf, nbytes, partials, status):
+    assert lib.pa_stream_read(buf, nbytes, partials, None) == status
+
+
+def test_stream_read_binding_refuses_cpu_tensors(lib):
+    import torch
+    with pytest.raises(ValueError, match="GPU"):
+        P.stream_read(torch.zeros(64, dtype=torch.int32))
