@@ -311,7 +311,7 @@ def prefill_leg(reps: int = 20, parity_seqs=(0, 9)) -> dict:
     return {"workload": PREFILL_WORKLOAD, "ms": ms, "tflops": tflops, "flops_per_call": flops,
             "roofline": {"bound": "mfma", "achieved": tflops, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": tflops / MFMA_BF16_PEAK_TFLOPS,
-                         "kernel": "pa_prefill_attention: prefill_kernel<BF16, 128, 4>"},
+                         "kernel": "pa_prefill_attention: prefill_kernel<BF16, 128, 4, 8> (8-wave workgroups)"},
             "parity": parity}
 
 

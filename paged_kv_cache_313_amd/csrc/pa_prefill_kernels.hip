@@ -8,14 +8,15 @@
 // to the tokens t <= p of the sequence's paged context.  This is a dense
 // contraction on both sides of the softmax, so both run on the matrix cores.
 //
-// Work unit: one workgroup of 4 waves per (sequence, KV head, block of query
-// tokens).  The 64 query rows of a workgroup are (token, head) pairs of the G
-// heads sharing the KV head, heads fastest: each wave owns 16 of them.  Keys
-// advance 32 at a time through double-buffered LDS tiles: K row-major, V
-// transposed (d-major), both gathered through the block table by all 256
-// threads, the next tile's loads in flight while the current one is used.
+// Work unit: one workgroup of 4 or 8 waves per (sequence, KV head, block of
+// query tokens).  The 128 or 256 query rows of a workgroup are (token, head)
+// pairs of the G heads sharing the KV head, heads fastest: each wave owns two
+// groups of 16.  Keys advance 64 at a time through double-buffered LDS tiles:
+// K row-major, V transposed (d-major), both gathered through the block table
+// by all threads, the next tile's loads in flight while the current one is
+// used.
 //
-// Per 32-key tile, each wave computes
+// Per tile, each wave computes, for each of its row groups and 16-key slices,
 //   S^T[key][row] = K Q^T          (A = K from LDS, B = its query rows, kept
 //                                   in registers for the whole unit)
 // so that lane l holds the scores of query row l % 16 for keys
@@ -24,8 +25,9 @@
 //   O^T[d][row] += V^T P^T          (A = V^T from LDS)
 // once k-slot 8 (l / 16) + j is taken to mean those keys (the contraction
 // order is free as long as A and B agree).  The probabilities never leave the
-// lane, and a query row's statistics are shared by the 4 lanes l % 16 = row:
-// two butterflies reduce a max or a sum.  Online softmax in the log2 domain
+// lane; a query row's running max is shared by the 4 lanes l % 16 = row (two
+// row swaps form it when it has to move) and its sum comes from the matrix
+// cores.  Online softmax in the log2 domain
 // with a lazy rescale (a row's reference max moves only when a score exceeds
 // it by more than 2^8), P rounded to the input type for the MFMA, fp32
 // accumulation.
@@ -34,11 +36,15 @@
 
 namespace pa {
 
-#ifndef PA_PREFILL_WAVES
-#define PA_PREFILL_WAVES 4
+// Workgroups of 8 waves (256 query rows) stage each K/V tile once for twice
+// the rows of a 4-wave one; measured, they were 8-14 % faster when every
+// sequence brings at most 2048 new tokens (chunked prefill over a cached
+// prefix, short prompts) and 5-11 % slower on fresh prompts of 4K-8K tokens,
+// whose causal diagonals leave the waves of one workgroup unequal work at
+// each barrier with no second workgroup on the CU to fill the wait.
+#ifndef PA_PREFILL_WIDE_MAX_QUERY
+#define PA_PREFILL_WIDE_MAX_QUERY 2048
 #endif
-constexpr int kPfWaves = PA_PREFILL_WAVES;
-constexpr int kPfThreads = kPfWaves * kWave;
 #ifndef PA_PREFILL_KEYS
 #define PA_PREFILL_KEYS 64
 #endif
@@ -58,7 +64,6 @@ constexpr float kPfLazy = 8.f;
 #define PA_PREFILL_SCHED 3
 #endif
 constexpr int kPfGroups = PA_PREFILL_GROUPS;
-constexpr int kPfRows = kPfWaves * 16 * kPfGroups;   // query rows (token, head) per workgroup
 
 // K is staged row-major.  V is staged transposed: row d of a tile holds its
 // key pairs as dwords (the d-th elements of keys 2p and 2p + 1).  The pairs
@@ -77,18 +82,19 @@ __device__ __forceinline__ int vt_swizzle(int row) { return 4 * ((row >> 4) & (k
 __device__ __forceinline__ int vt_pair(int x) {
   return 16 * (x >> 4) + 2 * ((x >> 2) & 3) + (x & 1) + 8 * ((x >> 1) & 1);
 }
-template <int D>
+template <int D, int NW>
 struct PfLayout {
+  static constexpr int kThreads = NW * kWave;
   static constexpr int kRowB = D * 2 + 16;           // K row pitch in LDS (bytes), padded
   static constexpr int kVtB = kPfKeys * 2 + 16;      // V^T row pitch in LDS (bytes), padded, 16-byte aligned
   static constexpr int kKBytes = kPfKeys * kRowB;
   static constexpr int kBufBytes = kKBytes + D * kVtB;
   static constexpr int CPR = D / 8;                  // 16-byte chunks per token row
   static constexpr int kPairs = kPfKeys / 2 * CPR;   // (key pair, d-chunk) units per tile
-  static constexpr bool kPartial = kPairs < kPfThreads;   // then threads >= kPairs load nothing
-  static constexpr int NPAIR = kPartial ? 1 : kPairs / kPfThreads;   // key pairs per thread per tile
+  static constexpr bool kPartial = kPairs < kThreads;   // then threads >= kPairs load nothing
+  static constexpr int NPAIR = kPartial ? 1 : kPairs / kThreads;   // key pairs per thread per tile
   static constexpr int NCH = 2 * NPAIR;              // chunks per thread per tile
-  static_assert(kPartial || NPAIR * kPfThreads == kPairs, "tile split");
+  static_assert(kPartial || NPAIR * kThreads == kPairs, "tile split");
   static_assert(kRowB % 16 == 0 && kVtB % 16 == 0 && kBufBytes % 16 == 0, "16-byte LDS rows");
 };
 
@@ -103,11 +109,12 @@ __device__ __forceinline__ float row_max4(float x) {
   return fmaxf(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
 }
 
-template <class T, int D, int G>
-__global__ __launch_bounds__(kPfThreads) void prefill_kernel(PrefillArgs a, int block_size, int bs_shift) {
-  using Lay = PfLayout<D>;
+template <class T, int D, int G, int NW>
+__global__ __launch_bounds__(NW * kWave) void prefill_kernel(PrefillArgs a, int block_size, int bs_shift) {
+  using Lay = PfLayout<D, NW>;
+  constexpr int kPfThreads = Lay::kThreads;
   constexpr int NG = kPfGroups;
-  constexpr int QB = kPfRows / G;          // query tokens per workgroup
+  constexpr int QB = NW * 16 * NG / G;     // query tokens per workgroup
   constexpr int TPW = 16 * NG / G;         // query tokens per wave
   constexpr int NKC = D / 32;              // k-chunks of the score MFMA
   constexpr int NDT = D / 16;              // 16-row d tiles of the output
@@ -402,26 +409,32 @@ __global__ __launch_bounds__(kPfThreads) void prefill_kernel(PrefillArgs a, int 
   }
 }
 
-template <class T, int D>
-static hipError_t prefill_group(const PrefillArgs& a, int bs, int group, hipStream_t st) {
+template <class T, int D, int NW>
+static hipError_t prefill_waves(const PrefillArgs& a, int bs, int group, hipStream_t st) {
   int shift = 0;
   while ((1 << shift) < bs) ++shift;
-  const int QB = kPfRows / group;
+  const int QB = NW * 16 * kPfGroups / group;
   PrefillArgs args = a;
   args.qblocks = (a.max_query_len + QB - 1) / QB;
   const uint64_t units = (uint64_t)a.num_seqs * a.num_kv_heads * args.qblocks;
   if (units == 0) return hipSuccess;
   if (units > 0x7fffffffull) return hipErrorInvalidValue;
-  const dim3 grid((uint32_t)units), block(kPfThreads);
+  const dim3 grid((uint32_t)units), block(NW * kWave);
   switch (group) {
-    case 1: hipLaunchKernelGGL((prefill_kernel<T, D, 1>), grid, block, 0, st, args, bs, shift); break;
-    case 2: hipLaunchKernelGGL((prefill_kernel<T, D, 2>), grid, block, 0, st, args, bs, shift); break;
-    case 4: hipLaunchKernelGGL((prefill_kernel<T, D, 4>), grid, block, 0, st, args, bs, shift); break;
-    case 8: hipLaunchKernelGGL((prefill_kernel<T, D, 8>), grid, block, 0, st, args, bs, shift); break;
-    case 16: hipLaunchKernelGGL((prefill_kernel<T, D, 16>), grid, block, 0, st, args, bs, shift); break;
+    case 1: hipLaunchKernelGGL((prefill_kernel<T, D, 1, NW>), grid, block, 0, st, args, bs, shift); break;
+    case 2: hipLaunchKernelGGL((prefill_kernel<T, D, 2, NW>), grid, block, 0, st, args, bs, shift); break;
+    case 4: hipLaunchKernelGGL((prefill_kernel<T, D, 4, NW>), grid, block, 0, st, args, bs, shift); break;
+    case 8: hipLaunchKernelGGL((prefill_kernel<T, D, 8, NW>), grid, block, 0, st, args, bs, shift); break;
+    case 16: hipLaunchKernelGGL((prefill_kernel<T, D, 16, NW>), grid, block, 0, st, args, bs, shift); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+template <class T, int D>
+static hipError_t prefill_group(const PrefillArgs& a, int bs, int group, hipStream_t st) {
+  return a.max_query_len <= PA_PREFILL_WIDE_MAX_QUERY ? prefill_waves<T, D, 8>(a, bs, group, st)
+                                                      : prefill_waves<T, D, 4>(a, bs, group, st);
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, Elem elem, int head_dim, int block_size, int group,

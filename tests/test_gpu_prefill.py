@@ -63,23 +63,31 @@ CASES = [(dt, D, bs, G) for dt in ("f16", "bf16") for D in (64, 128) for bs in (
 CASES += [("bf16", 128, 16, 2), ("bf16", 128, 16, 8), ("bf16", 128, 16, 16), ("f16", 64, 8, 16)]
 
 
+# The library runs 8-wave workgroups when max_query_len <= 2048 and 4-wave
+# ones above; a host bound above the real n selects the 4-wave kernel (the
+# extra query blocks have no rows and exit).
+NARROW_MAX_QUERY = 4096
+
+
+@pytest.mark.parametrize("max_query_len", [None, NARROW_MAX_QUERY], ids=["8waves", "4waves"])
 @pytest.mark.parametrize("dtype,D,bs,G", CASES)
-def test_prefill_matches_oracle(dtype, D, bs, G):
+def test_prefill_matches_oracle(dtype, D, bs, G, max_query_len):
     b, q, starts = case(dtype, D, bs, G, LENS, NEWS, seed=D + bs + G)
-    note(f"prefill dtype={dtype} D={D} bs={bs} G={G}")
-    out = run(b, q, starts)
+    note(f"prefill dtype={dtype} D={D} bs={bs} G={G} max_query_len={max_query_len}")
+    out = run(b, q, starts, max_query_len=max_query_len)
     ref = O.prefill_attention(q, b.k_pool, b.v_pool, b.block_tables, b.context_lens, starts, b.scale,
                               b.block_size, dtype)
     check_close(gpu_out_f64(out, dtype), ref, dtype, f"prefill {dtype}/D{D}/bs{bs}/G{G}", ulps=ULPS,
                 extra=p_rounding(q, b, starts))
 
 
-def test_fresh_prompts_and_whole_context():
+@pytest.mark.parametrize("max_query_len", [None, NARROW_MAX_QUERY], ids=["8waves", "4waves"])
+def test_fresh_prompts_and_whole_context(max_query_len):
     """n = L for every sequence: plain causal prefill through the pages."""
     lens = [5, 31, 32, 33, 129]
     b, q, starts = case("bf16", 128, 16, 4, lens, lens, seed=3)
-    note("prefill fresh prompts")
-    out = run(b, q, starts)
+    note(f"prefill fresh prompts max_query_len={max_query_len}")
+    out = run(b, q, starts, max_query_len=max_query_len)
     ref = O.prefill_attention(q, b.k_pool, b.v_pool, b.block_tables, b.context_lens, starts, b.scale, 16, "bf16")
     check_close(gpu_out_f64(out, "bf16"), ref, "bf16", "fresh prompts", ulps=ULPS, extra=p_rounding(q, b, starts))
     # the first token of each fresh prompt sees only itself: exactly its value row
@@ -113,6 +121,18 @@ def test_rows_not_to_write_are_left_alone():
                                seqs=[2])
     check_close(got[starts[2]:starts[2] + 64], ref2[starts[2]:starts[2] + 64], "f16", "seq 2 head", ulps=ULPS,
                 extra=ex[starts[2]:starts[2] + 64])
+
+
+def test_long_fresh_prompt_four_wave_path():
+    """A 2500-token fresh prompt (above the 8-wave bound by itself), GQA 8/2,
+    D 128, bf16: every output vs the oracle."""
+    lens = [2500]
+    b, q, starts = case("bf16", 128, 16, 4, lens, lens, seed=13)
+    note("prefill long fresh prompt")
+    out = run(b, q, starts)
+    ref = O.prefill_attention(q, b.k_pool, b.v_pool, b.block_tables, b.context_lens, starts, b.scale, 16, "bf16")
+    check_close(gpu_out_f64(out, "bf16"), ref, "bf16", "long fresh prompt", ulps=ULPS,
+                extra=p_rounding(q, b, starts))
 
 
 def test_chunked_prefill_at_serving_size():
