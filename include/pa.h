@@ -197,7 +197,10 @@ pa_status pa_decode_attention(void* out, const void* query, const void* k_pool, 
  *   context_lens   DEVICE int32 [num_seqs]
  *   query_start    DEVICE int32 [num_seqs + 1], non-decreasing, from 0 to
  *                  num_tokens (packed new tokens of every sequence)
- *   max_query_len  HOST upper bound of the per-sequence n (sizes the grid)
+ *   max_query_len  HOST upper bound of the per-sequence n (sizes the grid;
+ *                  up to 2048 it also selects workgroups of 256 query rows,
+ *                  above it of 128 -- a tuning choice, the results are equal
+ *                  up to rounding order)
  * dtype must be PA_F16 or PA_BF16 (PA_ERR_DTYPE otherwise).  Rows of a
  * sequence with n > L, or past max_query_len, are not written; ranges outside
  * [0, num_tokens) are skipped.  No workspace.
