@@ -62,6 +62,10 @@ def parse_args():
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB (5 times), the "
                          "reference kernel for scaling HBM byte counters, and exit")
+    ap.add_argument("--ingest-counters", metavar="DIR", default=None,
+                    help="only read rocprofv3 --pmc csv output under DIR/{fetch,write,calf,calw} (FETCH_SIZE and "
+                         "WRITE_SIZE passes of the default decode bench and of --calibrate-copy-mib 1024), write "
+                         "the decode call's HBM bytes to the profiles counters file, and exit (no GPU)")
     return ap.parse_args()
 
 
@@ -74,6 +78,61 @@ def calibrate_copy(mib):
         y.copy_(x)
     torch.cuda.synchronize()
     print(json.dumps({"calibration_copy_bytes": n, "launches": 5}), flush=True)
+
+
+def _pmc_per_dispatch(root, counter):
+    """Mean of `counter` per dispatch, by kernel name, over every
+    *counter_collection.csv under `root` (one row per dispatch and counter)."""
+    import csv
+    import glob
+    sums, counts = {}, {}
+    files = glob.glob(os.path.join(root, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {root}")
+    for fn in files:
+        with open(fn, newline="") as f:
+            for row in csv.DictReader(f):
+                if row.get("Counter_Name") != counter:
+                    continue
+                k = row["Kernel_Name"]
+                sums[k] = sums.get(k, 0.0) + float(row["Counter_Value"])
+                counts[k] = counts.get(k, 0) + 1
+    return {k: sums[k] / counts[k] for k in sums}
+
+
+def ingest_counters(root, config=3, partition=-1):
+    """Turn FETCH_SIZE / WRITE_SIZE passes (KiB per dispatch) into bytes per
+    decode call, each scaled by what the same counter reads for a plain copy of
+    known size, and store them keyed by the kernel sources' hash."""
+    calib = 1 << 30
+    fetch, write = _pmc_per_dispatch(os.path.join(root, "fetch"), "FETCH_SIZE"), \
+        _pmc_per_dispatch(os.path.join(root, "write"), "WRITE_SIZE")
+    calf, calw = _pmc_per_dispatch(os.path.join(root, "calf"), "FETCH_SIZE"), \
+        _pmc_per_dispatch(os.path.join(root, "calw"), "WRITE_SIZE")
+    copy_k = max(calf, key=calf.get)
+    ff = (calib / 1024) / calf[copy_k]
+    wf = (calib / 1024) / calw[copy_k]
+
+    def pick(d, tag):
+        ks = [k for k in d if tag in k]
+        if len(ks) != 1:
+            raise SystemExit(f"expected one kernel named like {tag!r}, found {ks}")
+        return ks[0]
+    dk, mk = pick(fetch, "decode_balanced_kernel"), pick(fetch, "decode_merge_balanced_kernel")
+    dec_b = fetch[dk] * 1024 * ff + write[dk] * 1024 * wf
+    mrg_f, mrg_w = fetch[mk] * 1024 * ff, write[mk] * 1024 * wf
+    out = {"config": config, "partition": partition, "source_sha": source_sha(), "kernel": dk,
+           "fetch_kib_per_dispatch": fetch[dk], "write_kib_per_dispatch": write[dk],
+           "calibration": {"copy_bytes": calib, "copy_kernel": copy_k, "fetch_kib": calf[copy_k],
+                           "write_kib": calw[copy_k], "fetch_factor": ff, "write_factor": wf},
+           "merge_kernel": {"name": mk, "fetch_kib_per_dispatch": fetch[mk], "write_kib_per_dispatch": write[mk],
+                            "fetch_bytes": mrg_f, "write_bytes": mrg_w},
+           "decode_kernel_bytes": dec_b, "hbm_bytes_per_launch": dec_b + mrg_f + mrg_w,
+           "note": "hbm_bytes_per_launch covers one pa_decode_attention call: the decode kernel and its merge"}
+    with open(COUNTERS_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out, indent=1))
 
 
 LARGE_PAGE_BLOCKS = 16   # two-level layout: 256-token large pages at bs 16
@@ -435,6 +494,9 @@ def main():
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}): "
               "the decode path here is a single-GPU kernel; sharding across GPUs is not implemented", file=sys.stderr)
         sys.exit(2)
+    if args.ingest_counters:
+        ingest_counters(args.ingest_counters)
+        return
     if args.calibrate_copy_mib:
         calibrate_copy(args.calibrate_copy_mib)
         return
