@@ -36,6 +36,28 @@ __device__ __forceinline__ u32x4 buf_ld16(rsrc_t r, uint32_t voff) {
 __device__ __forceinline__ u32x4 ld16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
+
+// Loads of data a kernel reads once (the K/V stream of a decode call, a
+// bandwidth sweep) carry the non-temporal hint (`nt`).  Measured on MI355X
+// over 4 GiB: 6.8-7.0 TB/s with it against 6.0-6.2 TB/s without, for
+// contiguous ranges and for randomly placed 4 KiB blocks alike.
+// Data that other waves of the same call read too keeps the default policy,
+// so that they hit in L2 and the MALL.
+#ifndef PA_STREAM_AUX
+#define PA_STREAM_AUX 2
+#endif
+constexpr int kAuxDefault = 0;
+constexpr int kStreamAux = PA_STREAM_AUX;   // buffer-load cache-policy bits (2 = nt)
+template <int AUX>
+__device__ __forceinline__ u32x4 buf_ld16_aux(rsrc_t r, uint32_t voff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, AUX);
+}
+template <int AUX>
+__device__ __forceinline__ u32x4 ld16_aux(const void* p) {
+  if constexpr (AUX == 2) return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return ld16(p);
+}
+__device__ __forceinline__ u32x4 ld16_stream(const void* p) { return ld16_aux<kStreamAux>(p); }
 __device__ __forceinline__ void st16(void* p, u32x4 v) {
   *reinterpret_cast<u32x4*>(p) = v;
 }
@@ -289,6 +311,15 @@ struct TableView {
   __device__ __forceinline__ int entry(int j) const {
     if (j < nl_blocks) return (large[j >> shift] << shift) + (j & ((1 << shift) - 1));
     return small[j - nl_blocks];
+  }
+  // The same value from one load of whichever level holds entry j, with no
+  // branch around it, so that the loads of several entries can all be in
+  // flight at once.
+  __device__ __forceinline__ int entry_sel(int j) const {
+    const bool in_large = j < nl_blocks;
+    const int32_t* base = in_large ? large : small;
+    const int x = base[in_large ? (j >> shift) : (j - nl_blocks)];
+    return in_large ? (x << shift) + (j & ((1 << shift) - 1)) : x;
   }
 };
 

@@ -140,12 +140,12 @@ __global__ __launch_bounds__(kStreamThreads) void stream_read_kernel(const u32x4
   for (; i + (kStreamUnroll - 1) * kStreamThreads < hi; i += kStreamUnroll * kStreamThreads) {
     u32x4 v[kStreamUnroll];
 #pragma unroll
-    for (int u = 0; u < kStreamUnroll; ++u) v[u] = p[i + u * kStreamThreads];
+    for (int u = 0; u < kStreamUnroll; ++u) v[u] = ld16_stream(p + i + u * kStreamThreads);
 #pragma unroll
     for (int u = 0; u < kStreamUnroll; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
   }
   for (; i < hi; i += kStreamThreads) {
-    const u32x4 v = p[i];
+    const u32x4 v = ld16_stream(p + i);
     acc ^= v.x ^ v.y ^ v.z ^ v.w;
   }
   for (int m = 32; m >= 1; m >>= 1) acc ^= (uint32_t)__shfl_xor((int)acc, m, kWave);

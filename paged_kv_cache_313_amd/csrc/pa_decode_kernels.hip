@@ -46,18 +46,64 @@ constexpr float kLazy = 8.f;
 #endif
 constexpr int kRing = PA_TILE_RING;
 
-// Stage table entries [first, first+count) of one sequence into this wave's
-// LDS window (ids clamped into the pool: memory-safe on bad tables).  LDS
+// Cache policy of the K/V loads.  A tile read once per call is loaded with
+// the non-temporal hint.  Blocks that the neighbouring sequences s-1 or s+1
+// map at the same logical position (the prompt blocks that the samples or
+// beams of one request share; a scheduler keeps those sequences together, so
+// their waves run at about the same time) are loaded with the default policy,
+// so that the neighbours hit in L2 or the MALL.  Shared blocks form a prefix
+// of each table, and the tile loop is run twice -- over the window's leading
+// shared blocks, then over the rest -- so that no branch sits between a
+// tile's loads and their use.  The policy does not change any result.
+
+// Stage table entries [first, first+count) of sequence s (1 <= count <=
+// kTblWin) into this wave's LDS window (ids clamped into the pool:
+// memory-safe on bad tables) and return how many leading entries are shared
+// with a neighbour, whose entries count only below its own block count.  All
+// loads are issued before any is used: every index is clamped into its row
+// (a row has at least one entry), so none needs a guard.  LDS
 // operations of one wave complete in order; the wait makes the entries
 // visible to every lane before the wave reads them.
-__device__ __forceinline__ void stage_table_wave(int32_t* tbl, const TableView& row, int first, int count,
-                                                 int num_blocks, int lane) {
-  for (int i = lane; i < count; i += kWave) {
-    const int e = row.entry(first + i);
-    tbl[i] = ((unsigned)e < (unsigned)num_blocks) ? e : 0;
+template <int BS>
+__device__ __forceinline__ int stage_table_wave(int32_t* tbl, const DecodeArgs& a, const TableView& row, int s,
+                                                int first, int count, int lane) {
+  constexpr int NI = kTblWin / kWave;
+  const bool has_prev = s > 0, has_next = s + 1 < a.num_seqs;
+  const int sp = has_prev ? s - 1 : s, sn = has_next ? s + 1 : s;
+  const int lp = a.context_lens[sp], ln = a.context_lens[sn];   // issued with the entries below
+  const TableView rprev = table_view(a, sp);
+  const TableView rnext = table_view(a, sn);
+  int e[NI], ep[NI], en[NI];
+#pragma unroll
+  for (int k = 0; k < NI; ++k) {
+    const int j = first + min(lane + k * kWave, count - 1);
+    e[k] = row.entry_sel(j);
+    ep[k] = rprev.entry_sel(min(j, rprev.capacity - 1));
+    en[k] = rnext.entry_sel(min(j, rnext.capacity - 1));
+  }
+  // the neighbours' lengths clamped as clamp_len does, in blocks
+  auto nblk = [&](int L, const TableView& v) {
+    L = min(max(L, 0), min(v.capacity * BS, a.max_context_len));
+    return (L + BS - 1) / BS;
+  };
+  const int nprev = has_prev ? nblk(lp, rprev) : 0;
+  const int nnext = has_next ? nblk(ln, rnext) : 0;
+  int lead = count;   // first entry not shared (wave-uniform: from ballots)
+#pragma unroll
+  for (int k = 0; k < NI; ++k) {
+    const int i = lane + k * kWave;
+    bool unshared = false;
+    if (i < count) {
+      const int j = first + i;
+      unshared = !((j < nprev && ep[k] == e[k]) || (j < nnext && en[k] == e[k]));
+      tbl[i] = ((unsigned)e[k] < (unsigned)a.num_blocks) ? e[k] : 0;
+    }
+    const uint64_t m = __ballot(unshared);
+    if (lead == count && m != 0) lead = min(count, k * kWave + (int)__builtin_ctzll(m));
   }
   __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
   __builtin_amdgcn_wave_barrier();
+  return lead;
 }
 
 // The table window a wave last staged: consecutive segments of a wave are
@@ -65,21 +111,36 @@ __device__ __forceinline__ void stage_table_wave(int32_t* tbl, const TableView& 
 // so a window that still covers the next one is reused (one dependent global
 // round trip less per segment start).
 struct TblCache {
-  int s = -1, first = 0, count = 0;
+  int s = -1, first = 0, count = 0, shared = 0;
 };
 
 // Entries [fblk, fblk + nent) of sequence s, staged unless the cached window
-// holds them; returns the LDS address of entry fblk.
-__device__ __forceinline__ int32_t* staged_window(int32_t* tbl, TblCache& tc, const TableView& row, int s,
-                                                  int fblk, int nent, int num_blocks, int lane) {
+// holds them; returns the LDS address of entry fblk and sets `nshared` to the
+// number of leading entries from fblk that are shared with a neighbour.
+template <int BS>
+__device__ __forceinline__ int32_t* staged_window(const DecodeArgs& a, int32_t* tbl, TblCache& tc,
+                                                  const TableView& row, int s, int fblk, int nent, int lane,
+                                                  int& nshared) {
   if (!(tc.s == s && tc.first <= fblk && fblk + nent <= tc.first + tc.count)) {
-    stage_table_wave(tbl, row, fblk, nent, num_blocks, lane);
+    tc.shared = stage_table_wave<BS>(tbl, a, row, s, fblk, nent, lane);
     tc.s = s;
     tc.first = fblk;
     tc.count = nent;
   }
+  nshared = min(max(tc.shared - (fblk - tc.first), 0), nent);
   return tbl + (fblk - tc.first);
 }
+
+// Tiles of a window (starting off0 tokens into its first block) that lie
+// wholly in its first nshared blocks.
+template <int BS>
+__device__ __forceinline__ int shared_tiles(int nshared, int off0, int ntiles) {
+  const int t = (nshared * BS - off0) / kTile;
+  return t < 0 ? 0 : (t > ntiles ? ntiles : t);
+}
+
+using PolicyDefault = std::integral_constant<int, kAuxDefault>;
+using PolicyStream = std::integral_constant<int, kStreamAux>;
 
 // Walk tiles 0 .. ntiles-1 keeping the next NB-1 tiles' K/V loads in flight
 // while the current one is computed.  The loop runs over NB tiles at a time
@@ -108,6 +169,19 @@ __device__ __forceinline__ void tile_loop(int ntiles, Load&& load, Compute&& com
 #pragma unroll
   for (int j = 0; j + 1 < NB; ++j)
     if (ti + j < ntiles) compute(ti + j, buf[j]);
+}
+
+// Tiles [0, nsh) of a window with the default cache policy, then tiles
+// [nsh, ntiles) with the non-temporal one: two loops, so that every load of a
+// loop has a fixed policy and nothing but the loop's own exit separates a
+// prefetch from its use.
+template <class Buf, class Load, class Compute>
+__device__ __forceinline__ void run_window(int ntiles, int nsh, Load& load, Compute& compute) {
+  if (nsh > 0)
+    tile_loop<Buf, kRing>(nsh, [&](int ti, Buf& b) { load(PolicyDefault{}, ti, b); },
+                          [&](int ti, const Buf& b) { compute(ti, b); });
+  tile_loop<Buf, kRing>(ntiles - nsh, [&](int ti, Buf& b) { load(PolicyStream{}, nsh + ti, b); },
+                        [&](int ti, const Buf& b) { compute(nsh + ti, b); });
 }
 
 // Byte offsets, from the start of a KV head's slice of the pool, of the
@@ -245,24 +319,26 @@ struct ValuCore {
       const int off0 = wb - fblk * BS;
       const int we = min((fblk + kTblWin) * BS, tok1);
       const int nent = (we - 1) / BS - fblk + 1;
-      const int32_t* tbl = staged_window(tbl_lds, tc, trow, s, fblk, nent, a.num_blocks, lane);
+      int nshared;
+      const int32_t* tbl = staged_window<BS>(a, tbl_lds, tc, trow, s, fblk, nent, lane, nshared);
 
-      auto load = [&](int ti, ValuBuf<NL>& buf) {
+      auto load = [&](auto pol, int ti, ValuBuf<NL>& buf) {
+        constexpr int AUX = decltype(pol)::value;
         size_t lo, hi;
         tile_offsets<BS, ROWB>(tbl, off0 + ti * kTile, nent, blk_stride, lo, hi);
         if constexpr (BS >= 16) {  // one block region: SGPR base + lane offset
           const rsrc_t rk = make_rsrc(kbase + lo, kTileBytes);
           const rsrc_t rv = make_rsrc(vbase + lo, kTileBytes);
 #pragma unroll
-          for (int j = 0; j < NL; ++j) buf.k[j] = buf_ld16(rk, lane_off + j * 64);
+          for (int j = 0; j < NL; ++j) buf.k[j] = buf_ld16_aux<AUX>(rk, lane_off + j * 64);
 #pragma unroll
-          for (int j = 0; j < NL; ++j) buf.v[j] = buf_ld16(rv, lane_off + j * 64);
+          for (int j = 0; j < NL; ++j) buf.v[j] = buf_ld16_aux<AUX>(rv, lane_off + j * 64);
         } else {  // block_size 8: tokens 8..15 come from the next block
           const size_t off = (hi_blk ? hi : lo) + lane_off;
 #pragma unroll
-          for (int j = 0; j < NL; ++j) buf.k[j] = ld16(kbase + off + j * 64);
+          for (int j = 0; j < NL; ++j) buf.k[j] = ld16_aux<AUX>(kbase + off + j * 64);
 #pragma unroll
-          for (int j = 0; j < NL; ++j) buf.v[j] = ld16(vbase + off + j * 64);
+          for (int j = 0; j < NL; ++j) buf.v[j] = ld16_aux<AUX>(vbase + off + j * 64);
         }
       };
       auto compute = [&](int ti, const ValuBuf<NL>& buf) {
@@ -297,7 +373,8 @@ struct ValuCore {
           for (int hh = 0; hh < H; ++hh) Axpy16<T>::run(pr[hh], vj, &acc[hh][j * NE]);
         }
       };
-      tile_loop<ValuBuf<NL>, kRing>((we - wb + kTile - 1) / kTile, load, compute);
+      run_window<ValuBuf<NL>>((we - wb + kTile - 1) / kTile, shared_tiles<BS>(nshared, off0, (we - wb + kTile - 1) / kTile),
+                              load, compute);
       wb = we;
     }
 
@@ -371,6 +448,9 @@ struct MfmaBuf {
   u32x4 k[NQK], v[NVI];
 };
 
+#ifndef PA_MFMA_WG_PER_CU
+#define PA_MFMA_WG_PER_CU 1
+#endif
 template <class T, int D, int BS, int G>
 struct MfmaCore {
   static constexpr int ROWB = D * 2;
@@ -382,7 +462,7 @@ struct MfmaCore {
   // prefetched per wave, more resident waves only add concurrent streams: on
   // the Llama-3-8B-shaped batch 1 workgroup per CU streamed 1-2 % faster than
   // 2 or 3, and equal on the long-context batch.
-  static constexpr int kBalancedWgPerCu = 1;
+  static constexpr int kBalancedWgPerCu = PA_MFMA_WG_PER_CU;
   static_assert(16 % G == 0 && G >= 2, "group");
   static_assert(kTblWin * BS % kTile == 0, "window");
   static constexpr uint32_t kTileBytes = (BS >= 16 ? kTile : BS) * ROWB;
@@ -426,25 +506,27 @@ struct MfmaCore {
       const int off0 = wb - fblk * BS;
       const int we = min((fblk + kTblWin) * BS, tok1);
       const int nent = (we - 1) / BS - fblk + 1;
-      const int32_t* tbl = staged_window(tbl_lds, tc, trow, s, fblk, nent, a.num_blocks, lane);
+      int nshared;
+      const int32_t* tbl = staged_window<BS>(a, tbl_lds, tc, trow, s, fblk, nent, lane, nshared);
 
-      auto load = [&](int ti, MfmaBuf<NQK, NVI>& buf) {
+      auto load = [&](auto pol, int ti, MfmaBuf<NQK, NVI>& buf) {
+        constexpr int AUX = decltype(pol)::value;
         size_t lo, hi;
         tile_offsets<BS, ROWB>(tbl, off0 + ti * kTile, nent, blk_stride, lo, hi);
         if constexpr (BS >= 16) {  // one block region: SGPR base + lane offset
           const rsrc_t rk = make_rsrc(kbase + lo, kTileBytes);
           const rsrc_t rv = make_rsrc(vbase + lo, kTileBytes);
 #pragma unroll
-          for (int i = 0; i < NQK; ++i) buf.k[i] = buf_ld16(rk, k_off + i * 64);
+          for (int i = 0; i < NQK; ++i) buf.k[i] = buf_ld16_aux<AUX>(rk, k_off + i * 64);
 #pragma unroll
-          for (int j = 0; j < NVI; ++j) buf.v[j] = buf_ld16(rv, v_off + (16 * j / CPR) * ROWB);
+          for (int j = 0; j < NVI; ++j) buf.v[j] = buf_ld16_aux<AUX>(rv, v_off + (16 * j / CPR) * ROWB);
         } else {  // block_size 8: tokens 8..15 come from the next block
           const char* kb = kbase + (k_hi ? hi : lo) + k_off;
           const char* vb = vbase + (v_hi ? hi : lo) + v_off;
 #pragma unroll
-          for (int i = 0; i < NQK; ++i) buf.k[i] = ld16(kb + i * 64);
+          for (int i = 0; i < NQK; ++i) buf.k[i] = ld16_aux<AUX>(kb + i * 64);
 #pragma unroll
-          for (int j = 0; j < NVI; ++j) buf.v[j] = ld16(vb + (16 * j / CPR) * ROWB);
+          for (int j = 0; j < NVI; ++j) buf.v[j] = ld16_aux<AUX>(vb + (16 * j / CPR) * ROWB);
         }
       };
       auto compute = [&](int ti, const MfmaBuf<NQK, NVI>& buf) {
@@ -500,7 +582,8 @@ struct MfmaCore {
           }
         }
       };
-      tile_loop<MfmaBuf<NQK, NVI>, kRing>((we - wb + kTile - 1) / kTile, load, compute);
+      run_window<MfmaBuf<NQK, NVI>>((we - wb + kTile - 1) / kTile,
+                                    shared_tiles<BS>(nshared, off0, (we - wb + kTile - 1) / kTile), load, compute);
       wb = we;
     }
 
