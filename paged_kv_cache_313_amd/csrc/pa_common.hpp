@@ -36,6 +36,9 @@ __device__ __forceinline__ u32x4 buf_ld16(rsrc_t r, uint32_t voff) {
 __device__ __forceinline__ u32x4 ld16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
+__device__ __forceinline__ void st16(void* p, u32x4 v) {
+  *reinterpret_cast<u32x4*>(p) = v;
+}
 
 // Loads of data a kernel reads once (the K/V stream of a decode call, a
 // bandwidth sweep) carry the non-temporal hint (`nt`).  Measured on MI355X
@@ -58,8 +61,10 @@ __device__ __forceinline__ u32x4 ld16_aux(const void* p) {
   return ld16(p);
 }
 __device__ __forceinline__ u32x4 ld16_stream(const void* p) { return ld16_aux<kStreamAux>(p); }
-__device__ __forceinline__ void st16(void* p, u32x4 v) {
-  *reinterpret_cast<u32x4*>(p) = v;
+template <int AUX>
+__device__ __forceinline__ void st16_aux(void* p, u32x4 v) {
+  if constexpr (AUX == 2) __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+  else st16(p, v);
 }
 
 // ---- unpack 16 loaded bytes to fp32 (exact) --------------------------------

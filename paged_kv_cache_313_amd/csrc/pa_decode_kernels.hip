@@ -54,7 +54,11 @@ constexpr int kRing = PA_TILE_RING;
 // so that the neighbours hit in L2 or the MALL.  Shared blocks form a prefix
 // of each table, and the tile loop is run twice -- over the window's leading
 // shared blocks, then over the rest -- so that no branch sits between a
-// tile's loads and their use.  The policy does not change any result.
+// tile's loads and their use.  This holds for the balanced grid (one
+// workgroup per CU, long ranges per wave).  Unit-mode grids (many resident
+// waves, one short segment each) load every tile with the default policy:
+// there the hint made a 64-sequence MHA batch 32 % slower.  The policy does
+// not change any result.
 
 // Stage table entries [first, first+count) of sequence s (1 <= count <=
 // kTblWin) into this wave's LDS window (ids clamped into the pool:
@@ -67,6 +71,15 @@ constexpr int kRing = PA_TILE_RING;
 template <int BS>
 __device__ __forceinline__ int stage_table_wave(int32_t* tbl, const DecodeArgs& a, const TableView& row, int s,
                                                 int first, int count, int lane) {
+  if (a.mode != kModeBalanced) {   // unit mode: every tile under the default policy
+    for (int i = lane; i < count; i += kWave) {
+      const int e = row.entry(first + i);
+      tbl[i] = ((unsigned)e < (unsigned)a.num_blocks) ? e : 0;
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+    __builtin_amdgcn_wave_barrier();
+    return count;
+  }
   constexpr int NI = kTblWin / kWave;
   const bool has_prev = s > 0, has_next = s + 1 < a.num_seqs;
   const int sp = has_prev ? s - 1 : s, sn = has_next ? s + 1 : s;
