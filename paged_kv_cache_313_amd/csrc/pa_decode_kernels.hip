@@ -112,7 +112,7 @@ __device__ __forceinline__ int stage_table_wave(int32_t* tbl, const DecodeArgs& 
       tbl[i] = ((unsigned)e[k] < (unsigned)a.num_blocks) ? e[k] : 0;
     }
     const uint64_t m = __ballot(unshared);
-    if (lead == count && m != 0) lead = min(count, k * kWave + (int)__builtin_ctzll(m));
+    if (lead == count && m != 0) lead = k * kWave + (int)__builtin_ctzll(m);
   }
   __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
   __builtin_amdgcn_wave_barrier();
@@ -144,10 +144,12 @@ __device__ __forceinline__ int32_t* staged_window(const DecodeArgs& a, int32_t* 
   return tbl + (fblk - tc.first);
 }
 
-// Tiles of a window (starting off0 tokens into its first block) that lie
-// wholly in its first nshared blocks.
+// Tiles of a window of nent blocks (starting off0 tokens into its first
+// block) that lie wholly in its first nshared blocks: all of them when every
+// block is shared.
 template <int BS>
-__device__ __forceinline__ int shared_tiles(int nshared, int off0, int ntiles) {
+__device__ __forceinline__ int shared_tiles(int nshared, int nent, int off0, int ntiles) {
+  if (nshared >= nent) return ntiles;
   const int t = (nshared * BS - off0) / kTile;
   return t < 0 ? 0 : (t > ntiles ? ntiles : t);
 }
@@ -386,8 +388,8 @@ struct ValuCore {
           for (int hh = 0; hh < H; ++hh) Axpy16<T>::run(pr[hh], vj, &acc[hh][j * NE]);
         }
       };
-      run_window<ValuBuf<NL>>((we - wb + kTile - 1) / kTile, shared_tiles<BS>(nshared, off0, (we - wb + kTile - 1) / kTile),
-                              load, compute);
+      const int ntiles = (we - wb + kTile - 1) / kTile;
+      run_window<ValuBuf<NL>>(ntiles, shared_tiles<BS>(nshared, nent, off0, ntiles), load, compute);
       wb = we;
     }
 
@@ -595,8 +597,8 @@ struct MfmaCore {
           }
         }
       };
-      run_window<MfmaBuf<NQK, NVI>>((we - wb + kTile - 1) / kTile,
-                                    shared_tiles<BS>(nshared, off0, (we - wb + kTile - 1) / kTile), load, compute);
+      const int ntiles = (we - wb + kTile - 1) / kTile;
+      run_window<MfmaBuf<NQK, NVI>>(ntiles, shared_tiles<BS>(nshared, nent, off0, ntiles), load, compute);
       wb = we;
     }
 
