@@ -142,7 +142,9 @@ int32_t pa_decode_choose_partition(int32_t num_seqs, int32_t num_kv_heads, int32
  *   query          DEVICE [num_seqs][num_q_heads][head_dim] of dtype
  *   k_pool, v_pool DEVICE pools (see above), read only
  *   block_tables   DEVICE int32 [num_seqs][max_blocks_per_seq]; entries past a
- *                  sequence's last block are never read
+ *                  sequence's last block never affect the result (the
+ *                  balanced split may read any entry of the array when it
+ *                  compares a row with its neighbours', see below)
  *   context_lens   DEVICE int32 [num_seqs]; counts every token attended to,
  *                  including one appended in the same step (append first)
  *   max_context_len HOST upper bound of context_lens (sizes the grid);
@@ -164,6 +166,14 @@ int32_t pa_decode_choose_partition(int32_t num_seqs, int32_t num_kv_heads, int32
  *                  bytes when that is non-zero (may be NULL otherwise);
  *                  scratch only, overwritten.  Calls that share a workspace
  *                  must be ordered on one stream.
+ *
+ * Cache policy (performance only, never the result): the balanced split
+ * loads K/V tiles with the non-temporal hint, except the leading blocks of a
+ * table that sequence s-1 or s+1 maps to the same physical blocks at the same
+ * logical positions (a shared prompt).  Those keep the default policy, so
+ * that neighbouring sequences hit in the caches.  Place the sequences that
+ * share blocks (the samples or beams of one request) next to each other in
+ * the batch.  The other modes use the default policy throughout.
  */
 pa_status pa_decode_attention(void* out, const void* query, const void* k_pool, const void* v_pool,
                               const int32_t* block_tables, const int32_t* context_lens,
