@@ -100,7 +100,7 @@ def _pmc_per_dispatch(root, counter):
     return {k: sums[k] / counts[k] for k in sums}
 
 
-def ingest_counters(root, config=3, partition=-1):
+def ingest_counters(root, config=3, partition=-1, out_path=None):
     """Turn FETCH_SIZE / WRITE_SIZE passes (KiB per dispatch) into bytes per
     decode call, each scaled by what the same counter reads for a plain copy of
     known size, and store them keyed by the kernel sources' hash."""
@@ -129,10 +129,11 @@ def ingest_counters(root, config=3, partition=-1):
                             "fetch_bytes": mrg_f, "write_bytes": mrg_w},
            "decode_kernel_bytes": dec_b, "hbm_bytes_per_launch": dec_b + mrg_f + mrg_w,
            "note": "hbm_bytes_per_launch covers one pa_decode_attention call: the decode kernel and its merge"}
-    with open(COUNTERS_FILE, "w") as f:
+    with open(out_path or COUNTERS_FILE, "w") as f:
         json.dump(out, f, indent=1)
         f.write("\n")
     print(json.dumps(out, indent=1))
+    return out
 
 
 LARGE_PAGE_BLOCKS = 16   # two-level layout: 256-token large pages at bs 16
