@@ -68,10 +68,10 @@ constexpr int kRing = PA_TILE_RING;
 // (a row has at least one entry), so none needs a guard.  LDS
 // operations of one wave complete in order; the wait makes the entries
 // visible to every lane before the wave reads them.
-template <int BS>
+template <int BS, bool SPLIT>
 __device__ __forceinline__ int stage_table_wave(int32_t* tbl, const DecodeArgs& a, const TableView& row, int s,
                                                 int first, int count, int lane) {
-  if (a.mode != kModeBalanced) {   // unit mode: every tile under the default policy
+  if constexpr (!SPLIT) {   // unit mode: every tile under the default policy
     for (int i = lane; i < count; i += kWave) {
       const int e = row.entry(first + i);
       tbl[i] = ((unsigned)e < (unsigned)a.num_blocks) ? e : 0;
@@ -130,12 +130,12 @@ struct TblCache {
 // Entries [fblk, fblk + nent) of sequence s, staged unless the cached window
 // holds them; returns the LDS address of entry fblk and sets `nshared` to the
 // number of leading entries from fblk that are shared with a neighbour.
-template <int BS>
+template <int BS, bool SPLIT>
 __device__ __forceinline__ int32_t* staged_window(const DecodeArgs& a, int32_t* tbl, TblCache& tc,
                                                   const TableView& row, int s, int fblk, int nent, int lane,
                                                   int& nshared) {
   if (!(tc.s == s && tc.first <= fblk && fblk + nent <= tc.first + tc.count)) {
-    tc.shared = stage_table_wave<BS>(tbl, a, row, s, fblk, nent, lane);
+    tc.shared = stage_table_wave<BS, SPLIT>(tbl, a, row, s, fblk, nent, lane);
     tc.s = s;
     tc.first = fblk;
     tc.count = nent;
@@ -189,9 +189,14 @@ __device__ __forceinline__ void tile_loop(int ntiles, Load&& load, Compute&& com
 // Tiles [0, nsh) of a window with the default cache policy, then tiles
 // [nsh, ntiles) with the non-temporal one: two loops, so that every load of a
 // loop has a fixed policy and nothing but the loop's own exit separates a
-// prefetch from its use.
-template <class Buf, class Load, class Compute>
+// prefetch from its use.  SPLIT is false for unit-mode kernels: one loop, all
+// tiles under the default policy.
+template <class Buf, bool SPLIT, class Load, class Compute>
 __device__ __forceinline__ void run_window(int ntiles, int nsh, Load& load, Compute& compute) {
+  if constexpr (!SPLIT) {   // unit mode: one loop, default policy
+    tile_loop<Buf, kRing>(ntiles, [&](int ti, Buf& b) { load(PolicyDefault{}, ti, b); }, compute);
+    return;
+  }
   if (nsh > 0)
     tile_loop<Buf, kRing>(nsh, [&](int ti, Buf& b) { load(PolicyDefault{}, ti, b); },
                           [&](int ti, const Buf& b) { compute(ti, b); });
@@ -295,6 +300,7 @@ struct ValuCore {
 
   // q heads h0 .. h0+H-1 of sequence s over tokens [tok0, tok1), run by one
   // wave; tbl is the wave's LDS window.
+  template <bool SPLIT>
   __device__ static void run(const DecodeArgs& a, int32_t* tbl_lds, TblCache& tc, int s, int h0, int tok0,
                              int tok1, const Dest& dst) {
     const int lane = threadIdx.x & (kWave - 1);
@@ -335,7 +341,7 @@ struct ValuCore {
       const int we = min((fblk + kTblWin) * BS, tok1);
       const int nent = (we - 1) / BS - fblk + 1;
       int nshared;
-      const int32_t* tbl = staged_window<BS>(a, tbl_lds, tc, trow, s, fblk, nent, lane, nshared);
+      const int32_t* tbl = staged_window<BS, SPLIT>(a, tbl_lds, tc, trow, s, fblk, nent, lane, nshared);
 
       auto load = [&](auto pol, int ti, ValuBuf<NL>& buf) {
         constexpr int AUX = decltype(pol)::value;
@@ -389,7 +395,7 @@ struct ValuCore {
         }
       };
       const int ntiles = (we - wb + kTile - 1) / kTile;
-      run_window<ValuBuf<NL>>(ntiles, shared_tiles<BS>(nshared, nent, off0, ntiles), load, compute);
+      run_window<ValuBuf<NL>, SPLIT>(ntiles, shared_tiles<BS>(nshared, nent, off0, ntiles), load, compute);
       wb = we;
     }
 
@@ -484,6 +490,7 @@ struct MfmaCore {
 
   // the G q heads h0 .. h0+G-1 (KV head h0 / G) of sequence s over tokens
   // [tok0, tok1), run by one wave; tbl is the wave's LDS window.
+  template <bool SPLIT>
   __device__ static void run(const DecodeArgs& a, int32_t* tbl_lds, TblCache& tc, int s, int h0, int tok0,
                              int tok1, const Dest& dst) {
     const int lane = threadIdx.x & (kWave - 1);
@@ -522,7 +529,7 @@ struct MfmaCore {
       const int we = min((fblk + kTblWin) * BS, tok1);
       const int nent = (we - 1) / BS - fblk + 1;
       int nshared;
-      const int32_t* tbl = staged_window<BS>(a, tbl_lds, tc, trow, s, fblk, nent, lane, nshared);
+      const int32_t* tbl = staged_window<BS, SPLIT>(a, tbl_lds, tc, trow, s, fblk, nent, lane, nshared);
 
       auto load = [&](auto pol, int ti, MfmaBuf<NQK, NVI>& buf) {
         constexpr int AUX = decltype(pol)::value;
@@ -598,7 +605,7 @@ struct MfmaCore {
         }
       };
       const int ntiles = (we - wb + kTile - 1) / kTile;
-      run_window<MfmaBuf<NQK, NVI>>(ntiles, shared_tiles<BS>(nshared, nent, off0, ntiles), load, compute);
+      run_window<MfmaBuf<NQK, NVI>, SPLIT>(ntiles, shared_tiles<BS>(nshared, nent, off0, ntiles), load, compute);
       wb = we;
     }
 
@@ -666,7 +673,7 @@ __global__ __launch_bounds__(NW * kWave) void decode_unit_kernel(DecodeArgs a, i
   const Dest dst{!a.split || L <= P, ((size_t)s * a.num_q_heads + h0) * a.num_parts + p,
                  (size_t)a.num_parts};
   TblCache tc;
-  Core::run(a, s_tbl[wave], tc, s, h0, t0, t1, dst);
+  Core::template run<false>(a, s_tbl[wave], tc, s, h0, t0, t1, dst);
 }
 
 // ============================================================================
@@ -778,7 +785,7 @@ __global__ __launch_bounds__(NW * kWave) void decode_balanced_kernel(DecodeArgs 
       const int tok0 = t0 * kTile, tok1 = min(t1 * kTile, L);
       const size_t slot = 2 * (size_t)w + (first ? 0 : 1);
       const Dest dst{t0 == 0 && t1 == nt, slot * H, 1};
-      Core::run(a, s_tbl[wave], tc, s, c * H, tok0, tok1, dst);
+      Core::template run<true>(a, s_tbl[wave], tc, s, c * H, tok0, tok1, dst);
       first = false;
     }
     f += n;
