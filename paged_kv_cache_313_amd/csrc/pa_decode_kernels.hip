@@ -710,9 +710,12 @@ __device__ __forceinline__ uint32_t xcd_contiguous(uint32_t b, uint32_t n) {
 
 template <int NT>
 __device__ __forceinline__ void tile_prefix(const DecodeArgs& a, int block_size, int32_t* s_cum,
-                                            int32_t* s_part) {
+                                            int32_t* s_wave) {
   // s_cum[s] = sum_{s' < s} cost(s'), cost = X + ceil(L / 16) (0 for an
-  // empty sequence), s = 0..S, by a block-wide scan
+  // empty sequence), s = 0..S: each thread sums a contiguous run of
+  // sequences, then the runs are offset by a shuffle scan within each wave
+  // and the totals of the waves before it
+  static_assert(NT % kWave == 0, "whole waves");
   const int S = a.num_seqs;
   const int per = (S + NT - 1) / NT;
   const int lo = threadIdx.x * per, hi = min(lo + per, S);
@@ -722,20 +725,24 @@ __device__ __forceinline__ void tile_prefix(const DecodeArgs& a, int block_size,
     s_cum[s] = sum;   // local exclusive prefix, offset below
     sum += nt > 0 ? nt + kSegCost : 0;
   }
-  s_part[threadIdx.x] = sum;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int run = 0;
-    for (int i = 0; i < NT; ++i) {
-      const int x = s_part[i];
-      s_part[i] = run;
-      run += x;
-    }
-    s_cum[S] = run;
+  const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
+  int x = sum;   // inclusive scan over the wave's lanes
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int y = __shfl_up(x, o, kWave);
+    if (lane >= o) x += y;
   }
+  if (lane == kWave - 1) s_wave[wv] = x;
   __syncthreads();
-  const int base = s_part[threadIdx.x];
+  int base = x - sum, total = 0;
+#pragma unroll
+  for (int i = 0; i < NT / kWave; ++i) {
+    const int t = s_wave[i];
+    base += i < wv ? t : 0;
+    total += t;
+  }
   for (int s = lo; s < hi; ++s) s_cum[s] += base;
+  if (threadIdx.x == 0) s_cum[S] = total;
   __syncthreads();
 }
 
@@ -743,10 +750,10 @@ template <class Core, class T, int D, int NW>
 __global__ __launch_bounds__(NW * kWave) void decode_balanced_kernel(DecodeArgs a, int block_size) {
   constexpr int H = Core::HEADS;
   __shared__ int32_t s_cum[kBalancedMaxSeqs + 1];
-  __shared__ int32_t s_part[NW * kWave];
+  __shared__ int32_t s_wave[NW];
   __shared__ int32_t s_tbl[NW][kTblWin];
   const int S = a.num_seqs, C = a.head_chunks;
-  tile_prefix<NW * kWave>(a, block_size, s_cum, s_part);
+  tile_prefix<NW * kWave>(a, block_size, s_cum, s_wave);
   if (blockIdx.x == 0)
     for (int s = threadIdx.x; s <= S; s += NW * kWave) a.ws_cum[s] = s_cum[s];
   // sequences with no tile own no range: their rows are zeros, written here
