@@ -54,16 +54,29 @@ def _run(cmd):
     return "\n".join(lines)
 
 
+def extra_defines() -> list:
+    """-D options from the PA_HIPCC_DEFINES environment variable (space
+    separated), for measuring alternatives to the tuned defaults, e.g.
+    PA_HIPCC_DEFINES=-DPA_STREAM_AUX=0 loads K/V with the default cache policy."""
+    defs = os.environ.get("PA_HIPCC_DEFINES", "").split()
+    bad = [d for d in defs if not d.startswith("-D")]
+    if bad:
+        raise ValueError(f"PA_HIPCC_DEFINES takes -D options only, got {bad}")
+    return defs
+
+
 def build(verbose: bool = False, jobs: int = 8) -> str:
     """Compile every source and link libpagedkv.so (always rebuilds)."""
     os.makedirs(BUILD_DIR, exist_ok=True)
     cc = hipcc()
     objs = []
     cmds = []
+    defs = extra_defines()
     for src in SOURCES:
         obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
         objs.append(obj)
-        cmds.append([cc, *COMPILE_FLAGS, *SOURCE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj])
+        cmds.append([cc, *COMPILE_FLAGS, *SOURCE_FLAGS.get(src, []), *defs, "-c", os.path.join(CSRC, src),
+                     "-o", obj])
     with ThreadPoolExecutor(max_workers=max(1, min(jobs, len(cmds)))) as ex:
         logs = list(ex.map(_run, cmds))
     tmp = LIB_PATH + ".tmp"
