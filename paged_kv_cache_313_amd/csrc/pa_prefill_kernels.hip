@@ -82,20 +82,34 @@ __device__ __forceinline__ int vt_swizzle(int row) { return 4 * ((row >> 4) & (k
 __device__ __forceinline__ int vt_pair(int x) {
   return 16 * (x >> 4) + 2 * ((x >> 2) & 3) + (x & 1) + 8 * ((x >> 1) & 1);
 }
+// V staging: 0 stores V transposed (8 dword stores per key pair); 1 keeps V
+// row-major in LDS (two 16-byte stores per key pair, like K) and forms the
+// P.V operand with gfx950's transposing LDS read, two 8-byte reads where the
+// transposed layout needs one 16-byte read.  Both pass the same tests; on the
+// 16 x 512-token chunked prefill the row-major form measured 594-605 us
+// against 589-596 us, so the transposed store stays the default.  The
+// row-major form is the one direct-to-LDS loads could fill.
+#ifndef PA_PREFILL_VTR
+#define PA_PREFILL_VTR 0
+#endif
 template <int D, int NW>
 struct PfLayout {
   static constexpr int kThreads = NW * kWave;
   static constexpr int kRowB = D * 2 + 16;           // K row pitch in LDS (bytes), padded
   static constexpr int kVtB = kPfKeys * 2 + 16;      // V^T row pitch in LDS (bytes), padded, 16-byte aligned
+  // V row pitch: D + 16 elements, so that the 4 rows one transposing read
+  // touches (32 bytes each) start 8 dwords apart in the 64 banks
+  static constexpr int kVrB = D * 2 + 32;
   static constexpr int kKBytes = kPfKeys * kRowB;
-  static constexpr int kBufBytes = kKBytes + D * kVtB;
+  static constexpr int kVBytes = PA_PREFILL_VTR ? kPfKeys * kVrB : D * kVtB;
+  static constexpr int kBufBytes = kKBytes + kVBytes;
   static constexpr int CPR = D / 8;                  // 16-byte chunks per token row
   static constexpr int kPairs = kPfKeys / 2 * CPR;   // (key pair, d-chunk) units per tile
   static constexpr bool kPartial = kPairs < kThreads;   // then threads >= kPairs load nothing
   static constexpr int NPAIR = kPartial ? 1 : kPairs / kThreads;   // key pairs per thread per tile
   static constexpr int NCH = 2 * NPAIR;              // chunks per thread per tile
   static_assert(kPartial || NPAIR * kThreads == kPairs, "tile split");
-  static_assert(kRowB % 16 == 0 && kVtB % 16 == 0 && kBufBytes % 16 == 0, "16-byte LDS rows");
+  static_assert(kRowB % 16 == 0 && kVtB % 16 == 0 && kVrB % 16 == 0 && kBufBytes % 16 == 0, "16-byte LDS rows");
 };
 
 // max over the 4 lanes of a query row (c, c + 16, c + 32, c + 48): the row
@@ -228,6 +242,11 @@ __global__ __launch_bounds__(NW * kWave) void prefill_kernel(PrefillArgs a, int 
         v0 = t0 + key < L ? v0 : z;
         v1 = t0 + key + 1 < L ? v1 : z;
       }
+      if constexpr (PA_PREFILL_VTR != 0) {
+        *reinterpret_cast<u32x4*>(vb + key * Lay::kVrB + dch * 16) = v0;
+        *reinterpret_cast<u32x4*>(vb + (key + 1) * Lay::kVrB + dch * 16) = v1;
+        continue;
+      }
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         // element e of both keys: low halves (even e) or high halves (odd e)
@@ -356,8 +375,25 @@ __global__ __launch_bounds__(NW * kWave) void prefill_kernel(PrefillArgs a, int 
       // 16 (h ^ sw / 16) + 4 (gq ^ (sw / 4) % 4) .. + 3: the row base, a
       // constant and one of four lane offsets
       const char* vlane = vb + c * Lay::kVtB;
+      // Transposing read (row-major V): within each 16-lane group, lane j
+      // receives value j % 4 of the 8-byte chunks addressed by lanes j / 4,
+      // 4 + j / 4, 8 + j / 4 and 12 + j / 4.  Lane (c, gq) addresses chunk
+      // c % 4 (d = 16 dt + 4 (c % 4) ..) of key row 32 h + 4 gq + c / 4, so
+      // lane c receives d = 16 dt + c of keys 32 h + 4 gq .. + 3 (k-slots
+      // 8 gq .. 8 gq + 3); the same 16 rows further gives keys 32 h + 16 + 4 gq
+      // .. + 3 (k-slots 8 gq + 4 ..).
+      typedef short v4i16 __attribute__((ext_vector_type(4)));
+      typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+      const char* vtr = vb + (4 * gq + (c >> 2)) * Lay::kVrB + 8 * (c & 3);
       auto read_v = [&](int step) {
         const int h = step / NDT, dt = step % NDT;
+        if constexpr (PA_PREFILL_VTR != 0) {
+          const char* src = vtr + 32 * h * Lay::kVrB + 32 * dt;
+          const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)src);
+          const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(src + 16 * Lay::kVrB));
+          const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+          return u32x4{l2.x, l2.y, h2.x, h2.y};
+        }
         const int sw = vt_swizzle(16 * dt);
         const char* src = vlane + 16 * dt * Lay::kVtB + 64 * (h ^ (sw >> 4)) + 16 * (gq ^ ((sw >> 2) & 3));
         return *reinterpret_cast<const u32x4*>(src);
@@ -379,13 +415,15 @@ __global__ __launch_bounds__(NW * kWave) void prefill_kernel(PrefillArgs a, int 
         av = nxt;
       }
 #if PA_PREFILL_SCHED > 0
-      // keep each V^T read PA_PREFILL_SCHED products ahead of its use
-      __builtin_amdgcn_sched_group_barrier(0x100, PA_PREFILL_SCHED, 0);
+      // keep each V^T read PA_PREFILL_SCHED products ahead of its use (two
+      // transposing reads per operand with row-major V)
+      constexpr int kVReads = PA_PREFILL_VTR ? 2 : 1;
+      __builtin_amdgcn_sched_group_barrier(0x100, kVReads * PA_PREFILL_SCHED, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, NG * (kPfSub / 2), 0);
 #pragma unroll
       for (int step = 0; step < NVS; ++step) {
         __builtin_amdgcn_sched_group_barrier(0x008, NG, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, kVReads, 0);
       }
 #endif
     }
