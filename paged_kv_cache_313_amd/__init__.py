@@ -43,6 +43,16 @@ def _dev(t: torch.Tensor, name: str) -> int:
     return t.data_ptr()
 
 
+def _check_out(out: torch.Tensor, query: torch.Tensor) -> None:
+    """A caller-supplied output must have the query's shape, dtype and device:
+    the kernels write exactly query.numel() elements of the query's dtype."""
+    if not isinstance(out, torch.Tensor):
+        raise TypeError("out must be a torch.Tensor")
+    if tuple(out.shape) != tuple(query.shape) or out.dtype != query.dtype or out.device != query.device:
+        raise ValueError(f"out must match the query: shape {tuple(query.shape)}, dtype {query.dtype}, device "
+                         f"{query.device} (got {tuple(out.shape)}, {out.dtype}, {out.device})")
+
+
 def _stream(t: torch.Tensor, stream) -> int:
     if stream is None:
         stream = torch.cuda.current_stream(t.device)
@@ -191,6 +201,8 @@ def decode_attention(query: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Te
         partition_size = choose_partition(S, Hkv, max_context_len, bs)
     if out is None:
         out = torch.empty_like(query)
+    else:
+        _check_out(out, query)
     need = decode_workspace_bytes(S, Hq, Hkv, D, max_context_len, partition_size)
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=query.device)
@@ -230,6 +242,8 @@ def prefill_attention(query: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.T
         raise TypeError("query and pools must share a dtype")
     if out is None:
         out = torch.empty_like(query)
+    else:
+        _check_out(out, query)
     st = lib.pa_prefill_attention(_dev(out, "out"), _dev(query, "query"), _dev(k_pool, "k_pool"),
                                   _dev(v_pool, "v_pool"), _dev(block_tables, "block_tables"),
                                   _dev(context_lens, "context_lens"), _dev(query_start, "query_start"), S, T,
@@ -269,6 +283,8 @@ def decode_attention_hier(query, k_pool, v_pool, small_tables, large_tables, num
         partition_size = choose_partition(S, Hkv, max_context_len, bs)
     if out is None:
         out = torch.empty_like(query)
+    else:
+        _check_out(out, query)
     need = decode_workspace_bytes(S, Hq, Hkv, D, max_context_len, partition_size)
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=query.device)
@@ -302,6 +318,8 @@ def prefill_attention_hier(query, k_pool, v_pool, small_tables, large_tables, nu
         raise TypeError("query and pools must share a dtype")
     if out is None:
         out = torch.empty_like(query)
+    else:
+        _check_out(out, query)
     st = lib.pa_prefill_attention_hier(_dev(out, "out"), _dev(query, "query"), _dev(k_pool, "k_pool"),
                                        _dev(v_pool, "v_pool"), _dev(small_tables, "small_tables"),
                                        _dev(large_tables, "large_tables"), _dev(num_large, "num_large"),

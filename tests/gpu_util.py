@@ -22,11 +22,13 @@ def note(msg: str) -> None:
     sys.stdout.flush()
 
 
-def gpu_step(b, d, partition_size=None, decode=True):
-    """The hot path in the order of one decode step: CoW copies, append, attention."""
-    if b.block_mapping is not None and len(b.block_mapping):
+def gpu_step(b, d, partition_size=None, decode=True, copy_append=True):
+    """The hot path in the order of one decode step: CoW copies, append,
+    attention (copy_append=False: attention alone, over pools that a step
+    already updated)."""
+    if copy_append and b.block_mapping is not None and len(b.block_mapping):
         P.block_copy(d.k_pool, d.v_pool, d.block_mapping)
-    if b.new_key is not None:
+    if copy_append and b.new_key is not None:
         P.kv_append(d.new_key, d.new_value, d.k_pool, d.v_pool, d.slot_mapping)
     out = None
     if decode:

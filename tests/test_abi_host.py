@@ -161,6 +161,28 @@ def test_binding_refuses_cpu_tensors(lib):
                            0.125, 1, partition_size=0, out=torch.empty(2, 4, 64))
 
 
+@pytest.mark.parametrize("out_shape,out_dtype", [((2, 4, 32), "float32"), ((1, 4, 64), "float32"),
+                                                 ((2, 4, 64), "bfloat16"), ((2, 4, 64, 1), "float32")])
+def test_binding_refuses_mismatched_out(lib, out_shape, out_dtype):
+    # an output smaller or narrower than the query would be written past its end
+    import torch
+    q = torch.zeros(2, 4, 64)
+    pool = torch.zeros(4, 4, 16, 64)
+    tbl, lens = torch.zeros(2, 1, dtype=torch.int32), torch.ones(2, dtype=torch.int32)
+    bad = torch.empty(out_shape, dtype=getattr(torch, out_dtype))
+    with pytest.raises(ValueError, match="out must match"):
+        P.decode_attention(q, pool, pool, tbl, lens, 0.125, 1, partition_size=0, out=bad)
+    with pytest.raises(ValueError, match="out must match"):
+        P.decode_attention_hier(q, pool, pool, tbl, torch.zeros(2, 1, dtype=torch.int32),
+                                torch.zeros(2, dtype=torch.int32), 1, lens, 0.125, 1, partition_size=0, out=bad)
+    qs = torch.arange(3, dtype=torch.int32)
+    with pytest.raises(ValueError, match="out must match"):
+        P.prefill_attention(q, pool, pool, tbl, lens, qs, 0.125, 1, out=bad)
+    with pytest.raises(ValueError, match="out must match"):
+        P.prefill_attention_hier(q, pool, pool, tbl, torch.zeros(2, 1, dtype=torch.int32),
+                                 torch.zeros(2, dtype=torch.int32), 1, lens, qs, 0.125, 1, out=bad)
+
+
 SWAP_OK = dict(pool_k=A, pool_v=B, ids=A, n=4, host=B, hkv=8, bs=16, d=128, nb=100, dtype=BF16)
 
 
