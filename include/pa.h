@@ -47,7 +47,9 @@
  *   and lengths are clamped or skipped (results for such inputs are
  *   unspecified, but memory stays safe).
  * - All entry points are reentrant; the library holds no state other than the
- *   thread-local last HIP error.
+ *   thread-local last HIP error, the cached launch geometry and the device
+ *   scratch of pa_decode_attention_noalloc (whose calls on one GPU must not
+ *   overlap).
  */
 #ifndef PAGEDKV_PA_H
 #define PAGEDKV_PA_H
@@ -182,6 +184,37 @@ pa_status pa_decode_attention(void* out, const void* query, const void* k_pool, 
                               int32_t num_blocks, int32_t max_context_len, float scale,
                               int32_t partition_size, pa_dtype dtype, void* workspace,
                               size_t workspace_bytes, void* stream);
+
+/*
+ * pa_decode_attention_noalloc -- pa_decode_attention without a workspace
+ * argument, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ *
+ * Same operation, arguments, kernels, results and errors as
+ * pa_decode_attention, except that the partial results of a split go to a
+ * static device scratch buffer of PA_DECODE_SCRATCH_BYTES that the library
+ * holds on every GPU it runs on, until the process ends.  The call allocates
+ * nothing.  Its first call on a device (with that device current) looks up
+ * the buffer's device address; make that first call outside graph capture.
+ *   - A call whose split needs more than PA_DECODE_SCRATCH_BYTES
+ *     (pa_decode_workspace_bytes) returns PA_ERR_WORKSPACE with no side
+ *     effect.  The balanced split (PA_PARTITION_BALANCED, the library's
+ *     choice) always fits; fixed partitions fit while
+ *     num_seqs * num_q_heads * ceil(max_context_len / P) * (head_dim + 2) * 4
+ *     <= PA_DECODE_SCRATCH_BYTES.
+ *   - Every call on one GPU shares that GPU's buffer, and a call leaves its
+ *     partial results there.  Nothing in it needs to start at zero: a call
+ *     reads only what it wrote itself.  Calls that may overlap on one GPU
+ *     (different streams, or different threads without ordering) race on the
+ *     buffer and give undefined results: order them on one stream.
+ */
+#define PA_DECODE_SCRATCH_BYTES (64u << 20)
+pa_status pa_decode_attention_noalloc(void* out, const void* query, const void* k_pool, const void* v_pool,
+                                      const int32_t* block_tables, const int32_t* context_lens,
+                                      int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                      int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                                      int32_t num_blocks, int32_t max_context_len, float scale,
+                                      int32_t partition_size, pa_dtype dtype, void* stream);
 
 /*
  * pa_prefill_attention -- causal multi-token attention over a paged, partly

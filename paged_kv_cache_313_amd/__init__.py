@@ -18,7 +18,8 @@ from . import _lib
 from ._lib import PA_PARTITION_BALANCED, PagedKVError, load  # noqa: F401
 from .block_manager import BlockManager  # noqa: F401
 
-__all__ = ["kv_append", "block_copy", "decode_attention", "prefill_attention", "decode_attention_hier",
+__all__ = ["kv_append", "block_copy", "decode_attention", "decode_attention_noalloc", "prefill_attention",
+           "decode_attention_hier",
            "prefill_attention_hier", "decode_workspace_bytes",
            "choose_partition", "swap_out", "swap_in", "swap_buffer", "stream_read", "PagedKVError", "load",
            "PA_PARTITION_BALANCED", "BlockManager"]
@@ -215,6 +216,39 @@ def decode_attention(query: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Te
                                  int(partition_size), _dtype_code(query), ws_ptr, ws_bytes,
                                  _stream(query, stream))
     _lib.check("pa_decode_attention", st)
+    return out
+
+
+def decode_attention_noalloc(query: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+                             block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
+                             max_context_len: int, partition_size: Optional[int] = None,
+                             out: torch.Tensor = None, stream=None) -> torch.Tensor:
+    """decode_attention through pa_decode_attention_noalloc: no workspace
+    argument, the split's partial results go to the library's static device
+    scratch (PA_DECODE_SCRATCH_BYTES per GPU; calls on one GPU must not
+    overlap).  ``out`` must be given (the call itself allocates nothing)."""
+    lib = load()
+    S, Hq, D = query.shape
+    NB, Hkv, bs, D2 = k_pool.shape
+    if D2 != D or v_pool.shape != k_pool.shape:
+        raise ValueError("head_dim mismatch between query and pools")
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise TypeError("block_tables and context_lens must be int32")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or context_lens.numel() != S:
+        raise ValueError("block_tables must be [S, max_blocks_per_seq] and context_lens [S]")
+    if not (query.dtype == k_pool.dtype == v_pool.dtype):
+        raise TypeError("query and pools must share a dtype")
+    if out is None:
+        raise ValueError("decode_attention_noalloc needs a caller-allocated out")
+    _check_out(out, query)
+    if partition_size is None:
+        partition_size = choose_partition(S, Hkv, max_context_len, bs)
+    st = lib.pa_decode_attention_noalloc(_dev(out, "out"), _dev(query, "query"), _dev(k_pool, "k_pool"),
+                                         _dev(v_pool, "v_pool"), _dev(block_tables, "block_tables"),
+                                         _dev(context_lens, "context_lens"), S, Hq, Hkv, D, bs,
+                                         block_tables.shape[1], NB, int(max_context_len), float(scale),
+                                         int(partition_size), _dtype_code(query), _stream(query, stream))
+    _lib.check("pa_decode_attention_noalloc", st)
     return out
 
 

@@ -12,6 +12,7 @@ LIB_PATH = os.path.join(HERE, "libpagedkv.so")
 PA_OK = 0
 PA_F32, PA_F16, PA_BF16 = 0, 1, 2
 PA_STREAM_READ_PARTIALS = 16384   # include/pa.h
+PA_DECODE_SCRATCH_BYTES = 64 << 20   # include/pa.h
 PA_PARTITION_BALANCED = -1
 STATUS_NAMES = {0: "PA_OK", 1: "PA_ERR_NULL", 2: "PA_ERR_SHAPE", 3: "PA_ERR_BLOCK_SIZE",
                 4: "PA_ERR_DTYPE", 5: "PA_ERR_PARTITION", 6: "PA_ERR_WORKSPACE", 7: "PA_ERR_HIP",
@@ -30,6 +31,8 @@ SIGNATURES = {
     "pa_decode_attention": (_c_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _c_i32, _c_i32, _c_i32, _c_i32,
                                      _c_i32, _c_i32, _c_i32, _c_i32, _c_f32, _c_i32, _c_i32, _vp,
                                      _c_size, _vp]),
+    "pa_decode_attention_noalloc": (_c_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _c_i32, _c_i32, _c_i32, _c_i32,
+                                             _c_i32, _c_i32, _c_i32, _c_i32, _c_f32, _c_i32, _c_i32, _vp]),
     "pa_prefill_attention": (_c_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_i32, _c_i32, _c_i32, _c_i32,
                                       _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_f32, _c_i32, _vp]),
     "pa_decode_attention_hier": (_c_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_i32, _c_i32, _c_i32,

@@ -15,6 +15,8 @@
 
 #define PA_EXPORT extern "C" __attribute__((visibility("default")))
 
+static_assert(pa::kDecodeScratchBytes == (size_t)PA_DECODE_SCRATCH_BYTES, "scratch size in pa.h");
+
 namespace {
 
 thread_local int g_last_hip_error = 0;
@@ -321,7 +323,7 @@ static pa_status decode_impl(void* out, const void* query, const void* k_pool, c
                              int32_t block_size, int32_t max_blocks_per_seq, int32_t num_blocks,
                              int32_t max_context_len, float scale, int32_t partition_size, pa_dtype dtype,
                              void* workspace, size_t workspace_bytes, void* stream,
-                             const HierTables& hier) {
+                             const HierTables& hier, bool use_scratch = false) {
   if (!dtype_ok(dtype)) return PA_ERR_DTYPE;
   if (!block_size_ok(block_size)) return PA_ERR_BLOCK_SIZE;
   if (num_seqs < 0 || num_q_heads < 1 || num_kv_heads < 1 || !head_dim_ok(head_dim) ||
@@ -370,6 +372,14 @@ static pa_status decode_impl(void* out, const void* query, const void* k_pool, c
   if (split) {
     const size_t need = pa_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
                                                   max_context_len, partition_size);
+    if (use_scratch) {   // the library's static device scratch instead of a caller's workspace
+      if (need > pa::kDecodeScratchBytes) return PA_ERR_WORKSPACE;
+      void* p = nullptr;
+      const hipError_t e = pa::decode_scratch(&p);
+      if (e != hipSuccess) return hip_status(e);
+      workspace = p;
+      workspace_bytes = pa::kDecodeScratchBytes;
+    }
     if (!workspace || workspace_bytes < need) return PA_ERR_WORKSPACE;
     if ((reinterpret_cast<uintptr_t>(workspace) & 15u) != 0) return PA_ERR_ALIGN;
     char* ws = static_cast<char*>(workspace);
@@ -428,4 +438,16 @@ PA_EXPORT pa_status pa_decode_attention_hier(void* out, const void* query, const
   return decode_impl(out, query, k_pool, v_pool, small_tables, context_lens, num_seqs, num_q_heads,
                      num_kv_heads, head_dim, block_size, max_small_per_seq, num_blocks, max_context_len,
                      scale, partition_size, dtype, workspace, workspace_bytes, stream, h);
+}
+
+PA_EXPORT pa_status pa_decode_attention_noalloc(void* out, const void* query, const void* k_pool,
+                                                const void* v_pool, const int32_t* block_tables,
+                                                const int32_t* context_lens, int32_t num_seqs,
+                                                int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                                int32_t block_size, int32_t max_blocks_per_seq,
+                                                int32_t num_blocks, int32_t max_context_len, float scale,
+                                                int32_t partition_size, pa_dtype dtype, void* stream) {
+  return decode_impl(out, query, k_pool, v_pool, block_tables, context_lens, num_seqs, num_q_heads,
+                     num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks, max_context_len,
+                     scale, partition_size, dtype, nullptr, 0, stream, HierTables{}, true);
 }

@@ -252,7 +252,11 @@ __device__ __forceinline__ uint32_t xcd_unit(uint32_t b, uint32_t n) {
 constexpr int kModeUnit = 0;       // one workgroup per (sequence, head group[, partition])
 constexpr int kModeBalanced = 1;   // resident grid, equal share of the flattened tiles each
 constexpr int kBalancedMaxSeqs = 4096;   // sequences a balanced launch can take (LDS prefix)
-constexpr int kBalancedMaxWaves = 4096;  // waves a balanced workspace is sized for
+// Waves a balanced workspace is sized for.  MI355X keeps 256 CUs x one 4-wave
+// workgroup resident in the balanced grid (1,024 waves); the grid is capped
+// here, so a device with more CUs gets fewer workgroups per CU, never more
+// partial slots than the workspace holds.
+constexpr int kBalancedMaxWaves = 2048;
 
 // Arguments of the decode kernels (by value, in the kernarg segment).
 struct DecodeArgs {

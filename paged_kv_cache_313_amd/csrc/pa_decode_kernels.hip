@@ -25,12 +25,39 @@
 //    and each takes an equal share of the flattened (sequence, head group,
 //    tile) space, so ragged batches finish together; a (sequence, head group)
 //    shared by several waves is merged by decode_merge_balanced_kernel.
+#include <mutex>
 #include <type_traits>
 
 #include "pa_common.hpp"
 #include "pa_launch.hpp"
 
 namespace pa {
+
+// Workspace of pa_decode_attention_noalloc, for callers that cannot allocate:
+// each GPU the library runs on holds its own copy until the process ends.
+// Host code never uses this name as an address (on the host it is only a
+// stand-in); decode_scratch() returns the device address.
+static __device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
+
+hipError_t decode_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
 
 constexpr int kTile = 16;      // tokens per tile
 constexpr int kTblWin = 256;   // block-table entries a wave stages in LDS at a time

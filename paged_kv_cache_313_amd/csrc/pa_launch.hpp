@@ -40,6 +40,12 @@ hipError_t launch_stream_read(const void* buf, uint64_t bytes, uint32_t* partial
 hipError_t launch_decode(const DecodeArgs& args, Elem elem, int head_dim, int block_size,
                          int group, hipStream_t stream);
 
+// Device scratch of the no-allocation decode entry point: a file-scope
+// __device__ array of kDecodeScratchBytes, one per GPU, whose device address
+// is looked up once per device (with that device current) and cached.
+constexpr size_t kDecodeScratchBytes = (size_t)64 << 20;
+hipError_t decode_scratch(void** ptr);
+
 // Prefill over a cached prefix (f16/bf16, group size 1..16): one launch.
 hipError_t launch_prefill(const PrefillArgs& args, Elem elem, int head_dim, int block_size, int group,
                           hipStream_t stream);

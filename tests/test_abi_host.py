@@ -130,15 +130,44 @@ def test_decode_argument_checks(lib, kw, status):
     assert decode(lib, **kw) == status
 
 
+def decode_noalloc(lib, **kw):
+    a = dict(DEC_OK, **kw)
+    return lib.pa_decode_attention_noalloc(a["out"], a["q"], a["k"], a["v"], a["tbl"], a["lens"], a["S"],
+                                           a["Hq"], a["Hkv"], a["D"], a["bs"], a["MB"], a["NB"], a["maxL"],
+                                           a["scale"], a["P"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=9), 4), (dict(bs=4), 3), (dict(D=80), 2), (dict(Hq=24, Hkv=8), 2), (dict(P=24), 5),
+    (dict(P=-1, S=4097), 5), (dict(out=None), 1), (dict(k=B + 4), 8),
+    # fixed partitions whose partials exceed the 64 MiB scratch: rejected before any HIP call
+    (dict(S=16, Hq=32, Hkv=8, maxL=131072, MB=8192, P=512), 6),
+    (dict(S=4096, Hq=32, Hkv=8, maxL=2048, P=512), 6),
+    (dict(S=0, out=None, q=None), 0),
+])
+def test_decode_noalloc_argument_checks(lib, kw, status):
+    assert decode_noalloc(lib, **kw) == status
+
+
+def test_decode_noalloc_scratch_covers_every_balanced_shape(lib):
+    # the library's default split fits the static scratch for every supported shape
+    f = lib.pa_decode_workspace_bytes
+    for G in (1, 2, 4, 8, 16):
+        for D in (64, 128):
+            assert f(4096, 8 * G, 8, D, 131072, -1) <= _lib.PA_DECODE_SCRATCH_BYTES
+    assert f(16, 32, 8, 128, 131072, 512) > _lib.PA_DECODE_SCRATCH_BYTES
+    assert f(16, 32, 8, 128, 65536, 512) <= _lib.PA_DECODE_SCRATCH_BYTES
+
+
 def test_workspace_size(lib):
     f = lib.pa_decode_workspace_bytes
     assert f(16, 32, 8, 128, 131072, 512) == 16 * 32 * 256 * 130 * 4
     assert f(16, 32, 8, 128, 131072, 0) == 0
     assert f(16, 32, 8, 128, 500, 512) == 0              # one partition: written directly
     assert f(3, 8, 8, 64, 513, 512) == 3 * 8 * 2 * 66 * 4
-    # balanced: prefix sums (padded to 16 B) + 2 slots x 4096 waves x group rows
-    assert f(256, 32, 8, 128, 8193, -1) == 1040 + 2 * 4096 * 4 * 130 * 4
-    assert f(5, 8, 8, 64, 100, -1) == 32 + 2 * 4096 * 1 * 66 * 4
+    # balanced: prefix sums (padded to 16 B) + 2 slots x 2048 waves x group rows
+    assert f(256, 32, 8, 128, 8193, -1) == 1040 + 2 * 2048 * 4 * 130 * 4
+    assert f(5, 8, 8, 64, 100, -1) == 32 + 2 * 2048 * 1 * 66 * 4
     assert f(-1, 8, 8, 64, 513, 512) == ctypes.c_size_t(-1).value
     assert f(4, 8, 3, 64, 513, 512) == ctypes.c_size_t(-1).value
     assert f(4, 8, 8, 64, 513, -2) == ctypes.c_size_t(-1).value
