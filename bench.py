@@ -28,7 +28,19 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBPS = 8000.0
 METRIC = "decode seq-steps/s + achieved KV-read GB/s (% of MI355X HBM peak), 1 GPU"
-COUNTERS_FILE = os.path.join(ROOT, "profiles", "decode_gqa_llama3_8b_counters.json")
+# rocprofv3 HBM byte counters of the decode call, one file per workload (and
+# per non-default partition choice), written by --ingest-counters
+PROFILE_STEMS = {1: "decode_tiny_mha_f32", 2: "decode_mha_opt13b", 3: "decode_gqa_llama3_8b",
+                 4: "decode_prefix_shared_sampling", 5: "decode_long_context"}
+
+
+def counters_file(config, block_size=16, partition=None):
+    """profiles/<workload>[_bs<block size>][_p<partition>]_counters.json; the
+    suffix _p<P> only when the partition is not the library's choice."""
+    stem = PROFILE_STEMS[config] + (f"_bs{block_size}" if config == 5 else "")
+    if partition is not None:
+        stem += f"_p{partition}"
+    return os.path.join(ROOT, "profiles", stem + "_counters.json")
 KERNEL_SOURCES = ["paged_kv_cache_313_amd/csrc/pa_decode_kernels.hip",
                   "paged_kv_cache_313_amd/csrc/pa_common.hpp"]
 
@@ -100,10 +112,12 @@ def _pmc_per_dispatch(root, counter):
     return {k: sums[k] / counts[k] for k in sums}
 
 
-def ingest_counters(root, config=3, partition=-1, out_path=None):
+def ingest_counters(root, config=3, partition=-1, out_path=None, block_size=16, explicit_partition=False):
     """Turn FETCH_SIZE / WRITE_SIZE passes (KiB per dispatch) into bytes per
     decode call, each scaled by what the same counter reads for a plain copy of
-    known size, and store them keyed by the kernel sources' hash."""
+    known size, and store them keyed by the kernel sources' hash.  `partition`
+    names the decode kernels: -1 the balanced kernel + its merge, P > 0 the
+    unit kernel + the partition merge, 0 the unit kernel alone."""
     calib = 1 << 30
     fetch, write = _pmc_per_dispatch(os.path.join(root, "fetch"), "FETCH_SIZE"), \
         _pmc_per_dispatch(os.path.join(root, "write"), "WRITE_SIZE")
@@ -118,18 +132,26 @@ def ingest_counters(root, config=3, partition=-1, out_path=None):
         if len(ks) != 1:
             raise SystemExit(f"expected one kernel named like {tag!r}, found {ks}")
         return ks[0]
-    dk, mk = pick(fetch, "decode_balanced_kernel"), pick(fetch, "decode_merge_balanced_kernel")
-    dec_b = fetch[dk] * 1024 * ff + write[dk] * 1024 * wf
-    mrg_f, mrg_w = fetch[mk] * 1024 * ff, write[mk] * 1024 * wf
-    out = {"config": config, "partition": partition, "source_sha": source_sha(), "kernel": dk,
-           "fetch_kib_per_dispatch": fetch[dk], "write_kib_per_dispatch": write[dk],
+    if partition == -1:
+        dk, mk = pick(fetch, "decode_balanced_kernel"), pick(fetch, "decode_merge_balanced_kernel")
+    elif partition > 0:
+        dk, mk = pick(fetch, "decode_unit_kernel"), pick(fetch, "decode_merge_parts_kernel")
+    else:
+        dk, mk = pick(fetch, "decode_unit_kernel"), None
+    dec_f, dec_w = fetch[dk] * 1024 * ff, write[dk] * 1024 * wf
+    mrg_f, mrg_w = (fetch[mk] * 1024 * ff, write[mk] * 1024 * wf) if mk else (0.0, 0.0)
+    out = {"config": config, "partition": partition, "block_size": block_size, "source_sha": source_sha(),
+           "kernel": dk, "fetch_kib_per_dispatch": fetch[dk], "write_kib_per_dispatch": write[dk],
            "calibration": {"copy_bytes": calib, "copy_kernel": copy_k, "fetch_kib": calf[copy_k],
                            "write_kib": calw[copy_k], "fetch_factor": ff, "write_factor": wf},
-           "merge_kernel": {"name": mk, "fetch_kib_per_dispatch": fetch[mk], "write_kib_per_dispatch": write[mk],
-                            "fetch_bytes": mrg_f, "write_bytes": mrg_w},
-           "decode_kernel_bytes": dec_b, "hbm_bytes_per_launch": dec_b + mrg_f + mrg_w,
+           "merge_kernel": None if mk is None else {
+               "name": mk, "fetch_kib_per_dispatch": fetch[mk], "write_kib_per_dispatch": write[mk],
+               "fetch_bytes": mrg_f, "write_bytes": mrg_w},
+           "decode_kernel_bytes": dec_f + dec_w, "fetch_bytes_per_launch": dec_f + mrg_f,
+           "write_bytes_per_launch": dec_w + mrg_w, "hbm_bytes_per_launch": dec_f + dec_w + mrg_f + mrg_w,
            "note": "hbm_bytes_per_launch covers one pa_decode_attention call: the decode kernel and its merge"}
-    with open(out_path or COUNTERS_FILE, "w") as f:
+    path = out_path or counters_file(config, block_size, partition if explicit_partition else None)
+    with open(path, "w") as f:
         json.dump(out, f, indent=1)
         f.write("\n")
     print(json.dumps(out, indent=1))
@@ -183,16 +205,95 @@ def _cpu_seq(s):
     return s, out
 
 
-def cpu_baseline(b, min_seconds):
+def cgroup_cpu_limit():
+    """CPUs granted by the cgroup's CPU quota (cgroup v2 cpu.max or v1
+    cfs_quota/period), or None when unlimited or unreadable."""
+    try:
+        with open("/sys/fs/cgroup/cpu.max") as f:
+            quota, period = f.read().split()[:2]
+        return None if quota == "max" else int(quota) / int(period)
+    except (OSError, ValueError):
+        pass
+    try:
+        with open("/sys/fs/cgroup/cpu/cpu.cfs_quota_us") as f:
+            quota = int(f.read())
+        with open("/sys/fs/cgroup/cpu/cpu.cfs_period_us") as f:
+            period = int(f.read())
+        return None if quota <= 0 else quota / period
+    except (OSError, ValueError):
+        return None
+
+
+def cpu_share():
+    """Worker processes for the oracle: the CPUs this process may run on
+    (sched_getaffinity), cut to the cgroup quota and to OMP_NUM_THREADS when
+    the host sets them (a shared GPU host states each job's CPU share that way)."""
+    aff = len(os.sched_getaffinity(0))
+    quota = cgroup_cpu_limit()
+    omp = os.environ.get("OMP_NUM_THREADS", "")
+    cores = aff
+    if quota:
+        cores = min(cores, max(1, int(quota)))
+    if omp.isdigit() and int(omp) > 0:
+        cores = min(cores, int(omp))
+    return max(1, cores), {"affinity_cpus": aff, "cgroup_cpu_limit": quota, "omp_num_threads": omp or None}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def cpu_single_core(b, min_seconds=2.0, max_passes=20):
+    """The oracle over the whole batch in this process on one core (one BLAS
+    thread): seq-steps/s.  Used for the small workloads only."""
+    import numpy as np
+    import oracle.pa_oracle as O
+    try:
+        from threadpoolctl import threadpool_limits
+        limit = threadpool_limits(1)
+    except Exception:
+        limit = None
+    try:
+        G = b.num_q_heads // b.num_kv_heads
+        out = np.empty((b.num_seqs, b.num_q_heads, b.head_dim))
+        passes = 0
+        t0 = time.perf_counter()
+        while True:
+            for s in range(b.num_seqs):
+                for g in range(b.num_kv_heads):
+                    out[s, g * G:(g + 1) * G] = O.decode_group(b.query, b._k_after, b._v_after, b.block_tables,
+                                                               b.context_lens, b.scale, b.block_size, b.dtype,
+                                                               s, g)
+            passes += 1
+            el = time.perf_counter() - t0
+            if el >= min_seconds or passes >= max_passes:
+                break
+    finally:
+        if limit is not None:
+            limit.restore_original_limits()
+    return {"value": b.num_seqs * passes / el, "unit": "seq-steps/s", "cores": 1,
+            "sample": f"all {b.num_seqs} sequences, {passes} passes in {el:.2f} s, 1 process x 1 BLAS thread"}
+
+
+def cpu_baseline(b, min_seconds, single_core=False):
     """The fp64 oracle, unchanged, over the whole batch: the step's CoW copies
     and appends, then attention for every sequence, sequences dealt
-    longest-first to one worker process per host core (one BLAS thread each)."""
+    longest-first to one worker process per CPU of this job's share (one BLAS
+    thread each)."""
     import multiprocessing as mp
 
     import numpy as np
     import oracle.pa_oracle as O
     global _CPU_BATCH
-    cores = max(1, min(len(os.sched_getaffinity(0)), 16))
+    cores, share = cpu_share()
     if "hier" in b.meta:     # the oracle reads two-level tables through their flat expansion
         import dataclasses
         large, nl, H = b.meta["hier"]
@@ -227,7 +328,10 @@ def cpu_baseline(b, min_seconds):
     res = {"value": value, "unit": "seq-steps/s", "cores": cores, "kind": "oracle",
            "sample": f"all {b.num_seqs} sequences of the workload (step's CoW copies + appends + fp64 attention), "
                      f"{passes} passes in {el:.2f} s, {cores} worker processes x 1 BLAS thread",
-           "kv_gbps_equiv": b.kv_bytes() * passes / el / 1e9}
+           "kv_gbps_equiv": b.kv_bytes() * passes / el / 1e9,
+           "cpu_model": cpu_model(), "cpu_share": share}
+    if single_core:
+        res["single_core"] = cpu_single_core(b)
     return res, out
 
 
@@ -250,6 +354,33 @@ def algorithmic_bytes(b):
     return kv + qo + tbl, kv
 
 
+def unique_kv_bytes(b):
+    """K+V bytes of the distinct physical blocks the decode reads: a block that
+    several sequences share (a prompt's blocks under parallel sampling) counts
+    once, with the most valid tokens any of its readers uses.  Two-level
+    layouts share nothing and equal the logical bytes."""
+    import numpy as np
+    if "hier" in b.meta:
+        return b.kv_bytes()
+    bs = b.block_size
+    L = b.context_lens.astype(np.int64)
+    nblk = -(-L // bs)
+    blocks, toks = [], []
+    for s in range(b.num_seqs):
+        n = int(nblk[s])
+        if n == 0:
+            continue
+        blocks.append(b.block_tables[s, :n].astype(np.int64))
+        t = np.full(n, bs, dtype=np.int64)
+        t[-1] = L[s] - (n - 1) * bs
+        toks.append(t)
+    if not blocks:
+        return 0
+    most = np.zeros(b.num_blocks, dtype=np.int64)
+    np.maximum.at(most, np.concatenate(blocks), np.concatenate(toks))
+    return int(most.sum()) * b.num_kv_heads * b.head_dim * 2 * b.elt_bytes
+
+
 def decode_kernel_name(b, part):
     core = "MfmaCore" if b.num_q_heads != b.num_kv_heads and b.dtype != "f32" else "ValuCore"
     if part == -1:
@@ -267,15 +398,18 @@ def source_sha():
     return h.hexdigest()[:16]
 
 
-def traffic_from_profile(config, partition):
+def counters_from_profile(config, partition, block_size=16, explicit_partition=False):
+    """The decode call's counter file for this workload, or None when there is
+    none or the kernel sources changed since it was taken."""
     try:
-        with open(COUNTERS_FILE) as f:
+        with open(counters_file(config, block_size, partition if explicit_partition else None)) as f:
             c = json.load(f)
     except (OSError, ValueError):
         return None
-    if c.get("source_sha") != source_sha() or c.get("config") != config or c.get("partition") != partition:
+    if (c.get("source_sha") != source_sha() or c.get("config") != config or c.get("partition") != partition
+            or c.get("block_size", 16) != block_size):
         return None
-    return c.get("hbm_bytes_per_launch")
+    return c
 
 
 def block_manager_leg(b, steps: int) -> dict:
@@ -461,6 +595,43 @@ def cold_decode_leg(decode_call, stream, reps: int = 10, evict_bytes: int = 1 <<
             "what": "median of per-call HIP-event times, each call after reading a 1 GiB scratch buffer"}
 
 
+def step_latency_leg(step_fn, stream, graphs, n: int = 20) -> dict:
+    """Percentiles of single-step latency: n steps, each bracketed by HIP
+    events on the stream.  A read of a 64 MiB buffer is queued before each
+    step (a 1 GiB one before the first), so that the host has queued the
+    events and the step before the GPU reaches them and no launch gap is
+    timed.  Steps replay a one-step HIP graph when graphs are in use."""
+    import numpy as np
+    import torch
+
+    run = step_fn
+    if graphs:
+        g = torch.cuda.CUDAGraph()
+        cs = torch.cuda.Stream()
+        cs.wait_stream(stream)
+        with torch.cuda.graph(g, stream=cs):
+            step_fn(cs)
+        stream.wait_stream(cs)
+        run = lambda st: g.replay()
+    big = torch.ones(1 << 28, dtype=torch.int32, device="cuda")
+    small = big[: 1 << 24]
+    sink = torch.empty((), dtype=torch.int64, device="cuda")
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    torch.cuda.synchronize()
+    torch.sum(big, dim=0, dtype=torch.int64, out=sink)
+    for e0, e1 in ev:
+        torch.sum(small, dim=0, dtype=torch.int64, out=sink)
+        e0.record(stream)
+        run(stream)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ms = np.array([e0.elapsed_time(e1) for e0, e1 in ev])
+    del big, small, sink
+    return {"steps": n, "p10_ms": float(np.percentile(ms, 10)), "p50_ms": float(np.percentile(ms, 50)),
+            "p90_ms": float(np.percentile(ms, 90)), "min_ms": float(ms.min()), "max_ms": float(ms.max()),
+            "what": "per-step HIP-event times, each step queued behind a 64 MiB read so no launch gap is timed"}
+
+
 def achievable_read_leg(stream, nbytes: int = 4 << 30, reps: int = 10) -> dict:
     """The box's achievable HBM read bandwidth: pa_stream_read sweeping a
     4 GiB buffer (16 times the MALL), reps back-to-back calls timed with HIP
@@ -496,7 +667,9 @@ def main():
               "the decode path here is a single-GPU kernel; sharding across GPUs is not implemented", file=sys.stderr)
         sys.exit(2)
     if args.ingest_counters:
-        ingest_counters(args.ingest_counters)
+        part = args.partition if args.partition is not None else -1
+        ingest_counters(args.ingest_counters, config=args.config, partition=part, block_size=args.block_size,
+                        explicit_partition=args.partition is not None)
         return
     if args.calibrate_copy_mib:
         calibrate_copy(args.calibrate_copy_mib)
@@ -520,8 +693,8 @@ def main():
           f"KV bytes {b.kv_bytes() / 1e9:.3f} GB", file=sys.stderr, flush=True)
 
     cpu, cpu_out = None, None
-    if not args.no_cpu_baseline:
-        cpu, cpu_out = cpu_baseline(b, args.cpu_seconds)   # before any GPU call (forked workers)
+    if not args.no_cpu_baseline:   # before any GPU call (forked workers)
+        cpu, cpu_out = cpu_baseline(b, args.cpu_seconds, single_core=args.config in (1, 2))
         print(f"[bench] cpu oracle: {cpu['value']:.1f} seq-steps/s on {cpu['cores']} cores",
               file=sys.stderr, flush=True)
 
@@ -636,11 +809,16 @@ def main():
     app_ms = events_ms(k_calls("append", append_only), 1) / K if has_append else None
     dec_ms = events_ms(k_calls("decode", decode_only), 1) / K
     alg_bytes, kv_bytes = algorithmic_bytes(b)
-    achieved = alg_bytes / (dec_ms * 1e-3) / 1e9
+    uniq_kv = unique_kv_bytes(b)
+    # the roofline counts each physical K/V byte once: blocks that several
+    # sequences share (prefix-shared sampling) are one HBM read at best
+    alg_unique = alg_bytes - kv_bytes + uniq_kv
+    achieved = alg_unique / (dec_ms * 1e-3) / 1e9
+    latency = step_latency_leg(step_fn, stream, graphs, max(K, 20))
 
     cold = cold_decode_leg(decode_only, stream)
     cold["kv_read_gbps"] = kv_bytes / (cold["decode_ms_median"] * 1e-3) / 1e9
-    cold["pct_of_hbm_peak"] = 100.0 * alg_bytes / (cold["decode_ms_median"] * 1e-3) / 1e9 / HBM_PEAK_GBPS
+    cold["pct_of_hbm_peak"] = 100.0 * alg_unique / (cold["decode_ms_median"] * 1e-3) / 1e9 / HBM_PEAK_GBPS
     stream_leg = achievable_read_leg(stream)
     stream_leg["decode_frac_of_achievable"] = achieved / stream_leg["gbps"]
     bm_leg = block_manager_leg(b, max(args.steps, 10))
@@ -662,10 +840,13 @@ def main():
         parity = {"max_abs_err": float(err.max()), "within_tolerance": ok,
                   "checked": "all outputs vs the fp64 oracle"}
 
+    explicit = args.partition is not None
+    ctr = counters_from_profile(args.config, part, b.block_size, explicit)
     cfg = {"workload": WORKLOADS[args.config], "num_seqs": b.num_seqs, "num_q_heads": b.num_q_heads,
            "num_kv_heads": b.num_kv_heads, "head_dim": b.head_dim, "block_size": b.block_size,
            "num_blocks": b.num_blocks, "partition_size": part, "table_layout": args.table_layout,
-           "kv_bytes_per_step": kv_bytes, "tokens": int(b.context_lens.sum())}
+           "kv_bytes_per_step": kv_bytes, "unique_kv_bytes_per_step": uniq_kv,
+           "tokens": int(b.context_lens.sum())}
     line = {
         "metric": METRIC,
         "value": b.num_seqs / (ms_per_step * 1e-3),
@@ -688,9 +869,17 @@ def main():
         "block_copy_ms": cp_ms,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS,
-                     "traffic": traffic_from_profile(args.config, part),
+                     "traffic": None if ctr is None else ctr["hbm_bytes_per_launch"],
                      "kernel": decode_kernel_name(b, part),
-                     "algorithmic_bytes_per_launch": alg_bytes},
+                     "algorithmic_bytes_per_launch": alg_unique,
+                     "logical_bytes_per_launch": alg_bytes,
+                     "logical_gbps": alg_bytes / (dec_ms * 1e-3) / 1e9,
+                     "fetched_bytes_per_launch": None if ctr is None else ctr.get("fetch_bytes_per_launch"),
+                     "bytes": "algorithmic = K/V of the distinct physical blocks read (valid tokens) + query + "
+                              "output + table entries + lengths; logical counts a shared block once per "
+                              "sequence that reads it; traffic/fetched = rocprofv3 FETCH_SIZE + WRITE_SIZE of "
+                              "the call, scaled by a plain copy's counts"},
+        "step_latency": latency,
         "cpu_baseline": cpu,
         "parity": parity,
         "decode_cold_cache": cold,
