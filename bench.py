@@ -41,7 +41,7 @@ def counters_file(config, block_size=16, partition=None):
     if partition is not None:
         stem += f"_p{partition}"
     return os.path.join(ROOT, "profiles", stem + "_counters.json")
-KERNEL_SOURCES = ["paged_kv_cache_313_amd/csrc/pa_decode_kernels.hip",
+KERNEL_SOURCES = ["paged_kv_cache_313_amd/csrc/pa_decode_core.hpp",
                   "paged_kv_cache_313_amd/csrc/pa_common.hpp"]
 
 WORKLOADS = {

@@ -19,9 +19,9 @@ BUILD_DIR = os.path.join(HERE, "_build")
 LIB_NAME = "libpagedkv.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 
-SOURCES = ["pa_api.cpp", "pa_block_manager.cpp", "pa_copy_kernels.hip", "pa_decode_kernels.hip",
-           "pa_prefill_kernels.hip"]
-HEADERS = ["pa_common.hpp", "pa_launch.hpp"]
+SOURCES = ["pa_decode_bf16.hip", "pa_decode_f16.hip", "pa_decode_f32.hip", "pa_prefill_kernels.hip",
+           "pa_api.cpp", "pa_block_manager.cpp", "pa_copy_kernels.hip", "pa_decode_kernels.hip"]
+HEADERS = ["pa_common.hpp", "pa_launch.hpp", "pa_decode_core.hpp"]
 ARCH = "gfx950"
 
 # Per-source additions.  The prefill kernel keeps its MFMA accumulators in

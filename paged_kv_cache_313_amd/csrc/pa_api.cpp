@@ -391,9 +391,10 @@ static pa_status decode_impl(void* out, const void* query, const void* k_pool, c
     } else {
       rows = (size_t)num_seqs * num_q_heads * (size_t)np;
     }
-    a.ws_m = reinterpret_cast<float*>(ws);
+    // partial outputs first: each row of head_dim floats starts 16-byte aligned
+    a.ws_o = reinterpret_cast<float*>(ws);
+    a.ws_m = a.ws_o + rows * (size_t)head_dim;
     a.ws_l = a.ws_m + rows;
-    a.ws_o = a.ws_l + rows;
   }
   a.large_tables = hier.large_tables;
   a.num_large = hier.num_large;

@@ -226,6 +226,43 @@ __device__ __forceinline__ float xor_lane(float x) {
   }
 }
 
+// x combined with the value of lane ^ 16 or lane ^ 32 by the VALU lane swaps
+// of gfx950 (v_permlane16_swap / v_permlane32_swap, no LDS crossbar): the
+// swap leaves the lane's own value in one result and its partner's in the
+// other, and both operations below are exact in either operand order, so
+// the results equal those of a butterfly through the crossbar bit for bit.
+template <int MASK>
+__device__ __forceinline__ float swap_pair_sum(float x) {
+  static_assert(MASK == 16 || MASK == 32, "lane swaps");
+  const uint32_t u = __float_as_uint(x);
+  if constexpr (MASK == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  } else {
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+}
+template <int MASK>
+__device__ __forceinline__ float swap_pair_max(float x) {
+  static_assert(MASK == 16 || MASK == 32, "lane swaps");
+  const uint32_t u = __float_as_uint(x);
+  if constexpr (MASK == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  } else {
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  }
+}
+
+// the value of lane (i + N) mod 16 within each 16-lane row (DPP row_ror:N)
+template <int N>
+__device__ __forceinline__ float row_ror(float x) {
+  static_assert(N >= 1 && N <= 15, "row rotate");
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x120 + N, 0xf, 0xf, false));
+}
+
 // broadcast lane `src` of each quad (DPP quad_perm) -- src in 0..3
 template <int SRC>
 __device__ __forceinline__ float quad_bcast(float x) {
@@ -266,10 +303,10 @@ struct DecodeArgs {
   const void* v_pool;
   const int32_t* block_tables;  // [S, MB]
   const int32_t* context_lens;  // [S]
+  float* ws_o;                // [S, Hq, NP, D] un-normalised partial outputs, 16-byte aligned
+                              // (balanced mode: 2 slots per wave of H rows each)
   float* ws_m;                // [S, Hq, NP] running max (log2 domain)
   float* ws_l;                // [S, Hq, NP] running sum
-  float* ws_o;                // [S, Hq, NP, D] un-normalised partial outputs
-                              // (balanced mode: 2 slots per wave of H rows each)
   int32_t* ws_cum;            // balanced mode: [S + 1] tile prefix sums
   int32_t num_seqs, num_q_heads, num_kv_heads;
   int32_t max_blocks_per_seq, num_blocks, max_context_len;

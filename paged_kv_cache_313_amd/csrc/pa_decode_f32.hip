@@ -1,0 +1,11 @@
+// Decode kernels over f32 pools (one instantiation unit per storage type,
+// compiled in parallel).
+#include "pa_decode_core.hpp"
+
+namespace pa {
+
+hipError_t launch_decode_f32(const DecodeArgs& a, int head_dim, int block_size, int group, hipStream_t st) {
+  return dispatch_t<F32>(a, head_dim, block_size, group, st);
+}
+
+}  // namespace pa

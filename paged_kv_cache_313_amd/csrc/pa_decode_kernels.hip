@@ -1,32 +1,8 @@
-// Decode attention over a paged KV cache (gfx950, wave64).
-//
-// One query token per sequence attends over the sequence's context, whose K/V
-// rows sit in fixed-size physical blocks reached through the sequence's block
-// table (vLLM/PagedAttention paged-KV analysis page, section 3.1: the kernel is
-// changed to read non-contiguous blocks; the simplified sketch walks the table
-// block by block and loads K and V of each physical page).  The sketch
-// normalises per block; the operation reached here is one softmax over the
-// whole context, evaluated as an online softmax: running maxima, running sums
-// and un-normalised accumulators are rescaled by exp(m_old - m_new) when a max
-// grows.  Scores are kept in the log2 domain (scale * log2(e) folded in) so
-// every exponential is one v_exp_f32.
-//
-// A *segment* is a token range [tok0, tok1) of one sequence for one group of
-// query heads sharing a KV head, and one wave runs it from start to end: it
-// stages the segment's block-table slice in its own LDS window (taking the
-// table->block dependent load off the tile path), streams the 16-token tiles
-// with the next tile's loads in flight, reduces across its lanes and writes
-// the result itself.  Waves never wait for one another, so a wave starting a
-// segment does not stall its neighbours.  Three ways to cut the work:
-//  * unit mode, no split: one segment per (sequence, head group);
-//  * unit mode, fixed partitions of P tokens: one segment per (sequence, head
-//    group, partition), partials merged by decode_merge_parts_kernel;
-//  * balanced mode: the grid holds exactly the waves the GPU keeps resident,
-//    and each takes an equal share of the flattened (sequence, head group,
-//    tile) space, so ragged batches finish together; a (sequence, head group)
-//    shared by several waves is merged by decode_merge_balanced_kernel.
+// Decode attention over a paged KV cache: the entry into the kernels of
+// pa_decode_core.hpp (instantiated per storage type in pa_decode_f32.hip,
+// pa_decode_f16.hip and pa_decode_bf16.hip), and the device scratch of the
+// no-allocation entry point.
 #include <mutex>
-#include <type_traits>
 
 #include "pa_common.hpp"
 #include "pa_launch.hpp"
@@ -59,1057 +35,12 @@ hipError_t decode_scratch(void** ptr) {
   return hipSuccess;
 }
 
-constexpr int kTile = 16;      // tokens per tile
-constexpr int kTblWin = 256;   // block-table entries a wave stages in LDS at a time
-// A lane rescales its accumulators only when a score exceeds its running max
-// by more than this (log2 units), so every p <= 2^8 and sums stay far from
-// fp32 overflow; the result is the same up to rounding.
-constexpr float kLazy = 8.f;
-// Tiles in flight per wave (tile_loop's ring): the current one and the next.
-// Rings of 3 and 4 (8 KiB tiles, fewer resident waves for their registers)
-// streamed no faster on the GQA batches.
-#ifndef PA_TILE_RING
-#define PA_TILE_RING 2
-#endif
-constexpr int kRing = PA_TILE_RING;
-
-// Cache policy of the K/V loads.  A tile read once per call is loaded with
-// the non-temporal hint.  Blocks that the neighbouring sequences s-1 or s+1
-// map at the same logical position (the prompt blocks that the samples or
-// beams of one request share; a scheduler keeps those sequences together, so
-// their waves run at about the same time) are loaded with the default policy,
-// so that the neighbours hit in L2 or the MALL.  Shared blocks form a prefix
-// of each table, and the tile loop is run twice -- over the window's leading
-// shared blocks, then over the rest -- so that no branch sits between a
-// tile's loads and their use.  This holds for the balanced grid (one
-// workgroup per CU, long ranges per wave).  Unit-mode grids (many resident
-// waves, one short segment each) load every tile with the default policy:
-// there the hint made a 64-sequence MHA batch 32 % slower.  The policy does
-// not change any result.
-
-// Stage table entries [first, first+count) of sequence s (1 <= count <=
-// kTblWin) into this wave's LDS window (ids clamped into the pool:
-// memory-safe on bad tables) and return how many leading entries are shared
-// with a neighbour, whose entries count only below its own block count.  All
-// loads are issued before any is used: every index is clamped into its row
-// (a row has at least one entry), so none needs a guard.  LDS
-// operations of one wave complete in order; the wait makes the entries
-// visible to every lane before the wave reads them.
-template <int BS, bool SPLIT>
-__device__ __forceinline__ int stage_table_wave(int32_t* tbl, const DecodeArgs& a, const TableView& row, int s,
-                                                int first, int count, int lane) {
-  if constexpr (!SPLIT) {   // unit mode: every tile under the default policy
-    for (int i = lane; i < count; i += kWave) {
-      const int e = row.entry(first + i);
-      tbl[i] = ((unsigned)e < (unsigned)a.num_blocks) ? e : 0;
-    }
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
-    __builtin_amdgcn_wave_barrier();
-    return count;
-  }
-  constexpr int NI = kTblWin / kWave;
-  const bool has_prev = s > 0, has_next = s + 1 < a.num_seqs;
-  const int sp = has_prev ? s - 1 : s, sn = has_next ? s + 1 : s;
-  const int lp = a.context_lens[sp], ln = a.context_lens[sn];   // issued with the entries below
-  const TableView rprev = table_view(a, sp);
-  const TableView rnext = table_view(a, sn);
-  int e[NI], ep[NI], en[NI];
-#pragma unroll
-  for (int k = 0; k < NI; ++k) {
-    const int j = first + min(lane + k * kWave, count - 1);
-    e[k] = row.entry_sel(j);
-    ep[k] = rprev.entry_sel(min(j, rprev.capacity - 1));
-    en[k] = rnext.entry_sel(min(j, rnext.capacity - 1));
-  }
-  // the neighbours' lengths clamped as clamp_len does, in blocks
-  auto nblk = [&](int L, const TableView& v) {
-    L = min(max(L, 0), min(v.capacity * BS, a.max_context_len));
-    return (L + BS - 1) / BS;
-  };
-  const int nprev = has_prev ? nblk(lp, rprev) : 0;
-  const int nnext = has_next ? nblk(ln, rnext) : 0;
-  int lead = count;   // first entry not shared (wave-uniform: from ballots)
-#pragma unroll
-  for (int k = 0; k < NI; ++k) {
-    const int i = lane + k * kWave;
-    bool unshared = false;
-    if (i < count) {
-      const int j = first + i;
-      unshared = !((j < nprev && ep[k] == e[k]) || (j < nnext && en[k] == e[k]));
-      tbl[i] = ((unsigned)e[k] < (unsigned)a.num_blocks) ? e[k] : 0;
-    }
-    const uint64_t m = __ballot(unshared);
-    if (lead == count && m != 0) lead = k * kWave + (int)__builtin_ctzll(m);
-  }
-  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
-  __builtin_amdgcn_wave_barrier();
-  return lead;
-}
-
-// The table window a wave last staged: consecutive segments of a wave are
-// mostly the same sequence under another KV head and need the same entries,
-// so a window that still covers the next one is reused (one dependent global
-// round trip less per segment start).
-struct TblCache {
-  int s = -1, first = 0, count = 0, shared = 0;
-};
-
-// Entries [fblk, fblk + nent) of sequence s, staged unless the cached window
-// holds them; returns the LDS address of entry fblk and sets `nshared` to the
-// number of leading entries from fblk that are shared with a neighbour.
-template <int BS, bool SPLIT>
-__device__ __forceinline__ int32_t* staged_window(const DecodeArgs& a, int32_t* tbl, TblCache& tc,
-                                                  const TableView& row, int s, int fblk, int nent, int lane,
-                                                  int& nshared) {
-  if (!(tc.s == s && tc.first <= fblk && fblk + nent <= tc.first + tc.count)) {
-    tc.shared = stage_table_wave<BS, SPLIT>(tbl, a, row, s, fblk, nent, lane);
-    tc.s = s;
-    tc.first = fblk;
-    tc.count = nent;
-  }
-  nshared = min(max(tc.shared - (fblk - tc.first), 0), nent);
-  return tbl + (fblk - tc.first);
-}
-
-// Tiles of a window of nent blocks (starting off0 tokens into its first
-// block) that lie wholly in its first nshared blocks: all of them when every
-// block is shared.
-template <int BS>
-__device__ __forceinline__ int shared_tiles(int nshared, int nent, int off0, int ntiles) {
-  if (nshared >= nent) return ntiles;
-  const int t = (nshared * BS - off0) / kTile;
-  return t < 0 ? 0 : (t > ntiles ? ntiles : t);
-}
-
-using PolicyDefault = std::integral_constant<int, kAuxDefault>;
-using PolicyStream = std::integral_constant<int, kStreamAux>;
-
-// Walk tiles 0 .. ntiles-1 keeping the next NB-1 tiles' K/V loads in flight
-// while the current one is computed.  The loop runs over NB tiles at a time
-// with a ring of NB buffers and has a single exit, so that no path (not even
-// a structurized, never-taken one) returns to the loop head with the
-// prefetches outstanding; that lets the compiler's vmcnt waits leave the newer
-// loads in flight.  Loads are unconditional: a prefetch past the last tile
-// re-reads it (an L2 hit) instead of branching.  After the loop fewer than NB
-// tiles remain, and they are exactly the ones already in buf[0 ..].
-template <class Buf, int NB = 2, class Load, class Compute>
-__device__ __forceinline__ void tile_loop(int ntiles, Load&& load, Compute&& compute) {
-  static_assert(NB >= 2, "ring");
-  if (ntiles <= 0) return;
-  const int last = ntiles - 1;
-  Buf buf[NB];
-#pragma unroll
-  for (int j = 0; j + 1 < NB; ++j) load(min(j, last), buf[j]);
-  int ti = 0;
-  for (; ti + NB <= ntiles; ti += NB) {
-#pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      load(min(ti + j + NB - 1, last), buf[(j + NB - 1) % NB]);
-      compute(ti + j, buf[j]);
-    }
-  }
-#pragma unroll
-  for (int j = 0; j + 1 < NB; ++j)
-    if (ti + j < ntiles) compute(ti + j, buf[j]);
-}
-
-// Tiles [0, nsh) of a window with the default cache policy, then tiles
-// [nsh, ntiles) with the non-temporal one: two loops, so that every load of a
-// loop has a fixed policy and nothing but the loop's own exit separates a
-// prefetch from its use.  SPLIT is false for unit-mode kernels: one loop, all
-// tiles under the default policy.
-template <class Buf, bool SPLIT, class Load, class Compute>
-__device__ __forceinline__ void run_window(int ntiles, int nsh, Load& load, Compute& compute) {
-  if constexpr (!SPLIT) {   // unit mode: one loop, default policy
-    tile_loop<Buf, kRing>(ntiles, [&](int ti, Buf& b) { load(PolicyDefault{}, ti, b); }, compute);
-    return;
-  }
-  if (nsh > 0)
-    tile_loop<Buf, kRing>(nsh, [&](int ti, Buf& b) { load(PolicyDefault{}, ti, b); },
-                          [&](int ti, const Buf& b) { compute(ti, b); });
-  tile_loop<Buf, kRing>(ntiles - nsh, [&](int ti, Buf& b) { load(PolicyStream{}, nsh + ti, b); },
-                        [&](int ti, const Buf& b) { compute(nsh + ti, b); });
-}
-
-// Byte offsets, from the start of a KV head's slice of the pool, of the
-// 16-token tile that starts `rel` tokens after the first staged block.  The
-// block id is wave-uniform, so the offsets live in SGPRs and each lane adds a
-// constant 32-bit offset: no per-lane address arithmetic on the tile path.
-// With block_size >= 16 the tile lies in one block (lo == hi); with 8 its
-// tokens [8, 16) are in the next block, which may be past the window's last
-// staged entry only when every one of those tokens is masked (then lo is
-// reused).
-template <int BS, int ROWB>
-__device__ __forceinline__ void tile_offsets(const int32_t* tbl, int rel, int nent, size_t blk_stride,
-                                             size_t& lo, size_t& hi) {
-  if constexpr (BS >= 16) {
-    const int b = __builtin_amdgcn_readfirstlane(tbl[rel / BS]);
-    lo = hi = (size_t)b * blk_stride + (size_t)(rel % BS) * ROWB;
-  } else {
-    const int e = rel / BS;
-    const int b0 = __builtin_amdgcn_readfirstlane(tbl[e]);
-    const int b1 = e + 1 < nent ? __builtin_amdgcn_readfirstlane(tbl[e + 1]) : b0;
-    lo = (size_t)b0 * blk_stride;
-    hi = (size_t)b1 * blk_stride;
-  }
-}
-
-// Where a segment's result goes: the output rows (direct) or partial rows
-// prow0 + hh * pstride of the workspace (m, l, un-normalised acc).
-struct Dest {
-  bool direct;
-  size_t prow0, pstride;
-};
-
-// Write n consecutive results of head row `orow`, starting at element d0.
-template <class T, int N>
-__device__ __forceinline__ void emit_chunk(const DecodeArgs& a, const Dest& dst, size_t orow, int hh,
-                                           int d0, int D, const float* acc, float l) {
-  if (dst.direct) {
-    const float inv = 1.f / l;
-#pragma unroll
-    for (int e = 0; e < N; ++e) store_elem<T>(a.out, orow * D + d0 + e, acc[e] * inv);
-  } else {
-    const size_t pr = dst.prow0 + (size_t)hh * dst.pstride;
-#pragma unroll
-    for (int e = 0; e < N; ++e) a.ws_o[pr * D + d0 + e] = acc[e];
-  }
-}
-
-__device__ __forceinline__ void emit_ml(const DecodeArgs& a, const Dest& dst, int hh, float m, float l) {
-  if (!dst.direct) {
-    const size_t pr = dst.prow0 + (size_t)hh * dst.pstride;
-    a.ws_m[pr] = m;
-    a.ws_l[pr] = l;
-  }
-}
-
-template <class T, int D, int H>
-__device__ __forceinline__ void store_zero_rows(const DecodeArgs& a, int s, int h0, int lane) {
-  for (int idx = lane; idx < H * D; idx += kWave)
-    store_elem<T>(a.out, ((size_t)s * a.num_q_heads + h0) * D + idx, 0.f);
-}
-
-// ============================================================================
-// VALU core: any dtype, H q heads (1, 2 or 4) of one KV head.
-// Lane layout per tile: token slot tt = lane / 4, quarter qp = lane % 4; the
-// lane holds the row bytes [16 (4 j + qp), +16) for j < NL, i.e. D/4
-// elements.  QK^T: v_dot2c_f32_{f16,bf16} (fp32 FMA for fp32) in four
-// independent chains, then a quad sum; P.V: v_fma_mix_f32 for fp16, fp32 FMAs
-// otherwise.  Each token slot keeps its own running max, sum and accumulator,
-// so the tile loop needs no cross-lane reduction beyond the quad's dot sum;
-// the slots are merged with the log-sum-exp rule at the end of the segment.
-// ============================================================================
-template <int NL>
-struct ValuBuf {
-  u32x4 k[NL], v[NL];
-};
-
-// Resident workgroups per CU of the VALU core's balanced grid (0: as many as
-// its resources allow, 3 for MHA fp16).  One was 2.6 % faster than three on
-// the OPT-13B-shaped MHA batch: fewer, longer ranges pay fewer segment starts.
-#ifndef PA_VALU_WG_PER_CU
-#define PA_VALU_WG_PER_CU 1
-#endif
-template <class T, int D, int BS, int H>
-struct ValuCore {
-  static constexpr int EB = T::bytes;
-  static constexpr int ROWB = D * EB;
-  static constexpr int NL = ROWB / 64;    // 16-byte loads per lane per token row
-  static constexpr int NE = 16 / EB;      // elements per 16 bytes
-  static constexpr int DPL = NL * NE;     // elements per lane (= D / 4)
-  static constexpr int HEADS = H;
-  static constexpr int kBalancedWgPerCu = PA_VALU_WG_PER_CU;
-  static_assert(DPL * 4 == D, "layout");
-  static_assert(kTblWin * BS % kTile == 0, "window");
-  // bytes a tile's buffer resource spans: its 16 rows (8 per block at block_size 8)
-  static constexpr uint32_t kTileBytes = (BS >= 16 ? kTile : BS) * ROWB;
-
-  // q heads h0 .. h0+H-1 of sequence s over tokens [tok0, tok1), run by one
-  // wave; tbl is the wave's LDS window.
-  template <bool SPLIT>
-  __device__ static void run(const DecodeArgs& a, int32_t* tbl_lds, TblCache& tc, int s, int h0, int tok0,
-                             int tok1, const Dest& dst) {
-    const int lane = threadIdx.x & (kWave - 1);
-    const int G = a.num_q_heads / a.num_kv_heads;
-    const int g = h0 / G;
-    const int tt = lane >> 2, qp = lane & 3;
-
-    u32x4 qraw[H][NL];  // the lane's D/4 query elements of each head, as stored
-#pragma unroll
-    for (int hh = 0; hh < H; ++hh) {
-      const char* qrow = reinterpret_cast<const char*>(a.query) +
-                         ((size_t)s * a.num_q_heads + h0 + hh) * ROWB + qp * 16;
-#pragma unroll
-      for (int j = 0; j < NL; ++j) qraw[hh][j] = ld16(qrow + j * 64);
-    }
-    float m_run[H], l_run[H], acc[H][DPL];
-#pragma unroll
-    for (int hh = 0; hh < H; ++hh) {
-      m_run[hh] = kNegInf;
-      l_run[hh] = 0.f;
-#pragma unroll
-      for (int i = 0; i < DPL; ++i) acc[hh][i] = 0.f;
-    }
-
-    const char* kbase = reinterpret_cast<const char*>(a.k_pool) + (size_t)g * BS * ROWB;
-    const char* vbase = reinterpret_cast<const char*>(a.v_pool) + (size_t)g * BS * ROWB;
-    const size_t blk_stride = (size_t)a.num_kv_heads * BS * ROWB;
-    const TableView trow = table_view(a, s);
-    // lane's row within the tile's block region, and which block (block_size 8)
-    const uint32_t lane_off = (uint32_t)((BS >= 16 ? tt : (tt & 7)) * ROWB + qp * 16);
-    const bool hi_blk = BS < 16 && tt >= 8;
-
-    // windows of at most kTblWin blocks; a segment may start inside a block
-    // (balanced mode, block_size 32): off0 is that start within its block
-    for (int wb = tok0; wb < tok1;) {
-      const int fblk = wb / BS;
-      const int off0 = wb - fblk * BS;
-      const int we = min((fblk + kTblWin) * BS, tok1);
-      const int nent = (we - 1) / BS - fblk + 1;
-      int nshared;
-      const int32_t* tbl = staged_window<BS, SPLIT>(a, tbl_lds, tc, trow, s, fblk, nent, lane, nshared);
-
-      auto load = [&](auto pol, int ti, ValuBuf<NL>& buf) {
-        constexpr int AUX = decltype(pol)::value;
-        size_t lo, hi;
-        tile_offsets<BS, ROWB>(tbl, off0 + ti * kTile, nent, blk_stride, lo, hi);
-        if constexpr (BS >= 16) {  // one block region: SGPR base + lane offset
-          const rsrc_t rk = make_rsrc(kbase + lo, kTileBytes);
-          const rsrc_t rv = make_rsrc(vbase + lo, kTileBytes);
-#pragma unroll
-          for (int j = 0; j < NL; ++j) buf.k[j] = buf_ld16_aux<AUX>(rk, lane_off + j * 64);
-#pragma unroll
-          for (int j = 0; j < NL; ++j) buf.v[j] = buf_ld16_aux<AUX>(rv, lane_off + j * 64);
-        } else {  // block_size 8: tokens 8..15 come from the next block
-          const size_t off = (hi_blk ? hi : lo) + lane_off;
-#pragma unroll
-          for (int j = 0; j < NL; ++j) buf.k[j] = ld16_aux<AUX>(kbase + off + j * 64);
-#pragma unroll
-          for (int j = 0; j < NL; ++j) buf.v[j] = ld16_aux<AUX>(vbase + off + j * 64);
-        }
-      };
-      auto compute = [&](int ti, const ValuBuf<NL>& buf) {
-        const bool valid = wb + ti * kTile + tt < we;
-        float pr[H];
-#pragma unroll
-        for (int hh = 0; hh < H; ++hh) {
-          float d[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int j = 0; j < NL; ++j) Dot16<T>::run(qraw[hh][j], buf.k[j], d);
-          float dot = (d[0] + d[1]) + (d[2] + d[3]);
-          dot += xor_lane<1>(dot);
-          dot += xor_lane<2>(dot);
-          const float sc = valid ? dot * a.scale_log2 : kNegInf;
-          const bool grow = sc > m_run[hh] + kLazy;   // true for a slot's first token
-          if (__any(grow)) {
-            const float m_new = grow ? sc : m_run[hh];
-            const float alpha = grow ? fast_exp2(m_run[hh] - m_new) : 1.f;
-            l_run[hh] *= alpha;
-#pragma unroll
-            for (int i = 0; i < DPL; ++i) acc[hh][i] *= alpha;
-            m_run[hh] = m_new;
-          }
-          pr[hh] = valid ? fast_exp2(sc - m_run[hh]) : 0.f;
-          l_run[hh] += pr[hh];
-        }
-#pragma unroll
-        for (int j = 0; j < NL; ++j) {
-          const u32x4 z = {0u, 0u, 0u, 0u};
-          const u32x4 vj = valid ? buf.v[j] : z;   // tail slots may hold NaN
-#pragma unroll
-          for (int hh = 0; hh < H; ++hh) Axpy16<T>::run(pr[hh], vj, &acc[hh][j * NE]);
-        }
-      };
-      const int ntiles = (we - wb + kTile - 1) / kTile;
-      run_window<ValuBuf<NL>, SPLIT>(ntiles, shared_tiles<BS>(nshared, nent, off0, ntiles), load, compute);
-      wb = we;
-    }
-
-    // merge the 16 token slots (lanes with equal qp): rescale to the common
-    // max, then sum; slots that saw no token have m = -inf and weigh 0
-#pragma unroll
-    for (int hh = 0; hh < H; ++hh) {
-      float M = m_run[hh];
-      M = fmaxf(M, xor_lane<4>(M));
-      M = fmaxf(M, xor_lane<8>(M));
-      M = fmaxf(M, xor_lane<16>(M));
-      M = fmaxf(M, xor_lane<32>(M));
-      const float f = m_run[hh] == kNegInf ? 0.f : fast_exp2(m_run[hh] - M);
-      float l = l_run[hh] * f;
-      l += xor_lane<4>(l);
-      l += xor_lane<8>(l);
-      l += xor_lane<16>(l);
-      l += xor_lane<32>(l);
-#pragma unroll
-      for (int i = 0; i < DPL; ++i) {
-        float x = acc[hh][i] * f;
-        x += xor_lane<4>(x);
-        x += xor_lane<8>(x);
-        x += xor_lane<16>(x);
-        x += xor_lane<32>(x);
-        acc[hh][i] = x;
-      }
-      const size_t orow = (size_t)s * a.num_q_heads + h0 + hh;
-      if (tt == 0) {  // lanes 0..3 hold the whole row
-#pragma unroll
-        for (int j = 0; j < NL; ++j)
-          emit_chunk<T, NE>(a, dst, orow, hh, (4 * j + qp) * NE, D, &acc[hh][j * NE], l);
-      }
-      if (lane == 0) emit_ml(a, dst, hh, M, l);
-    }
-  }
-};
-
-// ============================================================================
-// MFMA core for grouped queries (f16/bf16, G = Hq/Hkv in {2, 4, 8, 16}).
-//
-// Scores of a 16-token tile: S^T[t][n] = sum_d K[t][d] Q[n % G][d] with
-// v_mfma_f32_16x16x32_{bf16,f16}: A = the K tile (row m = token, loaded
-// straight from HBM, 16 bytes per lane), B = the G query rows replicated
-// 16/G times across the 16 columns.  The contraction order over d is free as
-// long as A and B agree, so lane (gr = lane/16, w = lane%16) feeds chunk
-// 4i + gr of token w to MFMA i: every load instruction reads 64 contiguous
-// bytes of 16 token rows.  The result lands as S[token 4 gr + r][head w % G],
-// r = 0..3, in every lane -- the same 4 tokens that the lane's V loads cover.
-// P.V stays on the VALU in fp32: each lane holds one 16-byte chunk of d for
-// its tokens, fetches p of the other heads from its quad (DPP) or row, and
-// accumulates G x 8 fp32 values.  Each row gr keeps its own running max per
-// head (no cross-row reduction per tile); rows merge at the end.
-// ============================================================================
-template <class T, int G>
-__device__ __forceinline__ float bcast_head(float x, int h, int lane) {
-  if constexpr (G <= 4) {
-    switch (h) {
-      case 0: return quad_bcast<0>(x);
-      case 1: return quad_bcast<1>(x);
-      case 2: return quad_bcast<2>(x);
-      default: return quad_bcast<3>(x);
-    }
-  } else {
-    return __shfl(x, (lane & ~15) + h, kWave);
-  }
-}
-
-template <int NQK, int NVI>
-struct MfmaBuf {
-  u32x4 k[NQK], v[NVI];
-};
-
-#ifndef PA_MFMA_WG_PER_CU
-#define PA_MFMA_WG_PER_CU 1
-#endif
-template <class T, int D, int BS, int G>
-struct MfmaCore {
-  static constexpr int ROWB = D * 2;
-  static constexpr int NQK = D / 32;   // MFMAs per tile (k = 32 per MFMA)
-  static constexpr int CPR = D / 8;    // 16-byte chunks per token row
-  static constexpr int NVI = D / 32;   // V chunks per lane per tile (16 * CPR / 64)
-  static constexpr int HEADS = G;
-  // Balanced grid: one workgroup per CU.  With 8 KiB tiles and one tile
-  // prefetched per wave, more resident waves only add concurrent streams: on
-  // the Llama-3-8B-shaped batch 1 workgroup per CU streamed 1-2 % faster than
-  // 2 or 3, and equal on the long-context batch.
-  static constexpr int kBalancedWgPerCu = PA_MFMA_WG_PER_CU;
-  static_assert(16 % G == 0 && G >= 2, "group");
-  static_assert(kTblWin * BS % kTile == 0, "window");
-  static constexpr uint32_t kTileBytes = (BS >= 16 ? kTile : BS) * ROWB;
-
-  // the G q heads h0 .. h0+G-1 (KV head h0 / G) of sequence s over tokens
-  // [tok0, tok1), run by one wave; tbl is the wave's LDS window.
-  template <bool SPLIT>
-  __device__ static void run(const DecodeArgs& a, int32_t* tbl_lds, TblCache& tc, int s, int h0, int tok0,
-                             int tok1, const Dest& dst) {
-    const int lane = threadIdx.x & (kWave - 1);
-    const int gr = lane >> 4, w = lane & 15;
-    const int g = h0 / G;
-
-    u32x4 qop[NQK];  // B operand: query row of head w % G, chunk 4 i + gr
-    {
-      const char* qrow = reinterpret_cast<const char*>(a.query) +
-                         ((size_t)s * a.num_q_heads + h0 + (w % G)) * ROWB;
-#pragma unroll
-      for (int i = 0; i < NQK; ++i) qop[i] = ld16(qrow + (4 * i + gr) * 16);
-    }
-    float m_run = kNegInf, l_run = 0.f;  // head w % G, tokens of row gr
-    float acc[G][8];                     // row gr, d = 8 * (w % CPR) + e
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
-
-    const char* kbase = reinterpret_cast<const char*>(a.k_pool) + (size_t)g * BS * ROWB;
-    const char* vbase = reinterpret_cast<const char*>(a.v_pool) + (size_t)g * BS * ROWB;
-    const size_t blk_stride = (size_t)a.num_kv_heads * BS * ROWB;
-    const TableView trow = table_view(a, s);
-    // K: token w of the tile, chunk 4 i + gr (i = instruction);
-    // V: token 4 gr + w / CPR + 16 j / CPR, chunk w % CPR (j = instruction)
-    const int tv0 = 4 * gr + w / CPR;
-    const uint32_t k_off = (uint32_t)((BS >= 16 ? w : (w & 7)) * ROWB + gr * 16);
-    const uint32_t v_off = (uint32_t)((BS >= 16 ? tv0 : (tv0 & 7)) * ROWB + (w % CPR) * 16);
-    const bool k_hi = BS < 16 && w >= 8;
-    const bool v_hi = BS < 16 && gr >= 2;
-
-    for (int wb = tok0; wb < tok1;) {
-      const int fblk = wb / BS;
-      const int off0 = wb - fblk * BS;
-      const int we = min((fblk + kTblWin) * BS, tok1);
-      const int nent = (we - 1) / BS - fblk + 1;
-      int nshared;
-      const int32_t* tbl = staged_window<BS, SPLIT>(a, tbl_lds, tc, trow, s, fblk, nent, lane, nshared);
-
-      auto load = [&](auto pol, int ti, MfmaBuf<NQK, NVI>& buf) {
-        constexpr int AUX = decltype(pol)::value;
-        size_t lo, hi;
-        tile_offsets<BS, ROWB>(tbl, off0 + ti * kTile, nent, blk_stride, lo, hi);
-        if constexpr (BS >= 16) {  // one block region: SGPR base + lane offset
-          const rsrc_t rk = make_rsrc(kbase + lo, kTileBytes);
-          const rsrc_t rv = make_rsrc(vbase + lo, kTileBytes);
-#pragma unroll
-          for (int i = 0; i < NQK; ++i) buf.k[i] = buf_ld16_aux<AUX>(rk, k_off + i * 64);
-#pragma unroll
-          for (int j = 0; j < NVI; ++j) buf.v[j] = buf_ld16_aux<AUX>(rv, v_off + (16 * j / CPR) * ROWB);
-        } else {  // block_size 8: tokens 8..15 come from the next block
-          const char* kb = kbase + (k_hi ? hi : lo) + k_off;
-          const char* vb = vbase + (v_hi ? hi : lo) + v_off;
-#pragma unroll
-          for (int i = 0; i < NQK; ++i) buf.k[i] = ld16_aux<AUX>(kb + i * 64);
-#pragma unroll
-          for (int j = 0; j < NVI; ++j) buf.v[j] = ld16_aux<AUX>(vb + (16 * j / CPR) * ROWB);
-        }
-      };
-      auto compute = [&](int ti, const MfmaBuf<NQK, NVI>& buf) {
-        const int ts = wb + ti * kTile;
-        f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int i = 0; i < NQK; ++i) sacc = mfma_16x16x32<T>(buf.k[i], qop[i], sacc);
-
-        float sc[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) sc[r] = (ts + 4 * gr + r < we) ? sacc[r] * a.scale_log2 : kNegInf;
-        const float tmax = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
-        const bool grow = tmax > m_run + kLazy;   // true for the row's first valid token
-        if (__any(grow)) {
-          const float m_new = grow ? tmax : m_run;
-          const float alpha = grow ? fast_exp2(m_run - m_new) : 1.f;
-          m_run = m_new;
-          l_run *= alpha;
-#pragma unroll
-          for (int h = 0; h < G; ++h) {
-            const float ah = bcast_head<T, G>(alpha, h, lane);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc[h][e] *= ah;
-          }
-        }
-        float pr[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          pr[r] = sc[r] == kNegInf ? 0.f : fast_exp2(sc[r] - m_run);
-          l_run += pr[r];
-        }
-#pragma unroll
-        for (int j = 0; j < NVI; ++j) {
-          const int idx = w + 16 * j;
-          const int rt = idx / CPR;   // token of the group: uniform for D = 128
-          const bool vvalid = ts + 4 * gr + rt < we;
-          const u32x4 z = {0u, 0u, 0u, 0u};
-          const u32x4 vj = vvalid ? buf.v[j] : z;   // tail slots may hold NaN
-          float vf[8];
-          Unpack<T>::run(vj, vf);
-#pragma unroll
-          for (int h = 0; h < G; ++h) {
-            float ph;
-            if constexpr (CPR == 16) {
-              ph = bcast_head<T, G>(pr[j], h, lane);
-            } else {  // D = 64: rows hold two tokens of the group, lanes w < 8 and w >= 8
-              const float pa_ = bcast_head<T, G>(pr[2 * j], h, lane);
-              const float pb_ = bcast_head<T, G>(pr[2 * j + 1], h, lane);
-              ph = (w < 8) ? pa_ : pb_;
-            }
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(ph, vf[e], acc[h][e]);
-          }
-        }
-      };
-      const int ntiles = (we - wb + kTile - 1) / kTile;
-      run_window<MfmaBuf<NQK, NVI>, SPLIT>(ntiles, shared_tiles<BS>(nshared, nent, off0, ntiles), load, compute);
-      wb = we;
-    }
-
-    // merge the four rows: rescale each to the head's common max, then sum
-    float M = m_run;
-    M = fmaxf(M, xor_lane<16>(M));
-    M = fmaxf(M, xor_lane<32>(M));
-    const float f = m_run == kNegInf ? 0.f : fast_exp2(m_run - M);
-    float l = l_run * f;
-    l += xor_lane<16>(l);
-    l += xor_lane<32>(l);
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float fh = bcast_head<T, G>(f, h, lane);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float x = acc[h][e] * fh;
-        if constexpr (CPR == 8) x += xor_lane<8>(x);
-        x += xor_lane<16>(x);
-        x += xor_lane<32>(x);
-        acc[h][e] = x;
-      }
-    }
-    // every row now holds all sums; row gr writes the heads h with h % 4 == gr
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float lh = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(l), h));
-      const float mh = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(M), h));
-      const size_t orow = (size_t)s * a.num_q_heads + h0 + h;
-      if (gr == (h & 3) && w < CPR) emit_chunk<T, 8>(a, dst, orow, h, 8 * w, D, acc[h], lh);
-      if (lane == 0) emit_ml(a, dst, h, mh, lh);
-    }
-  }
-};
-
-// ============================================================================
-// Unit-mode kernel: wave = (sequence, head group, partition), sequence the
-// fastest index.  xcd_unit spreads runs of neighbouring workgroups over the
-// XCDs.
-// ============================================================================
-template <class Core, class T, int D, int NW>
-__global__ __launch_bounds__(NW * kWave) void decode_unit_kernel(DecodeArgs a, int block_size) {
-  constexpr int H = Core::HEADS;
-  __shared__ int32_t s_tbl[NW][kTblWin];
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const uint32_t u = xcd_unit(blockIdx.x, gridDim.x) * NW + wave;
-  const int S = a.num_seqs, C = a.head_chunks;
-  if (u >= (uint32_t)S * C * a.num_parts) return;
-  const int s = (int)(u % (uint32_t)S);
-  const uint32_t rest = u / (uint32_t)S;
-  const int c = (int)(rest % (uint32_t)C);
-  const int p = (int)(rest / (uint32_t)C);
-  const int h0 = c * H;
-  const int L = clamp_len(a, s, block_size);
-  const int P = a.partition_size;
-  const int t0 = p * P;
-  if (L == 0) {
-    if (p == 0) store_zero_rows<T, D, H>(a, s, h0, lane);
-    return;
-  }
-  if (t0 >= L) return;
-  const int t1 = min(t0 + P, L);
-  // partial rows: (s, h, p) -> ((s * Hq + h) * NP + p)
-  const Dest dst{!a.split || L <= P, ((size_t)s * a.num_q_heads + h0) * a.num_parts + p,
-                 (size_t)a.num_parts};
-  TblCache tc;
-  Core::template run<false>(a, s_tbl[wave], tc, s, h0, t0, t1, dst);
-}
-
-// ============================================================================
-// Balanced-mode kernel.  Flattened space: each (sequence, head group) with
-// nt = ceil(L_s / 16) > 0 tiles costs X + nt units -- X for starting a
-// segment (its query, its first tiles' latency, its epilogue), then its
-// tiles -- so sequence s owns [C cum[s], C cum[s+1]) with cum the prefix of
-// C (X + nt) and head groups major.  Of ntot units, wave w of W takes
-// [w ntot / W, (w+1) ntot / W): waves whose range holds many short segments
-// get fewer tiles, and all finish together.  A (sequence, head group) whose
-// tiles all fall in one range is written directly; the first and the last
-// segment of a range, when they are pieces of a larger one, go to partial
-// slots 2w and 2w+1 (H rows each).  Each XCD gets a contiguous run of waves
-// (so samples sharing a prompt's blocks meet in one L2); workgroup 0 also
-// stores cum for the merge.
-// ============================================================================
-#ifndef PA_SEG_COST
-#define PA_SEG_COST 3
-#endif
-// Segment start cost in tiles: on a Llama-3-8B-shaped batch, equal-byte runs
-// at 1K and 8K tokens per sequence put a segment start at about 3 tiles.
-constexpr int kSegCost = PA_SEG_COST;
-__device__ __forceinline__ int64_t range_start(int64_t w, int64_t ntot, int64_t W) {
-  return w * ntot / W;
-}
-
-// Workgroup b runs on XCD b % 8: give XCD x the contiguous logical range
-// [x q + min(x, r), ...) of the n workgroups (q = n / 8, r = n % 8).
-__device__ __forceinline__ uint32_t xcd_contiguous(uint32_t b, uint32_t n) {
-  const uint32_t q = n / kNumXcd, r = n % kNumXcd;
-  const uint32_t x = b % kNumXcd, k = b / kNumXcd;
-  return x * q + (x < r ? x : r) + k;
-}
-
-template <int NT>
-__device__ __forceinline__ void tile_prefix(const DecodeArgs& a, int block_size, int32_t* s_cum,
-                                            int32_t* s_wave) {
-  // s_cum[s] = sum_{s' < s} cost(s'), cost = X + ceil(L / 16) (0 for an
-  // empty sequence), s = 0..S: each thread sums a contiguous run of
-  // sequences, then the runs are offset by a shuffle scan within each wave
-  // and the totals of the waves before it
-  static_assert(NT % kWave == 0, "whole waves");
-  const int S = a.num_seqs;
-  const int per = (S + NT - 1) / NT;
-  const int lo = threadIdx.x * per, hi = min(lo + per, S);
-  int sum = 0;
-  for (int s = lo; s < hi; ++s) {
-    const int nt = (clamp_len(a, s, block_size) + kTile - 1) / kTile;
-    s_cum[s] = sum;   // local exclusive prefix, offset below
-    sum += nt > 0 ? nt + kSegCost : 0;
-  }
-  const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
-  int x = sum;   // inclusive scan over the wave's lanes
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const int y = __shfl_up(x, o, kWave);
-    if (lane >= o) x += y;
-  }
-  if (lane == kWave - 1) s_wave[wv] = x;
-  __syncthreads();
-  int base = x - sum, total = 0;
-#pragma unroll
-  for (int i = 0; i < NT / kWave; ++i) {
-    const int t = s_wave[i];
-    base += i < wv ? t : 0;
-    total += t;
-  }
-  for (int s = lo; s < hi; ++s) s_cum[s] += base;
-  if (threadIdx.x == 0) s_cum[S] = total;
-  __syncthreads();
-}
-
-template <class Core, class T, int D, int NW>
-__global__ __launch_bounds__(NW * kWave) void decode_balanced_kernel(DecodeArgs a, int block_size) {
-  constexpr int H = Core::HEADS;
-  __shared__ int32_t s_cum[kBalancedMaxSeqs + 1];
-  __shared__ int32_t s_wave[NW];
-  __shared__ int32_t s_tbl[NW][kTblWin];
-  const int S = a.num_seqs, C = a.head_chunks;
-  tile_prefix<NW * kWave>(a, block_size, s_cum, s_wave);
-  if (blockIdx.x == 0)
-    for (int s = threadIdx.x; s <= S; s += NW * kWave) a.ws_cum[s] = s_cum[s];
-  // sequences with no tile own no range: their rows are zeros, written here
-  for (int s = blockIdx.x; s < S; s += gridDim.x)
-    if (s_cum[s + 1] == s_cum[s])
-      for (int idx = threadIdx.x; idx < a.num_q_heads * D; idx += NW * kWave)
-        store_elem<T>(a.out, (size_t)s * a.num_q_heads * D + idx, 0.f);
-
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int64_t W = (int64_t)gridDim.x * NW;
-  const int64_t w = (int64_t)xcd_contiguous(blockIdx.x, gridDim.x) * NW + wave;
-  const int64_t ntot = (int64_t)C * s_cum[S];
-  int64_t f = range_start(w, ntot, W);
-  const int64_t fb = range_start(w + 1, ntot, W);
-  if (f >= fb) return;
-  // the sequence holding tile f: the last s with C cum[s] <= f (empty
-  // sequences share their successor's cum and are skipped)
-  int lo = 0, hi = S - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if ((int64_t)C * s_cum[mid] <= f) lo = mid; else hi = mid - 1;
-  }
-  int s = lo;
-  int ntc = s_cum[s + 1] - s_cum[s];        // cost of one head group of s: X + nt
-  const int64_t rel = f - (int64_t)C * s_cum[s];
-  int c = (int)(rel / ntc);
-  int u = (int)(rel - (int64_t)c * ntc);    // position within that cost
-  bool first = true;
-  TblCache tc;
-  while (f < fb) {
-    const int n = (int)min((int64_t)(ntc - u), fb - f);
-    const int nt = ntc - kSegCost;
-    const int t0 = max(u - kSegCost, 0), t1 = min(u + n - kSegCost, nt);
-    if (t1 > t0) {   // the range holds real tiles of this head group
-      const int L = clamp_len(a, s, block_size);
-      const int tok0 = t0 * kTile, tok1 = min(t1 * kTile, L);
-      const size_t slot = 2 * (size_t)w + (first ? 0 : 1);
-      const Dest dst{t0 == 0 && t1 == nt, slot * H, 1};
-      Core::template run<true>(a, s_tbl[wave], tc, s, c * H, tok0, tok1, dst);
-      first = false;
-    }
-    f += n;
-    u += n;
-    if (u == ntc && f < fb) {  // next head group, or the next sequence with tiles
-      u = 0;
-      if (++c == C) {
-        c = 0;
-        do {
-          ++s;
-        } while (s_cum[s + 1] == s_cum[s]);
-      }
-      ntc = s_cum[s + 1] - s_cum[s];
-    }
-  }
-}
-
-// ============================================================================
-// Merges.  Partition mode, per (sequence, q head): M = max_p m_p,
-// w_p = 2^(m_p - M), out = sum_p w_p o_p / sum_p w_p l_p (o_p un-normalised).
-// One wave per row: lane p reads (m_p, l_p) for 64 partitions at a time; the
-// lanes then walk the partitions with the weight read from lane j, each lane
-// accumulating D/64 output elements, loads unrolled for memory parallelism.
-// ============================================================================
-template <class T, int D>
-__global__ __launch_bounds__(kWave) void decode_merge_parts_kernel(DecodeArgs a, int block_size) {
-  constexpr int EPL = D / kWave;            // output elements per lane
-  const int row = blockIdx.x;               // s * Hq + h
-  const int s = row / a.num_q_heads;
-  const int lane = threadIdx.x;
-  const int L = clamp_len(a, s, block_size);
-  const int P = a.partition_size;
-  const int np = (L + P - 1) / P;
-  if (np <= 1) return;                      // written directly by the partition pass
-  const size_t base = (size_t)row * a.num_parts;
-  float M = kNegInf;
-  for (int p = lane; p < np; p += kWave) M = fmaxf(M, a.ws_m[base + p]);
-  M = fmaxf(M, xor_lane<1>(M));
-  M = fmaxf(M, xor_lane<2>(M));
-  M = fmaxf(M, xor_lane<4>(M));
-  M = fmaxf(M, xor_lane<8>(M));
-  M = fmaxf(M, xor_lane<16>(M));
-  M = fmaxf(M, xor_lane<32>(M));
-  float den = 0.f, num[EPL];
-#pragma unroll
-  for (int e = 0; e < EPL; ++e) num[e] = 0.f;
-  for (int p0 = 0; p0 < np; p0 += kWave) {
-    const int p = p0 + lane;
-    const float wgt = p < np ? fast_exp2(a.ws_m[base + p] - M) : 0.f;
-    den = p < np ? fmaf(wgt, a.ws_l[base + p], den) : den;
-    const int cnt = min(kWave, np - p0);
-    const float* o = a.ws_o + (base + p0) * D + lane;
-    int j = 0;
-    for (; j + 4 <= cnt; j += 4) {
-      float ov[4][EPL];
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) ov[u][e] = o[(size_t)(j + u) * D + e * kWave];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wgt), j + u));
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) num[e] = fmaf(wj, ov[u][e], num[e]);
-      }
-    }
-    for (; j < cnt; ++j) {
-      const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wgt), j));
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) num[e] = fmaf(wj, o[(size_t)j * D + e * kWave], num[e]);
-    }
-  }
-  den += xor_lane<1>(den);
-  den += xor_lane<2>(den);
-  den += xor_lane<4>(den);
-  den += xor_lane<8>(den);
-  den += xor_lane<16>(den);
-  den += xor_lane<32>(den);
-#pragma unroll
-  for (int e = 0; e < EPL; ++e) store_elem<T>(a.out, (size_t)row * D + e * kWave + lane, num[e] / den);
-}
-
-// Balanced mode: the head groups whose tiles were split between waves are
-// found from the wave boundaries.  Boundary w (1 <= w < W, at position
-// b = range_start(w) of the flattened space) merges the head group whose
-// tiles [A, B) it is the first to split: A < b < B and wave w - 1 holds A.
-// Head groups written whole need nothing, so the launch is sized by the
-// boundaries, however many sequences there are.  The waves that shared [A, B)
-// are w_lo = w - 1 .. w_hi; wave w left its piece in slot 2w + (its range
-// starts at or after the head group's cost start A0 = A - X ? 0 : 1), and
-// waves with an empty range wrote nothing.  Per head, lane p holds piece p
-// (64 at a time) for the max and the sum, then all lanes walk the pieces with
-// slot and weight read from lane j (loads unrolled by 8), each accumulating
-// D/64 outputs.  Lanes without a piece point at w_lo's piece (always written
-// in this call) with weight 0, so nothing left in the workspace by an earlier
-// call is read.
-constexpr int kMergeWaves = 4;
-// The H heads of a boundary's head group go to min(H, 4) waves of one
-// workgroup (each taking every min(H, 4)-th head), and a workgroup serves
-// 4 / min(H, 4) boundaries.
-template <int H>
-constexpr int kMergeHeadWaves = H < kMergeWaves ? H : kMergeWaves;
-template <int H>
-constexpr int kMergeBoundaries = kMergeWaves / kMergeHeadWaves<H>;
-
-// The last s in [0, S) with C cum[s] <= x (cum non-decreasing, cum[0] = 0 <=
-// x): two rounds of a 64-lane ballot for S <= 4096, from global memory.
-__device__ __forceinline__ int find_seq(const int32_t* cum, int S, int C, int64_t x, int lane) {
-  int base = 0, span = S;
-  while (span > 1) {
-    const int step = (span + kWave - 1) / kWave;
-    const int idx = base + lane * step;
-    const bool le = lane * step < span && (int64_t)C * cum[idx] <= x;
-    const int last = __popcll(__ballot(le)) - 1;   // the true lanes are a prefix
-    base += last * step;
-    span = min(step, span - last * step);
-  }
-  return base;
-}
-
-template <class T, int D, int H>
-__global__ __launch_bounds__(kMergeWaves * kWave) void decode_merge_balanced_kernel(DecodeArgs a,
-                                                                                   int block_size,
-                                                                                   int nwaves) {
-  constexpr int EPL = D / kWave;
-  const int C = a.head_chunks;
-  const int lane = threadIdx.x & (kWave - 1);
-  const int64_t W = nwaves;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  if (wave / kMergeHeadWaves<H> >= kMergeBoundaries<H>) return;
-  const int64_t w = (int64_t)blockIdx.x * kMergeBoundaries<H> + wave / kMergeHeadWaves<H>;
-  if (w < 1 || w >= W) return;
-  const int64_t ntot = (int64_t)C * a.ws_cum[a.num_seqs];
-  const int64_t b = range_start(w, ntot, W);
-  if (b <= 0 || b >= ntot) return;
-  const int s = __builtin_amdgcn_readfirstlane(find_seq(a.ws_cum, a.num_seqs, C, b - 1, lane));
-  const int ntc = a.ws_cum[s + 1] - a.ws_cum[s];
-  const int c = (int)((b - 1 - (int64_t)C * a.ws_cum[s]) / ntc);
-  const int64_t A0 = (int64_t)C * a.ws_cum[s] + (int64_t)c * ntc;
-  const int64_t A = A0 + kSegCost, B = A0 + ntc;
-  if (!(A < b && b < B && range_start(w - 1, ntot, W) <= A)) return;
-  const size_t orow = (size_t)s * a.num_q_heads + (size_t)c * H;
-  const int64_t w_lo = w - 1, w_hi = (B * W - 1) / ntot;
-  const int k = (int)(w_hi - w_lo + 1);
-  const int slot_lo = (int)(2 * w_lo + (range_start(w_lo, ntot, W) >= A0 ? 0 : 1));
-  auto piece_slot = [&](int p, bool& ok) {
-    const int64_t w = w_lo + p;
-    const int64_t ws = range_start(w, ntot, W);
-    ok = p < k && ws != range_start(w + 1, ntot, W);
-    return ok ? (int)(2 * w + (ws >= A0 ? 0 : 1)) : slot_lo;
-  };
-  for (int hh = wave % kMergeHeadWaves<H>; hh < H; hh += kMergeHeadWaves<H>) {
-    float M = kNegInf;
-    for (int p0 = 0; p0 < k; p0 += kWave) {
-      bool ok;
-      const int slot = piece_slot(p0 + lane, ok);
-      M = fmaxf(M, a.ws_m[(size_t)slot * H + hh]);
-    }
-    M = fmaxf(M, xor_lane<1>(M));
-    M = fmaxf(M, xor_lane<2>(M));
-    M = fmaxf(M, xor_lane<4>(M));
-    M = fmaxf(M, xor_lane<8>(M));
-    M = fmaxf(M, xor_lane<16>(M));
-    M = fmaxf(M, xor_lane<32>(M));
-    float den = 0.f, num[EPL];
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) num[e] = 0.f;
-    for (int p0 = 0; p0 < k; p0 += kWave) {
-      bool ok;
-      const int slot = piece_slot(p0 + lane, ok);
-      const float wgt = ok ? fast_exp2(a.ws_m[(size_t)slot * H + hh] - M) : 0.f;
-      den = fmaf(wgt, a.ws_l[(size_t)slot * H + hh], den);
-      const int cnt = min(kWave, k - p0);
-      constexpr int U = 8;
-      for (int j0 = 0; j0 < cnt; j0 += U) {
-        float ov[U][EPL];
-        float wj[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const int j = min(j0 + u, cnt - 1);
-          const int sj = __builtin_amdgcn_readlane(slot, j);
-          wj[u] = j0 + u < cnt ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wgt), j)) : 0.f;
-          const float* o = a.ws_o + ((size_t)sj * H + hh) * D + lane;
-#pragma unroll
-          for (int e = 0; e < EPL; ++e) ov[u][e] = o[e * kWave];
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-#pragma unroll
-          for (int e = 0; e < EPL; ++e) num[e] = fmaf(wj[u], ov[u][e], num[e]);
-      }
-    }
-    den += xor_lane<1>(den);
-    den += xor_lane<2>(den);
-    den += xor_lane<4>(den);
-    den += xor_lane<8>(den);
-    den += xor_lane<16>(den);
-    den += xor_lane<32>(den);
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) store_elem<T>(a.out, (orow + hh) * D + e * kWave + lane, num[e] / den);
-  }
-}
-
-// ============================================================================
-// dispatch
-// ============================================================================
-#ifndef PA_WAVES_PER_UNIT
-#define PA_WAVES_PER_UNIT 4
-#endif
-constexpr int kWavesPerGroup = PA_WAVES_PER_UNIT;
-
-template <class Core, class T, int D>
-static hipError_t run_core(const DecodeArgs& a, int bs, hipStream_t st) {
-  constexpr int NW = kWavesPerGroup;
-  constexpr int H = Core::HEADS;
-  if (a.mode == kModeBalanced) {
-    auto kern = decode_balanced_kernel<Core, T, D, NW>;
-    int nwg = 0;
-    hipError_t e = balanced_grid(reinterpret_cast<const void*>(kern), NW * kWave, Core::kBalancedWgPerCu,
-                                 kBalancedMaxWaves / NW, &nwg);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3(nwg), dim3(NW * kWave), 0, st, a, bs);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const uint32_t waves = (uint32_t)nwg * NW;
-    constexpr uint32_t BPW = kMergeBoundaries<H>;
-    hipLaunchKernelGGL((decode_merge_balanced_kernel<T, D, H>), dim3((waves + BPW - 1) / BPW),
-                       dim3(kMergeWaves * kWave), 0, st, a, bs, (int)waves);
-    return hipGetLastError();
-  }
-  const uint64_t units = (uint64_t)a.num_seqs * a.head_chunks * a.num_parts;
-  const uint32_t groups = (uint32_t)((units + NW - 1) / NW);
-  hipLaunchKernelGGL((decode_unit_kernel<Core, T, D, NW>), dim3(groups), dim3(NW * kWave), 0, st, a, bs);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || !a.split) return e;
-  hipLaunchKernelGGL((decode_merge_parts_kernel<T, D>), dim3((uint32_t)a.num_seqs * a.num_q_heads),
-                     dim3(kWave), 0, st, a, bs);
-  return hipGetLastError();
-}
-
-template <class T, int D, int BS>
-static hipError_t dispatch_bs(const DecodeArgs& a, int group, hipStream_t st) {
-  if constexpr (!std::is_same<T, F32>::value) {
-    switch (group) {
-      case 2: return run_core<MfmaCore<T, D, BS, 2>, T, D>(a, BS, st);
-      case 4: return run_core<MfmaCore<T, D, BS, 4>, T, D>(a, BS, st);
-      case 8: return run_core<MfmaCore<T, D, BS, 8>, T, D>(a, BS, st);
-      case 16: return run_core<MfmaCore<T, D, BS, 16>, T, D>(a, BS, st);
-      default: break;   // group 1: VALU
-    }
-  }
-  switch (a.num_q_heads / a.head_chunks) {
-    case 1: return run_core<ValuCore<T, D, BS, 1>, T, D>(a, BS, st);
-    default: break;
-  }
-  if constexpr (std::is_same<T, F32>::value) {  // fp32 groups: 2 or 4 heads per unit
-    switch (a.num_q_heads / a.head_chunks) {
-      case 2: return run_core<ValuCore<T, D, BS, 2>, T, D>(a, BS, st);
-      case 4: return run_core<ValuCore<T, D, BS, 4>, T, D>(a, BS, st);
-      default: break;
-    }
-  }
-  return hipErrorInvalidValue;
-}
-
-template <class T, int D>
-static hipError_t dispatch_d(const DecodeArgs& a, int bs, int group, hipStream_t st) {
-  switch (bs) {
-    case 8: return dispatch_bs<T, D, 8>(a, group, st);
-    case 16: return dispatch_bs<T, D, 16>(a, group, st);
-    case 32: return dispatch_bs<T, D, 32>(a, group, st);
-    default: return hipErrorInvalidValue;
-  }
-}
-
-template <class T>
-static hipError_t dispatch_t(const DecodeArgs& a, int head_dim, int bs, int group, hipStream_t st) {
-  switch (head_dim) {
-    case 64: return dispatch_d<T, 64>(a, bs, group, st);
-    case 128: return dispatch_d<T, 128>(a, bs, group, st);
-    default: return hipErrorInvalidValue;
-  }
-}
-
 hipError_t launch_decode(const DecodeArgs& a, Elem elem, int head_dim, int block_size, int group,
                          hipStream_t st) {
   switch (elem) {
-    case Elem::F32: return dispatch_t<F32>(a, head_dim, block_size, group, st);
-    case Elem::F16: return dispatch_t<F16>(a, head_dim, block_size, group, st);
-    case Elem::BF16: return dispatch_t<BF16>(a, head_dim, block_size, group, st);
+    case Elem::F32: return launch_decode_f32(a, head_dim, block_size, group, st);
+    case Elem::F16: return launch_decode_f16(a, head_dim, block_size, group, st);
+    case Elem::BF16: return launch_decode_bf16(a, head_dim, block_size, group, st);
   }
   return hipErrorInvalidValue;
 }

@@ -39,6 +39,10 @@ hipError_t launch_stream_read(const void* buf, uint64_t bytes, uint32_t* partial
 // other cases the VALU core.
 hipError_t launch_decode(const DecodeArgs& args, Elem elem, int head_dim, int block_size,
                          int group, hipStream_t stream);
+// the same, one per storage type (separate translation units)
+hipError_t launch_decode_f32(const DecodeArgs& args, int head_dim, int block_size, int group, hipStream_t stream);
+hipError_t launch_decode_f16(const DecodeArgs& args, int head_dim, int block_size, int group, hipStream_t stream);
+hipError_t launch_decode_bf16(const DecodeArgs& args, int head_dim, int block_size, int group, hipStream_t stream);
 
 // Device scratch of the no-allocation decode entry point: a file-scope
 // __device__ array of kDecodeScratchBytes, one per GPU, whose device address

@@ -157,3 +157,30 @@ def test_split_ignores_stale_workspace(dtype, G, partition):
                              b.max_context_len, partition, workspace=ws)
     torch.cuda.synchronize()
     check_close(gpu_out_f64(out, dtype), oracle_out(b), dtype, "stale workspace")
+
+
+@pytest.mark.parametrize("dtype,G,bs", [("bf16", 4, 16), ("f16", 1, 8), ("f32", 2, 32)])
+def test_resident_partitions_match_unit_kernel_bit_for_bit(dtype, G, bs):
+    # more than 4096 sequences run fixed partitions one wave per unit; fewer run
+    # them on the resident grid.  The same sequences through both give the same bits.
+    rng = np.random.default_rng(11)
+    lens = rng.integers(0, 100, size=4100)
+    lens[:3] = [1, 16, 97]
+    b = W.make_decode_batch(12, num_seqs=len(lens), num_q_heads=2 * G, num_kv_heads=2, head_dim=64, dtype=dtype,
+                            block_size=bs, context_lens=lens.tolist())
+    d = torch_io.to_device(b)
+    part = max(16, bs)
+    note(f"resident vs unit partitions {dtype} G={G} bs={bs} P={part} S={len(lens)}")
+    whole = P.decode_attention(d.query, d.k_pool, d.v_pool, d.block_tables, d.context_lens, b.scale,
+                               b.max_context_len, part)
+    halves = [P.decode_attention(d.query[i:j], d.k_pool, d.v_pool, d.block_tables[i:j], d.context_lens[i:j],
+                                 b.scale, b.max_context_len, part) for i, j in ((0, 2050), (2050, 4100))]
+    torch.cuda.synchronize()
+    a = torch_io.torch_to_storage(whole, dtype)
+    c = np.concatenate([torch_io.torch_to_storage(h, dtype) for h in halves])
+    assert a.tobytes() == c.tobytes()
+    seqs = [0, 1, 2, 2049, 2050, 4099] + rng.choice(4100, 10, replace=False).tolist()
+    ref = oracle_out(b, seqs=sorted(set(seqs)))
+    got = gpu_out_f64(whole, dtype)
+    sel = sorted(set(seqs))
+    check_close(got[sel], ref[sel], dtype, "resident vs unit")

@@ -134,3 +134,80 @@ def test_balanced_schedule_covers_each_tile_once(lens, X):
     for C in (1, 2, 8):
         for W in list(range(1, 70)) + [255, 256, 512, 768, 2048]:
             walk(lens, C, W, X)
+
+
+def walk_parts(lens, C, W, P, X):
+    """decode_parts_resident_kernel's schedule: units (s, c, p) of P tokens,
+    unit (s, c, p) at C cum[s] + c cost(s) + p (X + P/16), cost(s) =
+    ceil(L/16) + X ceil(L/P); wave w runs the units starting in
+    [w ntot / W, (w+1) ntot / W), in order, as runs of one head group's
+    consecutive partitions."""
+    S, PT = len(lens), P // TILE
+    nts = [-(-L // TILE) for L in lens]
+    nps = [-(-L // P) for L in lens]
+    cum = [0]
+    for n, q in zip(nts, nps):
+        cum.append(cum[-1] + (n + q * X if n else 0))
+    ntot = C * cum[S]
+    done = {}
+    for w in range(W):
+        f, fb = w * ntot // W, (w + 1) * ntot // W
+        if f >= fb:
+            continue
+        lo, hi = 0, S - 1
+        while lo < hi:
+            mid = (lo + hi + 1) >> 1
+            if C * cum[mid] <= f:
+                lo = mid
+            else:
+                hi = mid - 1
+        s = lo
+        cost = cum[s + 1] - cum[s]
+        assert cost > 0
+        rel = f - C * cum[s]
+        c = rel // cost
+        r = rel - c * cost
+        p = (r + X + PT - 1) // (X + PT)
+        ustart = C * cum[s] + c * cost + p * (X + PT)
+        np_ = nps[s]
+        prev = None
+        while True:
+            if p >= np_:
+                p = 0
+                c += 1
+                if c == C:
+                    c = 0
+                    s += 1
+                    while s < S and cum[s + 1] == cum[s]:
+                        s += 1
+                    if s >= S:
+                        break
+                    cost = cum[s + 1] - cum[s]
+                    np_ = nps[s]
+                ustart = C * cum[s] + c * cost
+            if ustart >= fb:
+                break
+            assert ustart >= f
+            # the head group's partitions p .. pl that start before fb, one run
+            sc0 = ustart - p * (X + PT)
+            pl = min(np_ - 1, (fb - sc0 + X + PT - 1) // (X + PT) - 1)
+            assert pl >= p
+            for q in range(p, pl + 1):
+                assert sc0 + q * (X + PT) < fb
+                assert (s, c, q) not in done
+                done[(s, c, q)] = w
+                assert prev is None or prev < (s, c, q)      # in order
+                prev = (s, c, q)
+            ustart += (pl + 1 - p) * (X + PT)
+            p = pl + 1
+    want = {(s, c, p) for s in range(S) for c in range(C) for p in range(nps[s])}
+    assert set(done) == want
+
+
+@pytest.mark.parametrize("X", [0, 1, 3, 8])
+@pytest.mark.parametrize("lens", cases())
+def test_resident_partition_schedule_runs_each_unit_once(lens, X):
+    for P in (16, 64, 512):
+        for C in (1, 2, 8):
+            for W in list(range(1, 40)) + [255, 1024]:
+                walk_parts(lens, C, W, P, X)
