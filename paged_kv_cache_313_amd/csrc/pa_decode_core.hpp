@@ -275,23 +275,26 @@ __device__ __forceinline__ void emit_ml(const DecodeArgs& a, const Dest& dst, in
   }
 }
 
-// Partial results of the resident partition kernel, buffered in LDS per wave.
-// A global store in the middle of the K/V stream is costly: vmcnt counts
-// loads and stores in issue order, so the wait for the next tile's loads also
-// waits for the store's acknowledgement, which queues behind the read stream
-// (measured: about 7 us per flushed partition on the long-context batch).
-// So each partition's (acc, m, l) goes to a slot of the wave's LDS buffer,
-// and the slots are written out together when the buffer is full and when
-// the wave has finished all its work.
+// Results of the resident-grid kernels, buffered in LDS per wave.  A global
+// store in the middle of the K/V stream is costly: vmcnt counts loads and
+// stores in issue order, so the wait for the next tile's loads also waits for
+// the store's acknowledgement, which queues behind the read stream (measured:
+// about 7 us per flushed partition on the long-context batch).  So each
+// segment's or partition's (acc, m, l) goes to a slot of the wave's LDS
+// buffer, and the slots are written out together when the buffer is full and
+// when the wave has finished all its work: partial rows to the workspace,
+// whole results (acc / l, rounded once to the output type) to the output.
 template <int H, int D>
 struct PartBuf {
   static constexpr int kBytes = 32768;                      // per wave
   static constexpr int kSlotBytes = H * (D + 2) * 4 + 8;
   static constexpr int kCap = kBytes / kSlotBytes;          // slots (3 at H 16, D 128)
   static_assert(kCap >= 1, "one slot at least");
+  static constexpr size_t kDirect = (size_t)1 << 63;        // row tag: an output row
   float* o;        // [kCap][H][D], 16-byte aligned
   float* ml;       // [kCap][H][2]: m, l
-  size_t* row;     // [kCap]: partial row of head 0 (head hh: + hh * pstride)
+  size_t* row;     // [kCap]: head 0's partial row (head hh: + hh * pstride), or
+                   // kDirect | its output row (head hh: + hh)
   size_t pstride;
   int count;
   __device__ __forceinline__ void init(char* lds, size_t stride) {
@@ -301,15 +304,26 @@ struct PartBuf {
     pstride = stride;
     count = 0;
   }
-  // Write the buffered slots to the workspace (16-byte chunks, whole rows
-  // per instruction) and empty the buffer.
+  // Write the buffered slots out (16-byte chunks of whole rows per
+  // instruction) and empty the buffer.
+  template <class T>
   __device__ __forceinline__ void flush(const DecodeArgs& a, int lane) {
     constexpr int CPR = D / 4;
     __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the wave's slot writes have landed
     __builtin_amdgcn_wave_barrier();
     for (int k = 0; k < count; ++k) {
-      const size_t r0 = row[k];
+      const size_t tag = row[k];
+      const size_t r0 = tag & ~kDirect;
+      if (tag & kDirect) {   // wave-uniform
+        for (int idx = lane; idx < H * CPR; idx += kWave) {
+          const int hh = idx / CPR, ch = idx % CPR;
+          const float inv = 1.f / ml[(k * H + hh) * 2 + 1];
+          const f32x4 v = *reinterpret_cast<const f32x4*>(o + (k * H + hh) * D + 4 * ch);
 #pragma unroll
+          for (int e = 0; e < 4; ++e) store_elem<T>(a.out, (r0 + hh) * D + 4 * ch + e, v[e] * inv);
+        }
+        continue;
+      }
       for (int idx = lane; idx < H * CPR; idx += kWave) {
         const int hh = idx / CPR, ch = idx % CPR;
         st16(a.ws_o + (r0 + (size_t)hh * pstride) * D + 4 * ch,
@@ -325,9 +339,10 @@ struct PartBuf {
     __builtin_amdgcn_s_waitcnt(0xc07f);   // reads done before the slots are reused
     __builtin_amdgcn_wave_barrier();
   }
-  // The slot for the next partition (flushing first when the buffer is full).
+  // The slot for the next result (flushing first when the buffer is full).
+  template <class T>
   __device__ __forceinline__ int take(const DecodeArgs& a, int lane) {
-    if (count == kCap) flush(a, lane);
+    if (count == kCap) flush<T>(a, lane);
     return count;
   }
   // n consecutive results (n a multiple of 4) of head hh, from element d0
@@ -389,7 +404,7 @@ struct ValuCore {
 
   // q heads h0 .. h0+H-1 of sequence s over tokens [tok0, tok1), run by one
   // wave; tbl is the wave's LDS window.
-  template <bool SPLIT, bool PARTS = false>
+  template <bool SPLIT, bool PARTS = false, bool BUF = PARTS>
   __device__ static void run(const DecodeArgs& a, int32_t* tbl_lds, TblCache& tc, int s, int h0, int tok0,
                              int tok1, const Dest& dst, PartBuf<H, D>* pb = nullptr) {
     const int lane = threadIdx.x & (kWave - 1);
@@ -426,8 +441,9 @@ struct ValuCore {
     // 0..3 in the order of a butterfly over lane ^ 4, lane ^ 8; the lane
     // swaps then add the other rows.  Lanes 0..3 hold the results.
     auto finish = [&](const Dest& d) {
-      const bool buffered = PARTS && !d.direct;   // partials of a run go to the LDS buffer
-      const int slot = buffered ? pb->take(a, lane) : 0;
+      constexpr bool buffered = BUF;   // results go to the wave's LDS buffer
+      int slot = 0;
+      if constexpr (BUF) slot = pb->template take<T>(a, lane);
 #pragma unroll
       for (int hh = 0; hh < H; ++hh) {
         float M = m_run[hh];
@@ -467,8 +483,9 @@ struct ValuCore {
             emit_ml(a, d, hh, M, l);
         }
       }
-      if (buffered) {
-        if (lane == 0) pb->row[slot] = d.prow0;
+      if constexpr (BUF) {
+        if (lane == 0)
+          pb->row[slot] = d.direct ? (PartBuf<HEADS, D>::kDirect | ((size_t)s * a.num_q_heads + h0)) : d.prow0;
         ++pb->count;
       }
     };
@@ -615,7 +632,7 @@ struct MfmaCore {
 
   // the G q heads h0 .. h0+G-1 (KV head h0 / G) of sequence s over tokens
   // [tok0, tok1), run by one wave; tbl is the wave's LDS window.
-  template <bool SPLIT, bool PARTS = false>
+  template <bool SPLIT, bool PARTS = false, bool BUF = PARTS>
   __device__ static void run(const DecodeArgs& a, int32_t* tbl_lds, TblCache& tc, int s, int h0, int tok0,
                              int tok1, const Dest& dst, PartBuf<G, D>* pb = nullptr) {
     const int lane = threadIdx.x & (kWave - 1);
@@ -647,8 +664,9 @@ struct MfmaCore {
     // every row then holds all sums, and row gr writes the heads h with
     // h % 4 == gr
     auto finish = [&](const Dest& d) {
-      const bool buffered = PARTS && !d.direct;   // partials of a run go to the LDS buffer
-      const int slot = buffered ? pb->take(a, lane) : 0;
+      constexpr bool buffered = BUF;   // results go to the wave's LDS buffer
+      int slot = 0;
+      if constexpr (BUF) slot = pb->template take<T>(a, lane);
       float M = m_run;
       M = swap_pair_max<16>(M);
       M = swap_pair_max<32>(M);
@@ -686,8 +704,9 @@ struct MfmaCore {
             emit_ml(a, d, h, mh, lh);
         }
       }
-      if (buffered) {
-        if (lane == 0) pb->row[slot] = d.prow0;
+      if constexpr (BUF) {
+        if (lane == 0)
+          pb->row[slot] = d.direct ? (PartBuf<HEADS, D>::kDirect | ((size_t)s * a.num_q_heads + h0)) : d.prow0;
         ++pb->count;
       }
     };
@@ -916,6 +935,8 @@ __global__ __launch_bounds__(NW * kWave) void decode_balanced_kernel(DecodeArgs 
   __shared__ int32_t s_cum[kBalancedMaxSeqs + 1];
   __shared__ int32_t s_wave[NW];
   __shared__ int32_t s_tbl[NW][kTblWin];
+  using Buf = PartBuf<H, D>;
+  __shared__ __align__(16) char s_pbuf[NW][Buf::kBytes];
   const int S = a.num_seqs, C = a.head_chunks;
   tile_prefix<NW * kWave>(a, block_size, s_cum, s_wave);
   if (blockIdx.x == 0)
@@ -947,6 +968,9 @@ __global__ __launch_bounds__(NW * kWave) void decode_balanced_kernel(DecodeArgs 
   int u = (int)(rel - (int64_t)c * ntc);    // position within that cost
   bool first = true;
   TblCache tc;
+  Buf pb;
+  pb.init(s_pbuf[wave], 1);
+  const int lane = threadIdx.x & (kWave - 1);
   while (f < fb) {
     const int n = (int)min((int64_t)(ntc - u), fb - f);
     const int nt = ntc - kSegCost;
@@ -956,7 +980,7 @@ __global__ __launch_bounds__(NW * kWave) void decode_balanced_kernel(DecodeArgs 
       const int tok0 = t0 * kTile, tok1 = min(t1 * kTile, L);
       const size_t slot = 2 * (size_t)w + (first ? 0 : 1);
       const Dest dst{t0 == 0 && t1 == nt, slot * H, 1, 0};
-      Core::template run<true>(a, s_tbl[wave], tc, s, c * H, tok0, tok1, dst);
+      Core::template run<true, false, true>(a, s_tbl[wave], tc, s, c * H, tok0, tok1, dst, &pb);
       first = false;
     }
     f += n;
@@ -972,6 +996,7 @@ __global__ __launch_bounds__(NW * kWave) void decode_balanced_kernel(DecodeArgs 
       ntc = s_cum[s + 1] - s_cum[s];
     }
   }
+  pb.template flush<T>(a, lane);   // results of the wave's segments, after its last loads
 }
 
 // ============================================================================
@@ -1061,7 +1086,7 @@ __global__ __launch_bounds__(NW * kWave) void decode_parts_resident_kernel(Decod
     ustart += (int64_t)(pl + 1 - p) * (kSegCost + PT);
     p = pl + 1;
   }
-  pb.flush(a, lane);   // the K/V stream is over: nothing waits on these stores
+  pb.template flush<T>(a, lane);   // the K/V stream is over: nothing waits on these stores
 }
 
 // ============================================================================
