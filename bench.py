@@ -64,6 +64,8 @@ def parse_args():
     ap.add_argument("--table-layout", default="shuffled", choices=["shuffled", "identity", "hier"],
                     help="physical layout: shuffled blocks, identity (contiguous) tables, or two-level tables "
                          "with the prompt in 256-token large pages")
+    ap.add_argument("--group", type=int, default=None, choices=[2, 4, 8, 16],
+                    help="GQA group size of the Llama-3-8B-shaped workload (query heads = 8 x group; default 4)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-swap", action="store_true", help="skip the swap (preemption traffic) leg")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill leg")
@@ -167,6 +169,10 @@ def make_batch(args):
     hier = args.table_layout == "hier"
     if args.config in (2, 3, 5):
         kw["table_layout"] = "shuffled" if hier else args.table_layout
+    if args.group is not None:
+        if args.config != 3:
+            raise SystemExit("--group applies to the Llama-3-8B-shaped workload (--config 3)")
+        kw["num_q_heads"] = 8 * args.group
     if args.config == 5:
         b = W.config5(block_size=args.block_size, **kw)
     else:
@@ -841,8 +847,11 @@ def main():
                   "checked": "all outputs vs the fp64 oracle"}
 
     explicit = args.partition is not None
-    ctr = counters_from_profile(args.config, part, b.block_size, explicit)
-    cfg = {"workload": WORKLOADS[args.config], "num_seqs": b.num_seqs, "num_q_heads": b.num_q_heads,
+    ctr = None if args.group not in (None, 4) else counters_from_profile(args.config, part, b.block_size, explicit)
+    workload = WORKLOADS[args.config]
+    if args.group is not None and args.group != 4:
+        workload = workload.replace("32q/8kv heads", f"{8 * args.group}q/8kv heads")
+    cfg = {"workload": workload, "num_seqs": b.num_seqs, "num_q_heads": b.num_q_heads,
            "num_kv_heads": b.num_kv_heads, "head_dim": b.head_dim, "block_size": b.block_size,
            "num_blocks": b.num_blocks, "partition_size": part, "table_layout": args.table_layout,
            "kv_bytes_per_step": kv_bytes, "unique_kv_bytes_per_step": uniq_kv,

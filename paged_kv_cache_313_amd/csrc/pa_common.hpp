@@ -199,6 +199,26 @@ __device__ __forceinline__ f32x4 mfma_16x16x32<F16>(u32x4 a, u32x4 b, f32x4 c) {
                                                 __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
 
+// D[16x16] += A[16x16] B[16x16] in fp32.  Lane l supplies A row l % 16 and B
+// column l % 16, each as the 4 k-values 4 (l / 16) .. 4 (l / 16) + 3 packed in
+// 8 bytes (the lower half of the first dword is the first); it receives D
+// rows 4 (l / 16) .. 4 (l / 16) + 3 of column l % 16.
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+template <class T>
+__device__ __forceinline__ f32x4 mfma_16x16x16(u32x2 a, u32x2 b, f32x4 c);
+template <>
+__device__ __forceinline__ f32x4 mfma_16x16x16<BF16>(u32x2 a, u32x2 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, a), __builtin_bit_cast(i16x4, b),
+                                                   c, 0, 0, 0);
+}
+template <>
+__device__ __forceinline__ f32x4 mfma_16x16x16<F16>(u32x2 a, u32x2 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a), __builtin_bit_cast(f16x4, b), c,
+                                               0, 0, 0);
+}
+
 // two fp32 values rounded (to nearest even) into one packed 16-bit pair
 template <class T> __device__ __forceinline__ uint32_t pack2(float lo, float hi);
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -210,6 +230,17 @@ template <> __device__ __forceinline__ uint32_t pack2<BF16>(float lo, float hi) 
 }
 template <> __device__ __forceinline__ uint32_t pack2<F16>(float lo, float hi) {
   return (uint32_t)f32_to_f16_rne(lo) | ((uint32_t)f32_to_f16_rne(hi) << 16);
+}
+
+// the two values of a packed 16-bit pair, exactly in fp32
+template <class T> __device__ __forceinline__ void unpack2(uint32_t x, float& lo, float& hi);
+template <> __device__ __forceinline__ void unpack2<BF16>(uint32_t x, float& lo, float& hi) {
+  lo = __uint_as_float(x << 16);
+  hi = __uint_as_float(x & 0xffff0000u);
+}
+template <> __device__ __forceinline__ void unpack2<F16>(uint32_t x, float& lo, float& hi) {
+  lo = (float)__builtin_bit_cast(_Float16, (uint16_t)(x & 0xffffu));
+  hi = (float)__builtin_bit_cast(_Float16, (uint16_t)(x >> 16));
 }
 
 // ---- cross-lane moves -------------------------------------------------------

@@ -822,6 +822,198 @@ struct MfmaCore {
 };
 
 // ============================================================================
+// MFMA core with P.V on the matrix cores too (f16/bf16, head_dim 128, large
+// groups).  Scores as in MfmaCore: lane (gr = lane / 16, w = lane % 16) ends
+// a tile holding S[token 4 gr + r][head w % G], r = 0..3, and its V loads
+// hold tokens 4 gr + j (j = 0..3) at d = 8 w .. 8 w + 7.  Both are already
+// operands of O^T[d][head] += V^T P^T as v_mfma_f32_16x16x16_{bf16,f16}
+// products: B = the lane's 4 probabilities (k = token 4 gr + r, column =
+// head w % G), and A for product dt (dt = 0..7) = element dt of the lane's
+// 4 V chunks (row w, k = the same tokens), once output row i of product dt is
+// taken to stand for d = 8 i + dt.  Two byte permutes form each A; no value
+// crosses lanes.  The product sums over the 16 tokens of all four rows, so
+// the running max is per head over the whole tile (two lane swaps), and lane
+// (gr, w) ends holding O[head w % G][d] for d in [32 gr, 32 gr + 32).  The
+// probabilities are rounded to the input type for the product (and the row
+// sums add the same rounded values), as in the prefill kernel.  Per tile and
+// wave: 4 + 8 matrix-core products and about 60 vector instructions, where
+// MfmaCore's P.V needs G x 36 (2,300 at G = 16).
+// ============================================================================
+#ifndef PA_PV_MFMA_MIN_GROUP
+#define PA_PV_MFMA_MIN_GROUP 8
+#endif
+template <class T, int D, int BS, int G>
+struct MfmaPvCore {
+  static_assert(D == 128, "lane layout of the V chunks");
+  static constexpr int ROWB = D * 2;
+  static constexpr int NQK = D / 32;   // score products per tile (k = 32)
+  static constexpr int NVI = 4;        // V chunks per lane per tile: tokens 4 gr .. 4 gr + 3
+  static constexpr int NDT = 8;        // P.V products per tile (elements of a chunk)
+  static constexpr int HEADS = G;
+  static constexpr int kBalancedWgPerCu = PA_MFMA_WG_PER_CU;
+  static_assert(16 % G == 0 && G >= 2, "group");
+  static_assert(kTblWin * BS % kTile == 0, "window");
+  static constexpr uint32_t kTileBytes = (BS >= 16 ? kTile : BS) * ROWB;
+
+  template <bool SPLIT, bool PARTS = false, bool BUF = PARTS>
+  __device__ static void run(const DecodeArgs& a, int32_t* tbl_lds, TblCache& tc, int s, int h0, int tok0,
+                             int tok1, const Dest& dst, PartBuf<G, D>* pb = nullptr) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int gr = lane >> 4, w = lane & 15;
+    const int g = h0 / G;
+
+    u32x4 qop[NQK];  // B operand of the scores: query row of head w % G, chunk 4 i + gr
+    {
+      const char* qrow = reinterpret_cast<const char*>(a.query) +
+                         ((size_t)s * a.num_q_heads + h0 + (w % G)) * ROWB;
+#pragma unroll
+      for (int i = 0; i < NQK; ++i) qop[i] = ld16(qrow + (4 * i + gr) * 16);
+    }
+    float m_run, l_run;   // head w % G: max over the tiles so far, sum over row gr's tokens
+    f32x4 oacc[NDT];      // O[head w % G][8 (4 gr + r) + dt] in oacc[dt][r]
+    auto reset = [&]() {
+      m_run = kNegInf;
+      l_run = 0.f;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    };
+    reset();
+    int pend = tok0 + dst.part, pk = 0;   // with PARTS: end of the current partition, its index
+
+    // the four rows' sums add up to the head's; lanes w < G write head w,
+    // d = 32 gr .. 32 gr + 31 (row gr = 0 writes m and l)
+    auto finish = [&](const Dest& d) {
+      int slot = 0;
+      if constexpr (BUF) slot = pb->template take<T>(a, lane);
+      float l = swap_pair_sum<16>(l_run);
+      l = swap_pair_sum<32>(l);
+      float v[32];
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) v[8 * r + dt] = oacc[dt][r];
+      if (w < G) {
+        const size_t orow = (size_t)s * a.num_q_heads + h0 + w;
+        if constexpr (BUF) {
+          pb->template chunk<32>(slot, w, 32 * gr, v);
+          if (gr == 0) pb->set_ml(slot, w, m_run, l);
+        } else {
+          emit_chunk<T, 32>(a, d, orow, w, 32 * gr, D, v, l);
+          if (gr == 0) emit_ml(a, d, w, m_run, l);
+        }
+      }
+      if constexpr (BUF) {
+        if (lane == 0)
+          pb->row[slot] = d.direct ? (PartBuf<HEADS, D>::kDirect | ((size_t)s * a.num_q_heads + h0)) : d.prow0;
+        ++pb->count;
+      }
+    };
+
+    const char* kbase = reinterpret_cast<const char*>(a.k_pool) + (size_t)g * BS * ROWB;
+    const char* vbase = reinterpret_cast<const char*>(a.v_pool) + (size_t)g * BS * ROWB;
+    const size_t blk_stride = (size_t)a.num_kv_heads * BS * ROWB;
+    const TableView trow = table_view(a, s);
+    // K: token w of the tile, chunk 4 i + gr; V: token 4 gr + j, chunk w
+    const uint32_t k_off = (uint32_t)((BS >= 16 ? w : (w & 7)) * ROWB + gr * 16);
+    const uint32_t v_off = (uint32_t)((BS >= 16 ? 4 * gr : ((4 * gr) & 7)) * ROWB + w * 16);
+    const bool k_hi = BS < 16 && w >= 8;
+    const bool v_hi = BS < 16 && gr >= 2;
+
+    for (int wb = tok0; wb < tok1;) {
+      const int fblk = wb / BS;
+      const int off0 = wb - fblk * BS;
+      const int we = min((fblk + kTblWin) * BS, tok1);
+      const int nent = (we - 1) / BS - fblk + 1;
+      int nshared;
+      const int32_t* tbl = staged_window<BS, SPLIT>(a, tbl_lds, tc, trow, s, fblk, nent, lane, nshared);
+
+      auto load = [&](auto pol, int ti, MfmaBuf<NQK, NVI>& buf) {
+        constexpr int AUX = decltype(pol)::value;
+        size_t lo, hi;
+        tile_offsets<BS, ROWB>(tbl, off0 + ti * kTile, nent, blk_stride, lo, hi);
+        if constexpr (BS >= 16) {  // one block region: SGPR base + lane offset
+          const rsrc_t rk = make_rsrc(kbase + lo, kTileBytes);
+          const rsrc_t rv = make_rsrc(vbase + lo, kTileBytes);
+#pragma unroll
+          for (int i = 0; i < NQK; ++i) buf.k[i] = buf_ld16_aux<AUX>(rk, k_off + i * 64);
+#pragma unroll
+          for (int j = 0; j < NVI; ++j) buf.v[j] = buf_ld16_aux<AUX>(rv, v_off + j * ROWB);
+        } else {  // block_size 8: tokens 8..15 come from the next block
+          const char* kb = kbase + (k_hi ? hi : lo) + k_off;
+          const char* vb = vbase + (v_hi ? hi : lo) + v_off;
+#pragma unroll
+          for (int i = 0; i < NQK; ++i) buf.k[i] = ld16_aux<AUX>(kb + i * 64);
+#pragma unroll
+          for (int j = 0; j < NVI; ++j) buf.v[j] = ld16_aux<AUX>(vb + j * ROWB);
+        }
+      };
+      auto compute = [&](int ti, const MfmaBuf<NQK, NVI>& buf) {
+        const int ts = wb + ti * kTile;
+        f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < NQK; ++i) sacc = mfma_16x16x32<T>(buf.k[i], qop[i], sacc);
+
+        float sc[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sc[r] = (ts + 4 * gr + r < we) ? sacc[r] * a.scale_log2 : kNegInf;
+        float tmax = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+        tmax = swap_pair_max<16>(tmax);   // the head's max over the tile's 16 tokens
+        tmax = swap_pair_max<32>(tmax);
+        const bool grow = tmax > m_run + kLazy;   // true for the first tile
+        if (__any(grow)) {
+          const float m_new = grow ? tmax : m_run;
+          const float alpha = grow ? fast_exp2(m_run - m_new) : 1.f;
+          m_run = m_new;
+          l_run *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt) oacc[dt] *= alpha;
+        }
+        float pr[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) pr[r] = sc[r] == kNegInf ? 0.f : fast_exp2(sc[r] - m_run);
+        u32x2 pb_op;   // B operand: the 4 probabilities rounded to the input type
+        pb_op[0] = pack2<T>(pr[0], pr[1]);
+        pb_op[1] = pack2<T>(pr[2], pr[3]);
+        {
+          float r0, r1, r2, r3;   // the row sum adds the rounded weights that multiply V
+          unpack2<T>(pb_op[0], r0, r1);
+          unpack2<T>(pb_op[1], r2, r3);
+          l_run += (r0 + r1) + (r2 + r3);
+        }
+        u32x4 vz[NVI];
+#pragma unroll
+        for (int j = 0; j < NVI; ++j) {
+          const u32x4 z = {0u, 0u, 0u, 0u};
+          vz[j] = (ts + 4 * gr + j < we) ? buf.v[j] : z;   // tail slots may hold NaN
+        }
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          // element dt of tokens 4 gr + 0 .. 3: low halves (even dt) or high halves (odd dt)
+          const uint32_t sel = (dt & 1) ? 0x07060302u : 0x05040100u;
+          u32x2 av;
+          av[0] = __builtin_amdgcn_perm(vz[1][dt >> 1], vz[0][dt >> 1], sel);
+          av[1] = __builtin_amdgcn_perm(vz[3][dt >> 1], vz[2][dt >> 1], sel);
+          oacc[dt] = mfma_16x16x16<T>(av, pb_op, oacc[dt]);
+        }
+        if constexpr (PARTS) {   // a partition ends inside the run: write it, start the next
+          if (ts + kTile == pend && pend < tok1) {
+            finish(dest_part(dst, pk));
+            reset();
+            pend += dst.part;
+            ++pk;
+          }
+        }
+      };
+      const int ntiles = (we - wb + kTile - 1) / kTile;
+      run_window<MfmaBuf<NQK, NVI>, SPLIT>(ntiles, shared_tiles<BS>(nshared, nent, off0, ntiles), load, compute);
+      wb = we;
+    }
+
+    finish(dest_part(dst, pk));
+  }
+};
+
+// ============================================================================
 // Unit-mode kernel: wave = (sequence, head group, partition), sequence the
 // fastest index.  xcd_unit spreads runs of neighbouring workgroups over the
 // XCDs.
@@ -1344,14 +1536,26 @@ static hipError_t run_core(const DecodeArgs& a, int bs, hipStream_t st) {
   return hipGetLastError();
 }
 
+// Grouped queries: P.V on the matrix cores for head_dim 128 and groups of at
+// least PA_PV_MFMA_MIN_GROUP (there the vector P.V of MfmaCore, G x 36
+// instructions per V chunk, bounds the call: 65 % of the HBM peak at G = 8,
+// 32 % at G = 16 on the Llama-3-8B-shaped batch), MfmaCore otherwise.
+template <class T, int D, int BS, int G>
+static hipError_t run_gqa(const DecodeArgs& a, hipStream_t st) {
+  if constexpr (D == 128 && G >= PA_PV_MFMA_MIN_GROUP)
+    return run_core<MfmaPvCore<T, D, BS, G>, T, D>(a, BS, st);
+  else
+    return run_core<MfmaCore<T, D, BS, G>, T, D>(a, BS, st);
+}
+
 template <class T, int D, int BS>
 static hipError_t dispatch_bs(const DecodeArgs& a, int group, hipStream_t st) {
   if constexpr (!std::is_same<T, F32>::value) {
     switch (group) {
-      case 2: return run_core<MfmaCore<T, D, BS, 2>, T, D>(a, BS, st);
-      case 4: return run_core<MfmaCore<T, D, BS, 4>, T, D>(a, BS, st);
-      case 8: return run_core<MfmaCore<T, D, BS, 8>, T, D>(a, BS, st);
-      case 16: return run_core<MfmaCore<T, D, BS, 16>, T, D>(a, BS, st);
+      case 2: return run_gqa<T, D, BS, 2>(a, st);
+      case 4: return run_gqa<T, D, BS, 4>(a, st);
+      case 8: return run_gqa<T, D, BS, 8>(a, st);
+      case 16: return run_gqa<T, D, BS, 16>(a, st);
       default: break;   // group 1: VALU
     }
   }

@@ -55,6 +55,30 @@ def oracle_out(b, k_pool=None, v_pool=None, seqs=None):
                               b.block_size, b.dtype, seqs=seqs)
 
 
+PV_MFMA_MIN_GROUP = 8   # decode groups from this size (head_dim 128) run P.V on the matrix cores
+
+
+def pv_extra(b, k_pool=None, v_pool=None, seqs=None):
+    """Allowance for decode batches whose P.V runs on the matrix cores (f16 /
+    bf16, head_dim 128, group >= 8): the probabilities are rounded to the
+    input type (relative error <= u = 2^-(m+1) each) and normalised by the sum
+    of the same rounded weights, so each normalised weight is off by at most
+    2u / (1 - u) relatively and an output by at most that times
+    sum_t w_t |v_t| / sum_t w_t, which the oracle over |V| gives exactly;
+    2^-m covers 2u / (1 - u) up to a term of order u^2 that the ulp part of
+    the bound absorbs.  None for batches on the other cores."""
+    G = b.num_q_heads // b.num_kv_heads
+    if b.dtype == "f32" or b.head_dim != 128 or G < PV_MFMA_MIN_GROUP:
+        return None
+    if k_pool is None:
+        k_pool, v_pool = oracle_pools(b)
+    from workloads import synth as W
+    vabs = W.to_storage(np.abs(O.upcast(v_pool, b.dtype)).astype(np.float32), b.dtype)
+    mean = O.decode_attention(b.query, k_pool, vabs, b.block_tables, b.context_lens, b.scale, b.block_size,
+                              b.dtype, seqs=seqs)
+    return 2.0 ** -MANT_BITS[b.dtype] * mean
+
+
 def gpu_out_f64(out: torch.Tensor, dtype: str) -> np.ndarray:
     return O.upcast(torch_io.torch_to_storage(out, dtype), dtype)
 

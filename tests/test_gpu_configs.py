@@ -21,7 +21,7 @@ import paged_kv_cache_313_amd as P
 from workloads import synth as W
 from workloads import torch_io
 
-from gpu_util import check_close, gpu_out_f64, gpu_step, note, oracle_out, oracle_pools
+from gpu_util import check_close, gpu_out_f64, gpu_step, note, oracle_out, oracle_pools, pv_extra
 
 pytestmark = pytest.mark.gpu
 
@@ -32,6 +32,7 @@ def full_check(b, partitions=(None,), check_pools=False):
     d = torch_io.to_device(b)
     k_ref, v_ref = oracle_pools(b)
     ref = oracle_out(b, k_ref, v_ref)                 # every sequence
+    extra = pv_extra(b, k_ref, v_ref)
     for i, part in enumerate(partitions):
         chosen = part if part is not None else P.choose_partition(b.num_seqs, b.num_kv_heads,
                                                                   b.max_context_len, b.block_size)
@@ -45,7 +46,7 @@ def full_check(b, partitions=(None,), check_pools=False):
             assert k.view(np.uint8).tobytes() == k_ref.view(np.uint8).tobytes()
             assert v.view(np.uint8).tobytes() == v_ref.view(np.uint8).tobytes()
             del k, v
-        stats = check_close(gout, ref, b.dtype, f"{b.name}/P{chosen}")
+        stats = check_close(gout, ref, b.dtype, f"{b.name}/P{chosen}", extra=extra)
         note(f"{b.name}: partition={chosen}: all {b.num_seqs} seqs checked, max_abs={stats['max_abs']:.3g}")
         del out
     del d
@@ -63,6 +64,12 @@ def test_config2_opt13b_mha_f16():
 
 def test_config3_llama3_gqa_bf16_with_append():
     full_check(W.config3(), partitions=(None, 512), check_pools=True)
+
+
+@pytest.mark.parametrize("group", [8, 16])
+def test_config3_larger_groups_matrix_core_pv(group):
+    # the Llama-3-8B-shaped batch with 8 x group query heads: P.V on the matrix cores
+    full_check(W.config3(num_q_heads=8 * group), partitions=(None, 512))
 
 
 def test_config4_prefix_shared_cow_append():

@@ -13,7 +13,7 @@ import paged_kv_cache_313_amd as P
 from workloads import synth as W
 from workloads import torch_io
 
-from gpu_util import check_close, gpu_out_f64, gpu_step, note, oracle_out
+from gpu_util import check_close, gpu_out_f64, gpu_step, note, oracle_out, pv_extra
 
 pytestmark = pytest.mark.gpu
 
@@ -33,7 +33,8 @@ def run(b, partition_size):
 CASES = [(dt, D, bs, G) for dt in ("f32", "f16", "bf16") for D in (64, 128) for bs in (8, 16, 32)
          for G in (1, 4)]
 CASES += [("bf16", 128, 16, 2), ("bf16", 128, 16, 8), ("bf16", 128, 16, 16), ("f16", 64, 8, 8),
-          ("f32", 64, 16, 2), ("f32", 128, 16, 8)]
+          ("f32", 64, 16, 2), ("f32", 128, 16, 8), ("f16", 128, 8, 8), ("f16", 128, 32, 16), ("bf16", 128, 8, 16),
+          ("bf16", 128, 32, 8)]
 
 
 @pytest.mark.parametrize("partition", [0, 64, 512, -1])
@@ -42,7 +43,8 @@ def test_decode_matches_oracle(dtype, D, bs, G, partition):
     b = batch(dtype, D, bs, G)
     note(f"decode dtype={dtype} D={D} bs={bs} G={G} P={partition}")
     out = run(b, partition)
-    check_close(gpu_out_f64(out, dtype), oracle_out(b), dtype, f"{dtype}/D{D}/bs{bs}/G{G}/P{partition}")
+    check_close(gpu_out_f64(out, dtype), oracle_out(b), dtype, f"{dtype}/D{D}/bs{bs}/G{G}/P{partition}",
+                extra=pv_extra(b))
 
 
 @pytest.mark.parametrize("dtype,G", [("bf16", 4), ("f16", 1), ("f32", 1)])

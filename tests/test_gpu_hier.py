@@ -12,7 +12,7 @@ import paged_kv_cache_313_amd as P
 from workloads import synth as W
 from workloads import torch_io
 
-from gpu_util import check_close, gpu_out_f64, gpu_step, note
+from gpu_util import check_close, gpu_out_f64, gpu_step, note, pv_extra
 
 pytestmark = pytest.mark.gpu
 
@@ -40,7 +40,7 @@ PROMPTS = [1, 39, 290, 800, 2090]
 
 @pytest.mark.parametrize("partition", [0, 64, -1])
 @pytest.mark.parametrize("dtype,D,bs,G,H", [("bf16", 128, 16, 4, 16), ("f16", 64, 8, 1, 4), ("f32", 128, 32, 4, 2),
-                                            ("bf16", 64, 16, 8, 64), ("f16", 128, 16, 1, 1)])
+                                            ("bf16", 64, 16, 8, 64), ("f16", 128, 16, 1, 1), ("bf16", 128, 16, 16, 4)])
 def test_decode_hier_bit_identical_to_flat(dtype, D, bs, G, H, partition):
     b, hb, large, nl = pair(dtype, D, bs, G, LENS, PROMPTS, H, seed=bs + H)
     note(f"hier decode {dtype} D={D} bs={bs} G={G} H={H} P={partition}")
@@ -51,7 +51,7 @@ def test_decode_hier_bit_identical_to_flat(dtype, D, bs, G, H, partition):
     O.kv_append(kp, vp, hb.new_key, hb.new_value, hb.slot_mapping, bs)
     ref = O.decode_attention_hier(hb.query, kp, vp, large, nl, hb.block_tables, H, hb.context_lens, hb.scale, bs,
                                   dtype)
-    check_close(gpu_out_f64(hier, dtype), ref, dtype, "hier decode")
+    check_close(gpu_out_f64(hier, dtype), ref, dtype, "hier decode", extra=pv_extra(b))
 
 
 @pytest.mark.parametrize("dtype,G,H", [("bf16", 4, 16), ("f16", 1, 4)])

@@ -24,7 +24,7 @@ import paged_kv_cache_313_amd as P
 from workloads import synth as W
 from workloads import torch_io
 
-from gpu_util import check_close, note, oracle_out
+from gpu_util import check_close, note, oracle_out, pv_extra
 
 pytestmark = pytest.mark.gpu
 
@@ -68,7 +68,7 @@ def decode(b, partition):
 
 @pytest.mark.parametrize("partition", [0, 64, -1])
 @pytest.mark.parametrize("dtype,D,bs,G", [("bf16", 128, 16, 4), ("bf16", 128, 8, 4), ("f16", 128, 32, 1),
-                                          ("f32", 64, 16, 1), ("f16", 64, 8, 2)])
+                                          ("f32", 64, 16, 1), ("f16", 64, 8, 2), ("bf16", 128, 16, 8)])
 def test_shared_blocks_bit_identical_to_copied(dtype, D, bs, G, partition):
     copied, shared = make_pair(dtype, D, bs, G)
     note(f"shared vs copied blocks dtype={dtype} D={D} bs={bs} G={G} P={partition}")
@@ -77,4 +77,5 @@ def test_shared_blocks_bit_identical_to_copied(dtype, D, bs, G, partition):
     assert out_c.tobytes() == out_s.tobytes()
     ref = oracle_out(copied)
     np.testing.assert_array_equal(ref, oracle_out(shared))   # the oracle agrees on the two layouts
-    check_close(O.upcast(out_s, dtype), ref, dtype, f"{dtype}/D{D}/bs{bs}/G{G}/P{partition}")
+    check_close(O.upcast(out_s, dtype), ref, dtype, f"{dtype}/D{D}/bs{bs}/G{G}/P{partition}",
+                extra=pv_extra(copied))

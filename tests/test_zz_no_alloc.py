@@ -13,7 +13,7 @@ import paged_kv_cache_313_amd as P
 from workloads import synth as W
 from workloads import torch_io
 
-from gpu_util import check_close, gpu_out_f64, note, oracle_out
+from gpu_util import check_close, gpu_out_f64, note, oracle_out, pv_extra
 
 pytestmark = pytest.mark.gpu
 
@@ -47,7 +47,7 @@ def test_noalloc_matches_workspace_entry_point(dtype, D, bs, G, partition, lens)
         a = torch_io.torch_to_storage(out, dtype)
         r = torch_io.torch_to_storage(ref_out, dtype)
         assert a.tobytes() == r.tobytes(), f"call {call}: differs from pa_decode_attention"
-        check_close(gpu_out_f64(out, dtype), oracle_out(b), dtype, f"noalloc call {call}")
+        check_close(gpu_out_f64(out, dtype), oracle_out(b), dtype, f"noalloc call {call}", extra=pv_extra(b))
 
 
 def test_noalloc_refuses_partials_beyond_the_scratch():
