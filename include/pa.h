@@ -77,7 +77,14 @@ typedef enum {
   PA_ERR_HOST_MEMORY = 12 /* swap: the host buffer is not pinned, GPU-mapped memory */
 } pa_status;
 
+/* In C++ the enum has a fixed 32-bit underlying type, so that any int32 a C
+ * caller passes is a value of the type (and is rejected with PA_ERR_DTYPE
+ * unless it names a dtype); the ABI is that of a C enum, a 32-bit int. */
+#ifdef __cplusplus
+typedef enum : int32_t { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype;
+#else
 typedef enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype;
+#endif
 
 /* partition_size value selecting the balanced split of pa_decode_attention */
 #define PA_PARTITION_BALANCED (-1)

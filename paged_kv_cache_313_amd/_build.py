@@ -89,6 +89,48 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     return LIB_PATH
 
 
+# Host sanitizer build: the host-side translation units (the C ABI's checks
+# and the block manager) with AddressSanitizer and UndefinedBehaviorSanitizer
+# on their host code only, linked with the ordinary kernel objects.  Loaded by
+# a Python process that preloads clang's ASan runtime (sanitizer_runtime(),
+# which also carries the UBSan handlers); CPU use only.
+HOST_SOURCES = ["pa_api.cpp", "pa_block_manager.cpp"]
+SANITIZED_LIB = os.path.join(BUILD_DIR, "libpagedkv_sanitized.so")
+SANITIZE_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                  "-Xarch_host", "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer", "-g"]
+
+
+def sanitizer_runtime() -> str:
+    import glob
+    llvm = os.path.join(os.path.dirname(os.path.realpath(hipcc())), "..", "llvm")
+    hits = sorted(glob.glob(os.path.join(llvm, "lib", "clang", "*", "lib", "linux", "libclang_rt.asan-x86_64.so")))
+    hits = hits or sorted(glob.glob("/opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
+    if not hits:
+        raise RuntimeError("clang's ASan runtime (libclang_rt.asan-x86_64.so) not found")
+    return os.path.realpath(hits[-1])
+
+
+def build_sanitized() -> str:
+    """Compile HOST_SOURCES with host sanitizers and link them with the kernel
+    objects of the ordinary build (built first when missing)."""
+    kernel_objs = [os.path.join(BUILD_DIR, os.path.splitext(s)[0] + ".o") for s in SOURCES if s not in HOST_SOURCES]
+    if not all(os.path.exists(o) for o in kernel_objs):
+        build()
+    cc = hipcc()
+    objs = []
+    cmds = []
+    for src in HOST_SOURCES:
+        obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".asan.o")
+        objs.append(obj)
+        cmds.append([cc, *COMPILE_FLAGS, *SANITIZE_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+    with ThreadPoolExecutor(max_workers=len(cmds)) as ex:
+        list(ex.map(_run, cmds))
+    tmp = SANITIZED_LIB + ".tmp"
+    _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs, *kernel_objs])
+    os.replace(tmp, SANITIZED_LIB)
+    return SANITIZED_LIB
+
+
 if __name__ == "__main__":
     path = build(verbose="-v" in sys.argv)
     print(path)

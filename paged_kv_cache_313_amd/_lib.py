@@ -7,7 +7,8 @@ import ctypes
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libpagedkv.so")
+# PAGEDKV_LIB names another build of the same ABI (e.g. the host sanitizer build)
+LIB_PATH = os.environ.get("PAGEDKV_LIB") or os.path.join(HERE, "libpagedkv.so")
 
 PA_OK = 0
 PA_F32, PA_F16, PA_BF16 = 0, 1, 2
