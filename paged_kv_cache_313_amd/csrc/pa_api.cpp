@@ -45,11 +45,13 @@ int64_t num_partitions(int32_t max_context_len, int32_t partition_size) {
 
 size_t align16(size_t x) { return (x + 15) & ~(size_t)15; }
 
-// Balanced-mode workspace: tile prefix sums, then 2 partial slots per wave of
-// group-size rows (m, l, and head_dim partial outputs).
-size_t balanced_ws_bytes(int32_t num_seqs, int32_t group, int32_t head_dim) {
+// Balanced-mode workspace: one 32-byte merge descriptor per wave boundary,
+// then 2 partial slots per wave of group-size rows (head_dim partial outputs,
+// m, l).
+constexpr size_t kDescBytes = 4 * sizeof(int64_t);
+size_t balanced_ws_bytes(int32_t group, int32_t head_dim) {
   const size_t rows = 2 * (size_t)pa::kBalancedMaxWaves * (size_t)group;
-  return align16(((size_t)num_seqs + 1) * sizeof(int32_t)) + rows * ((size_t)head_dim + 2) * sizeof(float);
+  return (size_t)pa::kBalancedMaxWaves * kDescBytes + rows * ((size_t)head_dim + 2) * sizeof(float);
 }
 
 }  // namespace
@@ -300,7 +302,7 @@ PA_EXPORT size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads
       head_dim < 1 || max_context_len < 0 || partition_size < PA_PARTITION_BALANCED)
     return (size_t)-1;
   if (partition_size == PA_PARTITION_BALANCED)
-    return balanced_ws_bytes(num_seqs, num_q_heads / num_kv_heads, head_dim);
+    return balanced_ws_bytes(num_q_heads / num_kv_heads, head_dim);
   const int64_t np = num_partitions(max_context_len, partition_size);
   if (partition_size == 0 || np <= 1) return 0;
   return (size_t)num_seqs * (size_t)num_q_heads * (size_t)np * ((size_t)head_dim + 2) * sizeof(float);
@@ -385,8 +387,8 @@ static pa_status decode_impl(void* out, const void* query, const void* k_pool, c
     char* ws = static_cast<char*>(workspace);
     size_t rows;
     if (balanced) {
-      a.ws_cum = reinterpret_cast<int32_t*>(ws);
-      ws += align16(((size_t)num_seqs + 1) * sizeof(int32_t));
+      a.ws_desc = reinterpret_cast<int64_t*>(ws);
+      ws += (size_t)pa::kBalancedMaxWaves * kDescBytes;
       rows = 2 * (size_t)pa::kBalancedMaxWaves * (size_t)heads_per_unit;
     } else {
       rows = (size_t)num_seqs * num_q_heads * (size_t)np;

@@ -338,7 +338,8 @@ struct DecodeArgs {
                               // (balanced mode: 2 slots per wave of H rows each)
   float* ws_m;                // [S, Hq, NP] running max (log2 domain)
   float* ws_l;                // [S, Hq, NP] running sum
-  int32_t* ws_cum;            // balanced mode: [S + 1] tile prefix sums
+  int64_t* ws_desc;           // balanced mode: [kBalancedMaxWaves][4] merge descriptors, one per
+                              // wave boundary: {A0 (< 0: nothing to merge), ntot, output row, pieces}
   int32_t num_seqs, num_q_heads, num_kv_heads;
   int32_t max_blocks_per_seq, num_blocks, max_context_len;
   int32_t partition_size;     // tokens per unit (>= max_context_len when not split)

@@ -1131,8 +1131,6 @@ __global__ __launch_bounds__(NW * kWave) void decode_balanced_kernel(DecodeArgs 
   __shared__ __align__(16) char s_pbuf[NW][Buf::kBytes];
   const int S = a.num_seqs, C = a.head_chunks;
   tile_prefix<NW * kWave>(a, block_size, s_cum, s_wave);
-  if (blockIdx.x == 0)
-    for (int s = threadIdx.x; s <= S; s += NW * kWave) a.ws_cum[s] = s_cum[s];
   // sequences with no tile own no range: their rows are zeros, written here
   for (int s = blockIdx.x; s < S; s += gridDim.x)
     if (s_cum[s + 1] == s_cum[s])
@@ -1145,7 +1143,42 @@ __global__ __launch_bounds__(NW * kWave) void decode_balanced_kernel(DecodeArgs 
   const int64_t ntot = (int64_t)C * s_cum[S];
   int64_t f = range_start(w, ntot, W);
   const int64_t fb = range_start(w + 1, ntot, W);
-  if (f >= fb) return;
+  // The merge descriptor of boundary w (1 <= w < W, at position f): the head
+  // group [A0, A0 + cost) whose real tiles [A0 + X, A0 + cost) it is the first
+  // to split (wave w - 1 holds the first of them), or A0 = -1.  Every
+  // boundary's descriptor is written by its wave in every call, so the merge
+  // never reads one left by an earlier call.
+  int64_t desc[4] = {-1, ntot, 0, 0};
+  if (w >= 1 && f > 0 && f < ntot) {
+    int lo = 0, hi = S - 1;   // the last s with C cum[s] <= f - 1
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if ((int64_t)C * s_cum[mid] <= f - 1) lo = mid; else hi = mid - 1;
+    }
+    const int cost = s_cum[lo + 1] - s_cum[lo];
+    const int cm = (int)((f - 1 - (int64_t)C * s_cum[lo]) / cost);
+    const int64_t A0 = (int64_t)C * s_cum[lo] + (int64_t)cm * cost;
+    const int64_t A = A0 + kSegCost, B = A0 + cost;
+    if (A < f && f < B && range_start(w - 1, ntot, W) <= A) {
+      desc[0] = A0;
+      desc[2] = (int64_t)lo * a.num_q_heads + (int64_t)cm * H;
+      desc[3] = (B * W - 1) / ntot - (w - 1) + 1;   // waves w - 1 .. w_hi
+    }
+  }
+  const int lane = threadIdx.x & (kWave - 1);
+  auto write_desc = [&]() {
+    if (w >= 1 && lane == 0) {
+      int64_t* d = a.ws_desc + 4 * w;
+      d[0] = desc[0];
+      d[1] = desc[1];
+      d[2] = desc[2];
+      d[3] = desc[3];
+    }
+  };
+  if (f >= fb) {
+    write_desc();
+    return;
+  }
   // the sequence holding tile f: the last s with C cum[s] <= f (empty
   // sequences share their successor's cum and are skipped)
   int lo = 0, hi = S - 1;
@@ -1162,7 +1195,6 @@ __global__ __launch_bounds__(NW * kWave) void decode_balanced_kernel(DecodeArgs 
   TblCache tc;
   Buf pb;
   pb.init(s_pbuf[wave], 1);
-  const int lane = threadIdx.x & (kWave - 1);
   while (f < fb) {
     const int n = (int)min((int64_t)(ntc - u), fb - f);
     const int nt = ntc - kSegCost;
@@ -1189,6 +1221,7 @@ __global__ __launch_bounds__(NW * kWave) void decode_balanced_kernel(DecodeArgs 
     }
   }
   pb.template flush<T>(a, lane);   // results of the wave's segments, after its last loads
+  write_desc();
 }
 
 // ============================================================================
@@ -1369,8 +1402,11 @@ __global__ __launch_bounds__(kPartMergeWaves * kWave) void decode_merge_parts_ke
 // found from the wave boundaries.  Boundary w (1 <= w < W, at position
 // b = range_start(w) of the flattened space) merges the head group whose
 // tiles [A, B) it is the first to split: A < b < B and wave w - 1 holds A.
-// Head groups written whole need nothing, so the launch is sized by the
-// boundaries, however many sequences there are.  The waves that shared [A, B)
+// Decode wave w has already found that head group and left it in boundary
+// w's descriptor (output row, cost start A0, piece count), so the merge
+// starts with one load instead of a search of the prefix sums.  Head groups
+// written whole need nothing, so the launch is sized by the boundaries,
+// however many sequences there are.  The waves that shared [A, B)
 // are w_lo = w - 1 .. w_hi; wave w left its piece in slot 2w + (its range
 // starts at or after the head group's cost start A0 = A - X ? 0 : 1), and
 // waves with an empty range wrote nothing.  Per head, lane p holds piece p
@@ -1388,45 +1424,24 @@ constexpr int kMergeHeadWaves = H < kMergeWaves ? H : kMergeWaves;
 template <int H>
 constexpr int kMergeBoundaries = kMergeWaves / kMergeHeadWaves<H>;
 
-// The last s in [0, S) with C cum[s] <= x (cum non-decreasing, cum[0] = 0 <=
-// x): two rounds of a 64-lane ballot for S <= 4096, from global memory.
-__device__ __forceinline__ int find_seq(const int32_t* cum, int S, int C, int64_t x, int lane) {
-  int base = 0, span = S;
-  while (span > 1) {
-    const int step = (span + kWave - 1) / kWave;
-    const int idx = base + lane * step;
-    const bool le = lane * step < span && (int64_t)C * cum[idx] <= x;
-    const int last = __popcll(__ballot(le)) - 1;   // the true lanes are a prefix
-    base += last * step;
-    span = min(step, span - last * step);
-  }
-  return base;
-}
-
 template <class T, int D, int H>
 __global__ __launch_bounds__(kMergeWaves * kWave) void decode_merge_balanced_kernel(DecodeArgs a,
                                                                                    int block_size,
                                                                                    int nwaves) {
   constexpr int EPL = D / kWave;
-  const int C = a.head_chunks;
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t W = nwaves;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   if (wave / kMergeHeadWaves<H> >= kMergeBoundaries<H>) return;
   const int64_t w = (int64_t)blockIdx.x * kMergeBoundaries<H> + wave / kMergeHeadWaves<H>;
   if (w < 1 || w >= W) return;
-  const int64_t ntot = (int64_t)C * a.ws_cum[a.num_seqs];
-  const int64_t b = range_start(w, ntot, W);
-  if (b <= 0 || b >= ntot) return;
-  const int s = __builtin_amdgcn_readfirstlane(find_seq(a.ws_cum, a.num_seqs, C, b - 1, lane));
-  const int ntc = a.ws_cum[s + 1] - a.ws_cum[s];
-  const int c = (int)((b - 1 - (int64_t)C * a.ws_cum[s]) / ntc);
-  const int64_t A0 = (int64_t)C * a.ws_cum[s] + (int64_t)c * ntc;
-  const int64_t A = A0 + kSegCost, B = A0 + ntc;
-  if (!(A < b && b < B && range_start(w - 1, ntot, W) <= A)) return;
-  const size_t orow = (size_t)s * a.num_q_heads + (size_t)c * H;
-  const int64_t w_lo = w - 1, w_hi = (B * W - 1) / ntot;
-  const int k = (int)(w_hi - w_lo + 1);
+  const int64_t* desc = a.ws_desc + 4 * w;   // written by decode wave w in this call
+  const int64_t A0 = desc[0];
+  if (A0 < 0) return;
+  const int64_t ntot = desc[1];
+  const size_t orow = (size_t)desc[2];
+  const int k = (int)desc[3];
+  const int64_t w_lo = w - 1;
   const int slot_lo = (int)(2 * w_lo + (range_start(w_lo, ntot, W) >= A0 ? 0 : 1));
   auto piece_slot = [&](int p, bool& ok) {
     const int64_t w = w_lo + p;
