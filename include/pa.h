@@ -74,7 +74,8 @@ typedef enum {
   PA_ERR_NO_BLOCKS = 9,   /* block manager: the free blocks do not cover a batch */
   PA_ERR_SEQUENCE = 10,   /* block manager: a sequence id that is not live     */
   PA_ERR_CAPACITY = 11,   /* block manager: a caller's output buffer is too small */
-  PA_ERR_HOST_MEMORY = 12 /* swap: the host buffer is not pinned, GPU-mapped memory */
+  PA_ERR_HOST_MEMORY = 12, /* swap: the host buffer is not pinned, GPU-mapped memory */
+  PA_ERR_UNSUPPORTED = 13 /* this build does not provide the call (pa_debug_violations) */
 } pa_status;
 
 /* In C++ the enum has a fixed 32-bit underlying type, so that any int32 a C
@@ -375,6 +376,29 @@ pa_status pa_swap_in(const void* host_src, void* k_pool, void* v_pool, const int
  */
 #define PA_STREAM_READ_PARTIALS 16384
 pa_status pa_stream_read(const void* buf, uint64_t bytes, uint32_t* partials, void* stream);
+
+/*
+ * pa_debug_violations -- what the caller's contract checks of a checked build
+ * found.
+ *
+ * The normal build does not check device-side contents: kernels clamp or skip
+ * whatever breaks the contract stated above (memory stays safe, results for
+ * such inputs are unspecified).  A build with PA_DEBUG_CHECKS=1
+ * (paged_kv_cache_313_amd/_build.py build_checked(): libpagedkv_checked.so,
+ * same ABI) also records, in device flag words, each kind of violation a
+ * kernel met.  This call stores the bits met since the last clear, OR-ed over
+ * all kernels, in *flags, and resets them when clear != 0.
+ *   flags   HOST uint32, written (PA_VIOLATION_* bits)
+ * HOST; unlike every other entry point it synchronises with the device (it
+ * copies the flag words).  The normal build returns PA_ERR_UNSUPPORTED and
+ * makes no HIP call; a NULL flags gives PA_ERR_NULL.
+ */
+#define PA_VIOLATION_TABLE_ID 1u  /* a block-table entry in use was outside [0, num_blocks)         */
+#define PA_VIOLATION_LENGTH 2u    /* a length was negative or above its bound (max_context_len, the
+                                     table's capacity; prefill: query_start ranges, max_query_len)  */
+#define PA_VIOLATION_SLOT 4u      /* an append slot >= num_blocks * block_size                       */
+#define PA_VIOLATION_BLOCK_ID 8u  /* a copy-on-write or swap block id outside [0, num_blocks)        */
+pa_status pa_debug_violations(uint32_t* flags, int32_t clear);
 
 /* Static, human-readable name of a status code.  HOST only. */
 const char* pa_status_string(pa_status status);

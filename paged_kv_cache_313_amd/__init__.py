@@ -22,7 +22,7 @@ __all__ = ["kv_append", "block_copy", "decode_attention", "decode_attention_noal
            "decode_attention_hier",
            "prefill_attention_hier", "decode_workspace_bytes",
            "choose_partition", "swap_out", "swap_in", "swap_buffer", "stream_read", "PagedKVError", "load",
-           "PA_PARTITION_BALANCED", "BlockManager"]
+           "PA_PARTITION_BALANCED", "BlockManager", "debug_violations"]
 
 _DTYPES = {torch.float32: _lib.PA_F32, torch.float16: _lib.PA_F16, torch.bfloat16: _lib.PA_BF16}
 
@@ -158,6 +158,16 @@ def stream_read(buf: torch.Tensor, partials: Optional[torch.Tensor] = None, stre
     st = lib.pa_stream_read(_dev(buf, "buf"), nbytes, _dev(partials, "partials"), _stream(buf, stream))
     _lib.check("pa_stream_read", st)
     return partials
+
+
+def debug_violations(clear: bool = True) -> int:
+    """The PA_VIOLATION_* bits the kernels of a checked build (PA_DEBUG_CHECKS)
+    met since the last clear; synchronises the device.  The normal build
+    raises PagedKVError (PA_ERR_UNSUPPORTED)."""
+    import ctypes
+    flags = ctypes.c_uint32(0)
+    _lib.check("pa_debug_violations", load().pa_debug_violations(ctypes.byref(flags), 1 if clear else 0))
+    return int(flags.value)
 
 
 def decode_workspace_bytes(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int,

@@ -65,28 +65,38 @@ def extra_defines() -> list:
     return defs
 
 
-def build(verbose: bool = False, jobs: int = 8) -> str:
+CHECKED_DIR = os.path.join(BUILD_DIR, "checked")
+CHECKED_LIB = os.path.join(HERE, "libpagedkv_checked.so")
+
+
+def build_checked(verbose: bool = False, jobs: int = 8) -> str:
+    """The same library with the caller's-contract checks compiled in
+    (PA_DEBUG_CHECKS=1): libpagedkv_checked.so, read with pa_debug_violations."""
+    return build(verbose, jobs, defines=["-DPA_DEBUG_CHECKS=1"], obj_dir=CHECKED_DIR, lib_path=CHECKED_LIB)
+
+
+def build(verbose: bool = False, jobs: int = 8, defines=(), obj_dir: str = BUILD_DIR, lib_path: str = LIB_PATH) -> str:
     """Compile every source and link libpagedkv.so (always rebuilds)."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
+    os.makedirs(obj_dir, exist_ok=True)
     cc = hipcc()
     objs = []
     cmds = []
-    defs = extra_defines()
+    defs = extra_defines() + list(defines)
     for src in SOURCES:
-        obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
+        obj = os.path.join(obj_dir, os.path.splitext(src)[0] + ".o")
         objs.append(obj)
         cmds.append([cc, *COMPILE_FLAGS, *SOURCE_FLAGS.get(src, []), *defs, "-c", os.path.join(CSRC, src),
                      "-o", obj])
     with ThreadPoolExecutor(max_workers=max(1, min(jobs, len(cmds)))) as ex:
         logs = list(ex.map(_run, cmds))
-    tmp = LIB_PATH + ".tmp"
+    tmp = lib_path + ".tmp"
     logs.append(_run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]))
-    os.replace(tmp, LIB_PATH)
+    os.replace(tmp, lib_path)
     if verbose:
         for log in logs:
             if log.strip():
                 print(log)
-    return LIB_PATH
+    return lib_path
 
 
 # Host sanitizer build: the host-side translation units (the C ABI's checks
@@ -134,3 +144,5 @@ def build_sanitized() -> str:
 if __name__ == "__main__":
     path = build(verbose="-v" in sys.argv)
     print(path)
+    if "--checked" in sys.argv:
+        print(build_checked(verbose="-v" in sys.argv))

@@ -9,6 +9,7 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 # PAGEDKV_LIB names another build of the same ABI (e.g. the host sanitizer build)
 LIB_PATH = os.environ.get("PAGEDKV_LIB") or os.path.join(HERE, "libpagedkv.so")
+CHECKED_LIB_PATH = os.path.join(HERE, "libpagedkv_checked.so")   # PA_DEBUG_CHECKS=1 build
 
 PA_OK = 0
 PA_F32, PA_F16, PA_BF16 = 0, 1, 2
@@ -18,7 +19,8 @@ PA_PARTITION_BALANCED = -1
 STATUS_NAMES = {0: "PA_OK", 1: "PA_ERR_NULL", 2: "PA_ERR_SHAPE", 3: "PA_ERR_BLOCK_SIZE",
                 4: "PA_ERR_DTYPE", 5: "PA_ERR_PARTITION", 6: "PA_ERR_WORKSPACE", 7: "PA_ERR_HIP",
                 8: "PA_ERR_ALIGN", 9: "PA_ERR_NO_BLOCKS", 10: "PA_ERR_SEQUENCE", 11: "PA_ERR_CAPACITY",
-                12: "PA_ERR_HOST_MEMORY"}
+                12: "PA_ERR_HOST_MEMORY", 13: "PA_ERR_UNSUPPORTED"}
+PA_VIOLATION_TABLE_ID, PA_VIOLATION_LENGTH, PA_VIOLATION_SLOT, PA_VIOLATION_BLOCK_ID = 1, 2, 4, 8   # include/pa.h
 
 _c_i32, _c_i64, _c_size, _c_f32, _vp = (ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t,
                                         ctypes.c_float, ctypes.c_void_p)
@@ -47,6 +49,7 @@ SIGNATURES = {
     "pa_swap_in": (_c_i32, [_vp, _vp, _vp, _vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _vp]),
     "pa_stream_read": (_c_i32, [_vp, ctypes.c_uint64, _vp, _vp]),
     "pa_status_string": (ctypes.c_char_p, [_c_i32]),
+    "pa_debug_violations": (_c_i32, [ctypes.POINTER(ctypes.c_uint32), _c_i32]),
     # include/pa_block_manager.h (host only)
     "pa_bm_create": (_c_i32, [_c_i32, _c_i32, ctypes.POINTER(_vp)]),
     "pa_bm_destroy": (None, [_vp]),

@@ -104,6 +104,8 @@ PA_EXPORT const char* pa_status_string(pa_status s) {
     case PA_ERR_CAPACITY: return "PA_ERR_CAPACITY: an output buffer is too small";
     case PA_ERR_HOST_MEMORY:
       return "PA_ERR_HOST_MEMORY: the host buffer is not pinned memory mapped for the GPU";
+    case PA_ERR_UNSUPPORTED:
+      return "PA_ERR_UNSUPPORTED: this build of the library does not provide the call";
   }
   return "unknown pa_status";
 }
@@ -453,4 +455,25 @@ PA_EXPORT pa_status pa_decode_attention_noalloc(void* out, const void* query, co
   return decode_impl(out, query, k_pool, v_pool, block_tables, context_lens, num_seqs, num_q_heads,
                      num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks, max_context_len,
                      scale, partition_size, dtype, nullptr, 0, stream, HierTables{}, true);
+}
+
+PA_EXPORT pa_status pa_debug_violations(uint32_t* flags, int32_t clear) {
+  if (!flags) return PA_ERR_NULL;
+#if PA_DEBUG_CHECKS
+  hipError_t (*const units[])(uint32_t*, bool) = {pa::debug_violations_decode_f32, pa::debug_violations_decode_f16,
+                                                  pa::debug_violations_decode_bf16, pa::debug_violations_prefill,
+                                                  pa::debug_violations_copy};
+  uint32_t all = 0;
+  for (auto unit : units) {
+    uint32_t f = 0;
+    const hipError_t e = unit(&f, clear != 0);
+    if (e != hipSuccess) return hip_status(e);
+    all |= f;
+  }
+  *flags = all;
+  return PA_OK;
+#else
+  (void)clear;
+  return PA_ERR_UNSUPPORTED;
+#endif
 }

@@ -6,6 +6,41 @@
 
 namespace pa {
 
+// Contract checks (builds with PA_DEBUG_CHECKS=1 only).  Every kernel clamps
+// or skips what breaks the caller's contract (a table entry outside the pool,
+// a length above its bound, a slot or block id out of range); a checked build
+// also records each kind in this translation unit's flag word, which
+// pa_debug_violations() reads and clears.  Bits as in include/pa.h.
+#ifndef PA_DEBUG_CHECKS
+#define PA_DEBUG_CHECKS 0
+#endif
+constexpr uint32_t kViolationTableId = 1u;   // PA_VIOLATION_TABLE_ID
+constexpr uint32_t kViolationLength = 2u;    // PA_VIOLATION_LENGTH
+constexpr uint32_t kViolationSlot = 4u;      // PA_VIOLATION_SLOT
+constexpr uint32_t kViolationBlockId = 8u;   // PA_VIOLATION_BLOCK_ID
+#if PA_DEBUG_CHECKS
+static __device__ uint32_t violations;
+#define PA_FLAG_IF(cond, bit)                           \
+  do {                                                  \
+    if (cond) atomicOr(&::pa::violations, (bit));       \
+  } while (0)
+// host side of one translation unit: read (and optionally clear) its flags
+#define PA_VIOLATIONS_GETTER(name)                                                  \
+  hipError_t name(uint32_t* flags, bool clear) {                                    \
+    hipError_t e = hipMemcpyFromSymbol(flags, HIP_SYMBOL(violations), sizeof(uint32_t)); \
+    if (e != hipSuccess || !clear) return e;                                        \
+    const uint32_t zero = 0;                                                        \
+    return hipMemcpyToSymbol(HIP_SYMBOL(violations), &zero, sizeof(uint32_t));      \
+  }
+#else
+#define PA_FLAG_IF(cond, bit) ((void)0)
+#define PA_VIOLATIONS_GETTER(name)                     \
+  hipError_t name(uint32_t* flags, bool) {             \
+    *flags = 0;                                        \
+    return hipSuccess;                                 \
+  }
+#endif
+
 constexpr int kWave = 64;
 constexpr int kNumXcd = 8;          // MI355X: 8 XCDs of 32 CUs, workgroups dealt round-robin
 constexpr float kLog2e = 1.4426950408889634f;
@@ -422,6 +457,7 @@ __device__ __forceinline__ TableView table_view(const Args& a, int s) {
 __device__ __forceinline__ int clamp_len(const DecodeArgs& a, int s, int block_size) {
   int L = a.context_lens[s];
   const int cap_tbl = table_view(a, s).capacity * block_size;
+  PA_FLAG_IF(L < 0 || L > cap_tbl || L > a.max_context_len, kViolationLength);
   L = L < 0 ? 0 : L;
   L = L > cap_tbl ? cap_tbl : L;
   L = L > a.max_context_len ? a.max_context_len : L;

@@ -38,6 +38,7 @@ __global__ __launch_bounds__(256) void kv_append_kernel(
     const int64_t t = i / per_token;
     const int32_t r = (int32_t)(i - t * per_token);
     const int64_t slot = slot_mapping[t];
+    PA_FLAG_IF(slot >= num_slots, kViolationSlot);
     if (slot < 0 || slot >= num_slots) continue;
     const int32_t h = r / chunks_per_row;
     const int32_t c = r - h * chunks_per_row;
@@ -63,6 +64,7 @@ __global__ __launch_bounds__(kCopyThreads) void block_copy_kernel(
   u32x4* pool = (blockIdx.x & 1) ? v_pool : k_pool;
   const int32_t src = block_mapping[2 * pair];
   const int32_t dst = block_mapping[2 * pair + 1];
+  PA_FLAG_IF(src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks, kViolationBlockId);
   if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return;
   const u32x4* s = pool + (int64_t)src * chunks_per_block;
   u32x4* d = pool + (int64_t)dst * chunks_per_block;
@@ -97,6 +99,7 @@ __global__ __launch_bounds__(kCopyThreads) void swap_kernel(u32x4* __restrict__ 
   const int32_t entry = blockIdx.x >> 1;
   const int32_t kv = blockIdx.x & 1;
   const int32_t id = block_ids[entry];
+  PA_FLAG_IF(id < 0 || id >= num_blocks, kViolationBlockId);
   if (id < 0 || id >= num_blocks) return;
   u32x4* pool = (kv ? v_pool : k_pool) + (int64_t)id * chunks_per_block;
   u32x4* h = host + ((int64_t)entry * 2 + kv) * chunks_per_block;
@@ -199,5 +202,7 @@ hipError_t launch_block_copy(void* k_pool, void* v_pool, const int32_t* block_ma
                      block_mapping, chunks, num_blocks);
   return hipGetLastError();
 }
+
+PA_VIOLATIONS_GETTER(debug_violations_copy)
 
 }  // namespace pa

@@ -8,4 +8,6 @@ hipError_t launch_decode_bf16(const DecodeArgs& a, int head_dim, int block_size,
   return dispatch_t<BF16>(a, head_dim, block_size, group, st);
 }
 
+PA_VIOLATIONS_GETTER(debug_violations_decode_bf16)
+
 }  // namespace pa

@@ -77,6 +77,7 @@ __device__ __forceinline__ int stage_table_wave(int32_t* tbl, const DecodeArgs& 
   if constexpr (!SPLIT) {   // unit mode: every tile under the default policy
     for (int i = lane; i < count; i += kWave) {
       const int e = row.entry(first + i);
+      PA_FLAG_IF((unsigned)e >= (unsigned)a.num_blocks, kViolationTableId);
       tbl[i] = ((unsigned)e < (unsigned)a.num_blocks) ? e : 0;
     }
     __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
@@ -112,6 +113,7 @@ __device__ __forceinline__ int stage_table_wave(int32_t* tbl, const DecodeArgs& 
     if (i < count) {
       const int j = first + i;
       unshared = !((j < nprev && ep[k] == e[k]) || (j < nnext && en[k] == e[k]));
+      PA_FLAG_IF((unsigned)e[k] >= (unsigned)a.num_blocks, kViolationTableId);
       tbl[i] = ((unsigned)e[k] < (unsigned)a.num_blocks) ? e[k] : 0;
     }
     const uint64_t m = __ballot(unshared);

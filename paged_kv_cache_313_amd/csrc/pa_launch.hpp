@@ -44,6 +44,14 @@ hipError_t launch_decode_f32(const DecodeArgs& args, int head_dim, int block_siz
 hipError_t launch_decode_f16(const DecodeArgs& args, int head_dim, int block_size, int group, hipStream_t stream);
 hipError_t launch_decode_bf16(const DecodeArgs& args, int head_dim, int block_size, int group, hipStream_t stream);
 
+// Contract-violation flags of each translation unit (zero unless built with
+// PA_DEBUG_CHECKS=1); read, and cleared when asked, synchronously.
+hipError_t debug_violations_decode_f32(uint32_t* flags, bool clear);
+hipError_t debug_violations_decode_f16(uint32_t* flags, bool clear);
+hipError_t debug_violations_decode_bf16(uint32_t* flags, bool clear);
+hipError_t debug_violations_prefill(uint32_t* flags, bool clear);
+hipError_t debug_violations_copy(uint32_t* flags, bool clear);
+
 // Device scratch of the no-allocation decode entry point: a file-scope
 // __device__ array of kDecodeScratchBytes, one per GPU, whose device address
 // is looked up once per device (with that device current) and cached.

@@ -150,6 +150,10 @@ __global__ __launch_bounds__(NW * kWave) void prefill_kernel(PrefillArgs a, int 
   const int n = a.query_start[s + 1] - q0;
   const TableView trow = table_view(a, s);
   const int L = min(a.context_lens[s], trow.capacity * block_size);
+  PA_FLAG_IF(threadIdx.x == 0 && qb == 0 &&
+                 (a.context_lens[s] > trow.capacity * block_size || q0 < 0 || n < 0 || n > a.num_tokens - q0 ||
+                  n > L || n > a.max_query_len),
+             kViolationLength);
   if (q0 < 0 || n <= 0 || n > a.num_tokens - q0 || qb * QB >= n || n > L) return;
 
   const int tid = threadIdx.x;
@@ -215,6 +219,7 @@ __global__ __launch_bounds__(NW * kWave) void prefill_kernel(PrefillArgs a, int 
 #pragma unroll
     for (int jp = 0; jp < Lay::NPAIR; ++jp) {
       const int te = min(t0 + pair_key(jp), last_pair);
+      PA_FLAG_IF((unsigned)ids[jp] >= (unsigned)a.num_blocks, kViolationTableId);
       const int blk = ((unsigned)ids[jp] < (unsigned)a.num_blocks) ? ids[jp] : 0;
       const size_t off =
           ((((size_t)blk * a.num_kv_heads + g) * block_size + (te & bmask)) * D + pair_dch(jp) * 8) * 2;
@@ -474,6 +479,8 @@ static hipError_t prefill_group(const PrefillArgs& a, int bs, int group, hipStre
   return a.max_query_len <= PA_PREFILL_WIDE_MAX_QUERY ? prefill_waves<T, D, 8>(a, bs, group, st)
                                                       : prefill_waves<T, D, 4>(a, bs, group, st);
 }
+
+PA_VIOLATIONS_GETTER(debug_violations_prefill)
 
 hipError_t launch_prefill(const PrefillArgs& a, Elem elem, int head_dim, int block_size, int group,
                           hipStream_t stream) {

@@ -54,7 +54,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for code in range(12):
+    for code in range(14):
         s = lib.pa_status_string(code).decode()
         assert s.startswith(_lib.STATUS_NAMES[code])
     assert lib.pa_last_hip_error() == 0
@@ -246,3 +246,14 @@ def test_stream_read_binding_refuses_cpu_tensors(lib):
     import torch
     with pytest.raises(ValueError, match="GPU"):
         P.stream_read(torch.zeros(64, dtype=torch.int32))
+
+
+def test_debug_violations_unsupported_in_normal_build(lib):
+    # the normal build has no contract checks and makes no HIP call here
+    flags = ctypes.c_uint32(7)
+    if _lib.LIB_PATH.endswith("libpagedkv.so"):
+        assert lib.pa_debug_violations(ctypes.byref(flags), 1) == 13
+        assert flags.value == 7
+        with pytest.raises(P.PagedKVError, match="UNSUPPORTED"):
+            P.debug_violations()
+    assert lib.pa_debug_violations(None, 0) == 1

@@ -1,0 +1,107 @@
+"""The contract-checking build (PA_DEBUG_CHECKS=1, libpagedkv_checked.so):
+inputs that break the caller's contract -- a block-table entry outside the
+pool, a context length above its bound, an append slot past the pool, a
+copy-on-write pair with an id outside the pool -- are still handled safely
+(clamped or skipped, as in the normal build) and are now reported by
+pa_debug_violations, one bit per kind; a clean step reports nothing, and the
+checked build's outputs equal the normal build's bit for bit."""
+
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_313_amd as P
+from paged_kv_cache_313_amd import _lib
+from workloads import synth as W
+from workloads import torch_io
+
+from gpu_util import check_close, gpu_out_f64, note, oracle_out
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture()
+def checked():
+    if not os.path.exists(_lib.CHECKED_LIB_PATH):
+        pytest.fail("libpagedkv_checked.so not built (paged_kv_cache_313_amd._build.build_checked)")
+    normal = _lib.load()
+    lib = _lib.load(_lib.CHECKED_LIB_PATH)
+    _lib._LIB = lib
+    try:
+        P.debug_violations(clear=True)
+        yield lib, normal
+    finally:
+        _lib._LIB = normal
+
+
+def batch(dtype="bf16", G=4, lens=(40, 300, 17), seed=8):
+    return W.make_decode_batch(seed, num_seqs=len(lens), num_q_heads=2 * G, num_kv_heads=2, head_dim=128,
+                               dtype=dtype, block_size=16, context_lens=list(lens), append=True)
+
+
+def step(b, d, partition):
+    P.kv_append(d.new_key, d.new_value, d.k_pool, d.v_pool, d.slot_mapping)
+    out = P.decode_attention(d.query, d.k_pool, d.v_pool, d.block_tables, d.context_lens, b.scale,
+                             b.max_context_len, partition)
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("partition", [-1, 64, 0])
+def test_clean_step_reports_nothing_and_matches_normal_build(checked, partition):
+    b = batch()
+    note(f"checked build, clean step P={partition}")
+    d = torch_io.to_device(b)
+    out = step(b, d, partition)
+    assert P.debug_violations() == 0
+    check_close(gpu_out_f64(out, "bf16"), oracle_out(b), "bf16", "checked build")
+    lib, normal = checked
+    _lib._LIB = normal   # the normal build on the same inputs gives the same bits
+    d2 = torch_io.to_device(b)
+    ref = step(b, d2, partition)
+    _lib._LIB = lib
+    assert torch_io.torch_to_storage(out, "bf16").tobytes() == torch_io.torch_to_storage(ref, "bf16").tobytes()
+
+
+@pytest.mark.parametrize("partition", [-1, 64])
+def test_table_entry_outside_the_pool_is_reported(checked, partition):
+    b = batch()
+    b.block_tables = b.block_tables.copy()
+    b.block_tables[1, 3] = b.num_blocks + 5          # an entry the 300-token sequence uses
+    note(f"checked build, bad table entry P={partition}")
+    d = torch_io.to_device(b)
+    step(b, d, partition)
+    assert P.debug_violations() & _lib.PA_VIOLATION_TABLE_ID
+    assert P.debug_violations() == 0                 # cleared by the previous call
+
+
+def test_length_above_its_bound_is_reported(checked):
+    b = batch()
+    note("checked build, length above max_context_len")
+    d = torch_io.to_device(b)
+    P.kv_append(d.new_key, d.new_value, d.k_pool, d.v_pool, d.slot_mapping)
+    P.decode_attention(d.query, d.k_pool, d.v_pool, d.block_tables, d.context_lens, b.scale, 100, -1)
+    torch.cuda.synchronize()
+    assert P.debug_violations() == _lib.PA_VIOLATION_LENGTH   # 300 > 100: clamped and reported
+
+
+def test_slot_and_copy_pair_outside_the_pool_are_reported(checked):
+    b = batch()
+    note("checked build, bad slot and CoW pair")
+    d = torch_io.to_device(b)
+    slots = d.slot_mapping.clone()
+    slots[0] = b.num_blocks * b.block_size + 3
+    P.kv_append(d.new_key, d.new_value, d.k_pool, d.v_pool, slots)
+    torch.cuda.synchronize()
+    assert P.debug_violations() == _lib.PA_VIOLATION_SLOT
+    pairs = torch.tensor([[0, 1], [b.num_blocks, 2]], dtype=torch.int32, device="cuda")
+    P.block_copy(d.k_pool, d.v_pool, pairs)
+    torch.cuda.synchronize()
+    assert P.debug_violations() == _lib.PA_VIOLATION_BLOCK_ID
+    # negative slots are the contract's "skip", not a violation
+    slots[0] = -1
+    P.kv_append(d.new_key, d.new_value, d.k_pool, d.v_pool, slots)
+    torch.cuda.synchronize()
+    assert P.debug_violations() == 0
