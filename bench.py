@@ -69,6 +69,8 @@ def parse_args():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-swap", action="store_true", help="skip the swap (preemption traffic) leg")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill leg")
+    ap.add_argument("--no-aux", action="store_true",
+                    help="skip the cold-cache, achievable-read, step-latency and block-manager legs (profiled runs)")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of HIP-graph replays")
     ap.add_argument("--prefill-only", action="store_true",
                     help="only time pa_prefill_attention on the chunked-prefill workload and print its line")
@@ -136,8 +138,10 @@ def ingest_counters(root, config=3, partition=-1, out_path=None, block_size=16, 
         return ks[0]
     if partition == -1:
         dk, mk = pick(fetch, "decode_balanced_kernel"), pick(fetch, "decode_merge_balanced_kernel")
-    elif partition > 0:
-        dk, mk = pick(fetch, "decode_unit_kernel"), pick(fetch, "decode_merge_parts_kernel")
+    elif partition > 0:   # fixed partitions: the resident-grid kernel (the unit kernel above 4096 sequences)
+        resident = [k for k in fetch if "decode_parts_resident_kernel" in k]
+        dk = pick(fetch, "decode_parts_resident_kernel" if resident else "decode_unit_kernel")
+        mk = pick(fetch, "decode_merge_parts_kernel")
     else:
         dk, mk = pick(fetch, "decode_unit_kernel"), None
     dec_f, dec_w = fetch[dk] * 1024 * ff, write[dk] * 1024 * wf
@@ -388,11 +392,13 @@ def unique_kv_bytes(b):
 
 
 def decode_kernel_name(b, part):
-    core = "MfmaCore" if b.num_q_heads != b.num_kv_heads and b.dtype != "f32" else "ValuCore"
+    G = b.num_q_heads // b.num_kv_heads
+    core = "ValuCore" if G == 1 or b.dtype == "f32" else ("MfmaPvCore" if G >= 8 and b.head_dim == 128 else "MfmaCore")
     if part == -1:
         return f"pa_decode_attention: decode_balanced_kernel<{core}> + decode_merge_balanced_kernel"
     if part and part > 0:
-        return f"pa_decode_attention: decode_unit_kernel<{core}> + decode_merge_parts_kernel"
+        kern = "decode_parts_resident_kernel" if b.num_seqs <= 4096 else "decode_unit_kernel"
+        return f"pa_decode_attention: {kern}<{core}> + decode_merge_parts_kernel"
     return f"pa_decode_attention: decode_unit_kernel<{core}>"
 
 
@@ -820,14 +826,16 @@ def main():
     # sequences share (prefix-shared sampling) are one HBM read at best
     alg_unique = alg_bytes - kv_bytes + uniq_kv
     achieved = alg_unique / (dec_ms * 1e-3) / 1e9
-    latency = step_latency_leg(step_fn, stream, graphs, max(K, 20))
+    latency = None if args.no_aux else step_latency_leg(step_fn, stream, graphs, max(K, 20))
 
-    cold = cold_decode_leg(decode_only, stream)
-    cold["kv_read_gbps"] = kv_bytes / (cold["decode_ms_median"] * 1e-3) / 1e9
-    cold["pct_of_hbm_peak"] = 100.0 * alg_unique / (cold["decode_ms_median"] * 1e-3) / 1e9 / HBM_PEAK_GBPS
-    stream_leg = achievable_read_leg(stream)
-    stream_leg["decode_frac_of_achievable"] = achieved / stream_leg["gbps"]
-    bm_leg = block_manager_leg(b, max(args.steps, 10))
+    cold = stream_leg = bm_leg = None
+    if not args.no_aux:
+        cold = cold_decode_leg(decode_only, stream)
+        cold["kv_read_gbps"] = kv_bytes / (cold["decode_ms_median"] * 1e-3) / 1e9
+        cold["pct_of_hbm_peak"] = 100.0 * alg_unique / (cold["decode_ms_median"] * 1e-3) / 1e9 / HBM_PEAK_GBPS
+        stream_leg = achievable_read_leg(stream)
+        stream_leg["decode_frac_of_achievable"] = achieved / stream_leg["gbps"]
+        bm_leg = block_manager_leg(b, max(args.steps, 10))
     swap = None if args.no_swap else swap_leg(d, b)
     prefill = None if args.no_prefill else prefill_leg(parity_seqs=() if args.no_cpu_baseline else (0, 9))
 

@@ -72,6 +72,15 @@ def test_ingest_partition_modes_name_the_unit_kernels(tmp_path):
     out0 = bench.ingest_counters(str(tmp_path), config=2, partition=0, out_path=str(tmp_path / "z.json"))
     assert out0["merge_kernel"] is None
     assert out0["hbm_bytes_per_launch"] == pytest.approx((100.0 * 2 + 8.0) * 1024)
+    # up to 4096 sequences fixed partitions run on the resident grid
+    RES = UNIT.replace("decode_unit_kernel", "decode_parts_resident_kernel")
+    for d in ("fetch", "write"):
+        import shutil
+        shutil.rmtree(tmp_path / d)
+    write_pass(tmp_path / "fetch", "FETCH_SIZE", [(RES, 50.0), (PARTS, 6.0)])
+    write_pass(tmp_path / "write", "WRITE_SIZE", [(RES, 2.0), (PARTS, 1.0)])
+    out2 = bench.ingest_counters(str(tmp_path), config=5, partition=512, out_path=str(tmp_path / "r.json"))
+    assert out2["kernel"] == RES and out2["hbm_bytes_per_launch"] == pytest.approx(((50.0 + 6.0) * 2 + 3.0) * 1024)
 
 
 def test_counter_files_are_named_by_workload():
