@@ -12,9 +12,9 @@
 // query tokens).  The 128 or 256 query rows of a workgroup are (token, head)
 // pairs of the G heads sharing the KV head, heads fastest: each wave owns two
 // groups of 16.  Keys advance 64 at a time through double-buffered LDS tiles:
-// K row-major, V transposed (d-major), both gathered through the block table
-// by all threads, the next tile's loads in flight while the current one is
-// used.
+// K and V row-major (V's operand comes from gfx950's transposing LDS read),
+// both gathered through the block table by all threads, the next tile's
+// loads in flight while the current one is used.
 //
 // Per tile, each wave computes, for each of its row groups and 16-key slices,
 //   S^T[key][row] = K Q^T          (A = K from LDS, B = its query rows, kept
@@ -82,15 +82,17 @@ __device__ __forceinline__ int vt_swizzle(int row) { return 4 * ((row >> 4) & (k
 __device__ __forceinline__ int vt_pair(int x) {
   return 16 * (x >> 4) + 2 * ((x >> 2) & 3) + (x & 1) + 8 * ((x >> 1) & 1);
 }
-// V staging: 0 stores V transposed (8 dword stores per key pair); 1 keeps V
-// row-major in LDS (two 16-byte stores per key pair, like K) and forms the
-// P.V operand with gfx950's transposing LDS read, two 8-byte reads where the
-// transposed layout needs one 16-byte read.  Both pass the same tests; on the
-// 16 x 512-token chunked prefill the row-major form measured 594-605 us
-// against 589-596 us, so the transposed store stays the default.  The
-// row-major form is the one direct-to-LDS loads could fill.
+// V staging: 1 (the default) keeps V row-major in LDS (two 16-byte stores
+// per key pair, like K) and forms the P.V operand with gfx950's transposing
+// LDS read, two 8-byte reads per operand; 0 stores V transposed (8 dword
+// stores per key pair, one 16-byte operand read).  Both give bit-identical
+// results.  Alternating in one process, 6 times each, the row-major form
+// took 517-605 us against 544-609 us on the 16 x 512-token chunked prefill
+// and 816-872 us against 830-882 us on 4 fresh 4096-token prompts.
+// Filling the tiles with gfx950's global-to-LDS loads instead of registers
+// (1 KiB runs, padded or swizzled images) was slower: 645-726 us.
 #ifndef PA_PREFILL_VTR
-#define PA_PREFILL_VTR 0
+#define PA_PREFILL_VTR 1
 #endif
 template <int D, int NW>
 struct PfLayout {
