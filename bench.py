@@ -489,7 +489,7 @@ def prefill_leg(reps: int = 20, parity_seqs=(0, 9)) -> dict:
     stream = torch.cuda.current_stream()
     f = lambda: P.prefill_attention(qd, d.k_pool, d.v_pool, d.block_tables, d.context_lens, st, b.scale, n,
                                     out=out, stream=stream)
-    for _ in range(3):
+    for _ in range(10):   # warm-up: about 6 ms of calls
         f()
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
