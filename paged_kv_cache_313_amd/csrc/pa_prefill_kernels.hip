@@ -31,6 +31,8 @@
 // with a lazy rescale (a row's reference max moves only when a score exceeds
 // it by more than 2^8), P rounded to the input type for the MFMA, fp32
 // accumulation.
+#include <type_traits>
+
 #include "pa_common.hpp"
 #include "pa_launch.hpp"
 
@@ -233,18 +235,20 @@ __global__ __launch_bounds__(NW * kWave) void prefill_kernel(PrefillArgs a, int 
   };
   // Keys at or past L (only in the tile that holds the context's end) get
   // V = 0: their slots may hold anything, and a zero weight times a NaN is NaN.
-  auto store_tile = [&](int buf, int t0) {
+  // The tile that holds the context's end (TAIL) is stored by its own copy of
+  // the code, so that the other tiles carry no selects for it.
+  auto store_tile_as = [&](auto tail_tag, int buf, int t0) {
+    constexpr bool TAIL = decltype(tail_tag)::value;
     if (!loader) return;
     char* kb = lds + buf * Lay::kBufBytes;
     char* vb = kb + Lay::kKBytes;
-    const bool tail = t0 + kPfKeys > L;   // uniform
 #pragma unroll
     for (int jp = 0; jp < Lay::NPAIR; ++jp) {
       const int key = pair_key(jp), dch = pair_dch(jp);
       *reinterpret_cast<u32x4*>(kb + key * Lay::kRowB + dch * 16) = kreg[2 * jp];
       *reinterpret_cast<u32x4*>(kb + (key + 1) * Lay::kRowB + dch * 16) = kreg[2 * jp + 1];
       u32x4 v0 = vreg[2 * jp], v1 = vreg[2 * jp + 1];
-      if (tail) {
+      if constexpr (TAIL) {
         const u32x4 z = {0u, 0u, 0u, 0u};
         v0 = t0 + key < L ? v0 : z;
         v1 = t0 + key + 1 < L ? v1 : z;
@@ -263,6 +267,12 @@ __global__ __launch_bounds__(NW * kWave) void prefill_kernel(PrefillArgs a, int 
         *reinterpret_cast<uint32_t*>(vb + row * Lay::kVtB + ((pair_pos(jp) ^ vt_swizzle(row)) << 2)) = w;
       }
     }
+  };
+  auto store_tile = [&](int buf, int t0) {
+    if (t0 + kPfKeys > L)   // uniform
+      store_tile_as(std::true_type{}, buf, t0);
+    else
+      store_tile_as(std::false_type{}, buf, t0);
   };
 
   // Row sums come from the matrix cores: a 16 x 32 operand of ones times the
@@ -336,12 +346,13 @@ __global__ __launch_bounds__(NW * kWave) void prefill_kernel(PrefillArgs a, int 
         for (int sub = 0; sub < kPfSub; ++sub)
 #pragma unroll
           for (int i = 0; i < 4; ++i) sc[4 * sub + i] = st[grp][sub][i];
-        if (diag) {
+        if (diag) {   // key kt + 16 sub + i is seen when 16 sub + i <= pos - kt
+          const int dpos = pos[grp] - kt;
 #pragma unroll
           for (int sub = 0; sub < kPfSub; ++sub)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-              sc[4 * sub + i] = (kt + 16 * sub + i <= pos[grp]) ? sc[4 * sub + i] : kNegInf;
+              sc[4 * sub + i] = (16 * sub + i <= dpos) ? sc[4 * sub + i] : kNegInf;
         }
         float tmax = sc[0];
 #pragma unroll
