@@ -855,7 +855,10 @@ def main():
                   "checked": "all outputs vs the fp64 oracle"}
 
     explicit = args.partition is not None
-    ctr = None if args.group not in (None, 4) else counters_from_profile(args.config, part, b.block_size, explicit)
+    # counters were taken on the default workload shapes (shuffled tables, the
+    # workload's own group size) only
+    same_shape = args.group in (None, 4) and args.table_layout == "shuffled"
+    ctr = counters_from_profile(args.config, part, b.block_size, explicit) if same_shape else None
     workload = WORKLOADS[args.config]
     if args.group is not None and args.group != 4:
         workload = workload.replace("32q/8kv heads", f"{8 * args.group}q/8kv heads")
