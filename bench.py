@@ -41,6 +41,7 @@ def counters_file(config, block_size=16, partition=None):
     if partition is not None:
         stem += f"_p{partition}"
     return os.path.join(ROOT, "profiles", stem + "_counters.json")
+SETTLE_S = 0.06   # seconds of whole steps before the timed region (clock settling)
 KERNEL_SOURCES = ["paged_kv_cache_313_amd/csrc/pa_decode_core.hpp",
                   "paged_kv_cache_313_amd/csrc/pa_common.hpp"]
 
@@ -489,7 +490,10 @@ def prefill_leg(reps: int = 20, parity_seqs=(0, 9)) -> dict:
     stream = torch.cuda.current_stream()
     f = lambda: P.prefill_attention(qd, d.k_pool, d.v_pool, d.block_tables, d.context_lens, st, b.scale, n,
                                     out=out, stream=stream)
-    for _ in range(10):   # warm-up: about 6 ms of calls
+    # warm-up: the leg follows the swap leg, during which the GPU is mostly
+    # idle, and from there the first ~50 calls (~30 ms) ran up to 20 % slower
+    # while the clock settled; 100 calls (~55 ms) reach the steady rate.
+    for _ in range(100):
         f()
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
@@ -798,6 +802,18 @@ def main():
             print(f"[bench] graph capture failed ({exc}); timing eager launches", file=sys.stderr, flush=True)
             graphs = None
             torch.cuda.synchronize()
+    # Settle the clock: after lighter work the GPU takes a few tens of ms of
+    # load to reach its steady clock (on the prefill the first ~30 ms of
+    # calls ran up to 20 % slower), so whole steps run for SETTLE_S first.
+    t_settle = time.perf_counter() + SETTLE_S
+    while True:
+        if graphs:
+            graphs["step"].replay()
+        else:
+            step_fn(stream)
+        torch.cuda.synchronize()
+        if time.perf_counter() >= t_settle:
+            break
     timing = f"one HIP graph of {K} steps" if graphs else "eager launches"
     print(f"[bench] warmup done ({args.warmup} steps), timing {K} steps ({timing})", file=sys.stderr, flush=True)
 
@@ -873,7 +889,7 @@ def main():
         "unit": "seq-steps/s",
         "n_gpus": 1,
         "steps": args.steps,
-        "warmup": args.warmup,
+        "warmup": args.warmup, "settle_s": SETTLE_S,
         "ms_per_step": ms_per_step,
         "higher_is_better": True,
         "scaling": "weak",

@@ -88,11 +88,11 @@ __device__ __forceinline__ int vt_pair(int x) {
 // per key pair, like K) and forms the P.V operand with gfx950's transposing
 // LDS read, two 8-byte reads per operand; 0 stores V transposed (8 dword
 // stores per key pair, one 16-byte operand read).  Both give bit-identical
-// results.  Alternating in one process, 6 times each, the row-major form
-// took 517-605 us against 544-609 us on the 16 x 512-token chunked prefill
-// and 816-872 us against 830-882 us on 4 fresh 4096-token prompts.
-// Filling the tiles with gfx950's global-to-LDS loads instead of registers
-// (1 KiB runs, padded or swizzled images) was slower: 645-726 us.
+// results.  Timed after 30 warm-up calls each, in alternating order: equal
+// on the 16 x 512-token chunked prefill (medians 502-514 us for both and the
+// later changes), 1-2 % faster on 4 fresh 4096-token prompts.  Filling the
+// tiles with gfx950's global-to-LDS loads instead of registers (1 KiB runs,
+// padded or swizzled images) was slower.
 #ifndef PA_PREFILL_VTR
 #define PA_PREFILL_VTR 1
 #endif
