@@ -116,8 +116,7 @@ pa_status pa_kv_append(const void* key, const void* value, void* k_pool, void* v
  * pa_decode_workspace_bytes -- size of the workspace that pa_decode_attention
  * needs for this shape and partition_size (see there); 0 when none is needed
  * (no split, or a single partition), (size_t)-1 for invalid arguments.  The
- * balanced split's size depends only on the group size Hq/Hkv and head_dim
- * (for a multi-head batch, Hq == Hkv, it is sized for pairs of heads).
+ * balanced split's size depends only on the group size Hq/Hkv and head_dim.
  * HOST only; makes no HIP call.
  */
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,

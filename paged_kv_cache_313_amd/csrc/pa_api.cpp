@@ -50,10 +50,7 @@ size_t align16(size_t x) { return (x + 15) & ~(size_t)15; }
 // m, l).
 constexpr size_t kDescBytes = 4 * sizeof(int64_t);
 size_t balanced_ws_bytes(int32_t group, int32_t head_dim) {
-  // head rows per partial slot: the group, or 2 for multi-head batches (pairs
-  // of heads per unit; fp32 uses one)
-  const size_t per_slot = group < 2 ? 2 : (size_t)group;
-  const size_t rows = 2 * (size_t)pa::kBalancedMaxWaves * per_slot;
+  const size_t rows = 2 * (size_t)pa::kBalancedMaxWaves * (size_t)group;
   return (size_t)pa::kBalancedMaxWaves * kDescBytes + rows * ((size_t)head_dim + 2) * sizeof(float);
 }
 
@@ -351,10 +348,7 @@ static pa_status decode_impl(void* out, const void* query, const void* k_pool, c
   const int64_t np = balanced ? 1 : num_partitions(max_context_len, partition_size);
   const bool split = balanced || np > 1;
   const bool mfma = dtype != PA_F32 && group >= 2;
-  // multi-head fp16/bf16 in the balanced split: each unit streams the K/V of
-  // two consecutive heads (one segment start for twice the bytes)
-  const bool kv_pairs = balanced && group == 1 && dtype != PA_F32 && num_q_heads % 2 == 0;
-  const int32_t heads_per_unit = mfma ? group : kv_pairs ? 2 : (group < 4 ? group : 4);
+  const int32_t heads_per_unit = mfma ? group : (group < 4 ? group : 4);
   const int64_t chunks = mfma ? num_kv_heads : num_q_heads / heads_per_unit;
   const int64_t units = (int64_t)num_seqs * chunks * np;
   if (units > INT32_MAX) return PA_ERR_SHAPE;

@@ -370,8 +370,7 @@ __device__ __forceinline__ void store_zero_rows(const DecodeArgs& a, int s, int 
 }
 
 // ============================================================================
-// VALU core: any dtype, H q heads (1, 2 or 4) of one KV head, or (KVH) H
-// heads of a multi-head batch, each with its own KV head.
+// VALU core: any dtype, H q heads (1, 2 or 4) of one KV head.
 // Lane layout per tile: token slot tt = lane / 4, quarter qp = lane % 4; the
 // lane holds the row bytes [16 (4 j + qp), +16) for j < NL, i.e. D/4
 // elements.  QK^T: v_dot2c_f32_{f16,bf16} (fp32 FMA for fp32) in four
@@ -379,14 +378,10 @@ __device__ __forceinline__ void store_zero_rows(const DecodeArgs& a, int s, int 
 // otherwise.  Each token slot keeps its own running max, sum and accumulator,
 // so the tile loop needs no cross-lane reduction beyond the quad's dot sum;
 // the slots are merged with the log-sum-exp rule at the end of the segment.
-// With KVH the H heads' K/V rows of a token are the H consecutive head rows
-// of its block, so one buffer resource spans the unit's tile of every head:
-// a segment streams H times the bytes of a one-head segment for one start
-// (query load, first-tile latency, epilogue).
 // ============================================================================
-template <int NL, int NKV = 1>
+template <int NL>
 struct ValuBuf {
-  u32x4 k[NKV][NL], v[NKV][NL];
+  u32x4 k[NL], v[NL];
 };
 
 // Resident workgroups per CU of the VALU core's balanced grid (0: as many as
@@ -395,9 +390,8 @@ struct ValuBuf {
 #ifndef PA_VALU_WG_PER_CU
 #define PA_VALU_WG_PER_CU 1
 #endif
-template <class T, int D, int BS, int H, bool KVH = false>
+template <class T, int D, int BS, int H>
 struct ValuCore {
-  static constexpr int NKV = KVH ? H : 1;   // KV heads streamed per tile
   static constexpr int EB = T::bytes;
   static constexpr int ROWB = D * EB;
   static constexpr int NL = ROWB / 64;    // 16-byte loads per lane per token row
@@ -408,9 +402,7 @@ struct ValuCore {
   static_assert(DPL * 4 == D, "layout");
   static_assert(kTblWin * BS % kTile == 0, "window");
   // bytes a tile's buffer resource spans: its 16 rows (8 per block at block_size 8)
-  // of each of the NKV consecutive KV heads (BS rows apart in a block)
-  static constexpr uint32_t kHeadBytes = BS * ROWB;
-  static constexpr uint32_t kTileBytes = (NKV - 1) * kHeadBytes + (BS >= 16 ? kTile : BS) * ROWB;
+  static constexpr uint32_t kTileBytes = (BS >= 16 ? kTile : BS) * ROWB;
 
   // q heads h0 .. h0+H-1 of sequence s over tokens [tok0, tok1), run by one
   // wave; tbl is the wave's LDS window.
@@ -518,7 +510,7 @@ struct ValuCore {
       int nshared;
       const int32_t* tbl = staged_window<BS, SPLIT>(a, tbl_lds, tc, trow, s, fblk, nent, lane, nshared);
 
-      auto load = [&](auto pol, int ti, ValuBuf<NL, NKV>& buf) {
+      auto load = [&](auto pol, int ti, ValuBuf<NL>& buf) {
         constexpr int AUX = decltype(pol)::value;
         size_t lo, hi;
         tile_offsets<BS, ROWB>(tbl, off0 + ti * kTile, nent, blk_stride, lo, hi);
@@ -526,33 +518,25 @@ struct ValuCore {
           const rsrc_t rk = make_rsrc(kbase + lo, kTileBytes);
           const rsrc_t rv = make_rsrc(vbase + lo, kTileBytes);
 #pragma unroll
-          for (int kv = 0; kv < NKV; ++kv)
+          for (int j = 0; j < NL; ++j) buf.k[j] = buf_ld16_aux<AUX>(rk, lane_off + j * 64);
 #pragma unroll
-            for (int j = 0; j < NL; ++j) buf.k[kv][j] = buf_ld16_aux<AUX>(rk, lane_off + kv * kHeadBytes + j * 64);
-#pragma unroll
-          for (int kv = 0; kv < NKV; ++kv)
-#pragma unroll
-            for (int j = 0; j < NL; ++j) buf.v[kv][j] = buf_ld16_aux<AUX>(rv, lane_off + kv * kHeadBytes + j * 64);
+          for (int j = 0; j < NL; ++j) buf.v[j] = buf_ld16_aux<AUX>(rv, lane_off + j * 64);
         } else {  // block_size 8: tokens 8..15 come from the next block
           const size_t off = (hi_blk ? hi : lo) + lane_off;
 #pragma unroll
-          for (int kv = 0; kv < NKV; ++kv)
+          for (int j = 0; j < NL; ++j) buf.k[j] = ld16_aux<AUX>(kbase + off + j * 64);
 #pragma unroll
-            for (int j = 0; j < NL; ++j) buf.k[kv][j] = ld16_aux<AUX>(kbase + off + kv * kHeadBytes + j * 64);
-#pragma unroll
-          for (int kv = 0; kv < NKV; ++kv)
-#pragma unroll
-            for (int j = 0; j < NL; ++j) buf.v[kv][j] = ld16_aux<AUX>(vbase + off + kv * kHeadBytes + j * 64);
+          for (int j = 0; j < NL; ++j) buf.v[j] = ld16_aux<AUX>(vbase + off + j * 64);
         }
       };
-      auto compute = [&](int ti, const ValuBuf<NL, NKV>& buf) {
+      auto compute = [&](int ti, const ValuBuf<NL>& buf) {
         const bool valid = wb + ti * kTile + tt < we;
         float pr[H];
 #pragma unroll
         for (int hh = 0; hh < H; ++hh) {
           float d[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int j = 0; j < NL; ++j) Dot16<T>::run(qraw[hh][j], buf.k[KVH ? hh : 0][j], d);
+          for (int j = 0; j < NL; ++j) Dot16<T>::run(qraw[hh][j], buf.k[j], d);
           float dot = (d[0] + d[1]) + (d[2] + d[3]);
           dot += xor_lane<1>(dot);
           dot += xor_lane<2>(dot);
@@ -572,17 +556,9 @@ struct ValuCore {
 #pragma unroll
         for (int j = 0; j < NL; ++j) {
           const u32x4 z = {0u, 0u, 0u, 0u};
-          if constexpr (KVH) {
+          const u32x4 vj = valid ? buf.v[j] : z;   // tail slots may hold NaN
 #pragma unroll
-            for (int hh = 0; hh < H; ++hh) {
-              const u32x4 vj = valid ? buf.v[hh][j] : z;   // tail slots may hold NaN
-              Axpy16<T>::run(pr[hh], vj, &acc[hh][j * NE]);
-            }
-          } else {
-            const u32x4 vj = valid ? buf.v[0][j] : z;   // tail slots may hold NaN
-#pragma unroll
-            for (int hh = 0; hh < H; ++hh) Axpy16<T>::run(pr[hh], vj, &acc[hh][j * NE]);
-          }
+          for (int hh = 0; hh < H; ++hh) Axpy16<T>::run(pr[hh], vj, &acc[hh][j * NE]);
         }
         if constexpr (PARTS) {   // a partition ends inside the run: write it, start the next
           if (wb + ti * kTile + kTile == pend && pend < tok1) {
@@ -594,7 +570,7 @@ struct ValuCore {
         }
       };
       const int ntiles = (we - wb + kTile - 1) / kTile;
-      run_window<ValuBuf<NL, NKV>, SPLIT>(ntiles, shared_tiles<BS>(nshared, nent, off0, ntiles), load, compute);
+      run_window<ValuBuf<NL>, SPLIT>(ntiles, shared_tiles<BS>(nshared, nent, off0, ntiles), load, compute);
       wb = we;
     }
 
@@ -1601,15 +1577,9 @@ static hipError_t dispatch_bs(const DecodeArgs& a, int group, hipStream_t st) {
       default: break;   // group 1: VALU
     }
   }
-  if (group == 1) {   // multi-head: one head per unit, or pairs of heads (balanced split, 16-bit)
-    switch (a.num_q_heads / a.head_chunks) {
-      case 1: return run_core<ValuCore<T, D, BS, 1>, T, D>(a, BS, st);
-      case 2:
-        if constexpr (!std::is_same<T, F32>::value)
-          if (a.mode == kModeBalanced) return run_core<ValuCore<T, D, BS, 2, true>, T, D>(a, BS, st);
-        return hipErrorInvalidValue;
-      default: return hipErrorInvalidValue;
-    }
+  switch (a.num_q_heads / a.head_chunks) {
+    case 1: return run_core<ValuCore<T, D, BS, 1>, T, D>(a, BS, st);
+    default: break;
   }
   if constexpr (std::is_same<T, F32>::value) {  // fp32 groups: 2 or 4 heads per unit
     switch (a.num_q_heads / a.head_chunks) {

@@ -166,9 +166,8 @@ def test_workspace_size(lib):
     assert f(16, 32, 8, 128, 500, 512) == 0              # one partition: written directly
     assert f(3, 8, 8, 64, 513, 512) == 3 * 8 * 2 * 66 * 4
     # balanced: a 32-byte merge descriptor per wave boundary + 2 slots x 2048 waves x group rows
-    # (2 rows for multi-head batches, whose units may take pairs of heads)
     assert f(256, 32, 8, 128, 8193, -1) == 2048 * 32 + 2 * 2048 * 4 * 130 * 4
-    assert f(5, 8, 8, 64, 100, -1) == 2048 * 32 + 2 * 2048 * 2 * 66 * 4
+    assert f(5, 8, 8, 64, 100, -1) == 2048 * 32 + 2 * 2048 * 1 * 66 * 4
     assert f(-1, 8, 8, 64, 513, 512) == ctypes.c_size_t(-1).value
     assert f(4, 8, 3, 64, 513, 512) == ctypes.c_size_t(-1).value
     assert f(4, 8, 8, 64, 513, -2) == ctypes.c_size_t(-1).value
