@@ -515,8 +515,11 @@ struct ValuCore {
         size_t lo, hi;
         tile_offsets<BS, ROWB>(tbl, off0 + ti * kTile, nent, blk_stride, lo, hi);
         if constexpr (BS >= 16) {  // one block region: SGPR base + lane offset
-          const rsrc_t rk = make_rsrc(kbase + lo, kTileBytes);
-          const rsrc_t rv = make_rsrc(vbase + lo, kTileBytes);
+          // the resource ends at the window's last token: rows past it read
+          // as zeros without a memory access (they are masked below)
+          const uint32_t tb = (uint32_t)min(kTile, we - (wb + ti * kTile)) * ROWB;
+          const rsrc_t rk = make_rsrc(kbase + lo, tb);
+          const rsrc_t rv = make_rsrc(vbase + lo, tb);
 #pragma unroll
           for (int j = 0; j < NL; ++j) buf.k[j] = buf_ld16_aux<AUX>(rk, lane_off + j * 64);
 #pragma unroll
@@ -738,8 +741,11 @@ struct MfmaCore {
         size_t lo, hi;
         tile_offsets<BS, ROWB>(tbl, off0 + ti * kTile, nent, blk_stride, lo, hi);
         if constexpr (BS >= 16) {  // one block region: SGPR base + lane offset
-          const rsrc_t rk = make_rsrc(kbase + lo, kTileBytes);
-          const rsrc_t rv = make_rsrc(vbase + lo, kTileBytes);
+          // the resource ends at the window's last token: rows past it read
+          // as zeros without a memory access (they are masked below)
+          const uint32_t tb = (uint32_t)min(kTile, we - (wb + ti * kTile)) * ROWB;
+          const rsrc_t rk = make_rsrc(kbase + lo, tb);
+          const rsrc_t rv = make_rsrc(vbase + lo, tb);
 #pragma unroll
           for (int i = 0; i < NQK; ++i) buf.k[i] = buf_ld16_aux<AUX>(rk, k_off + i * 64);
 #pragma unroll
@@ -934,8 +940,11 @@ struct MfmaPvCore {
         size_t lo, hi;
         tile_offsets<BS, ROWB>(tbl, off0 + ti * kTile, nent, blk_stride, lo, hi);
         if constexpr (BS >= 16) {  // one block region: SGPR base + lane offset
-          const rsrc_t rk = make_rsrc(kbase + lo, kTileBytes);
-          const rsrc_t rv = make_rsrc(vbase + lo, kTileBytes);
+          // the resource ends at the window's last token: rows past it read
+          // as zeros without a memory access (they are masked below)
+          const uint32_t tb = (uint32_t)min(kTile, we - (wb + ti * kTile)) * ROWB;
+          const rsrc_t rk = make_rsrc(kbase + lo, tb);
+          const rsrc_t rv = make_rsrc(vbase + lo, tb);
 #pragma unroll
           for (int i = 0; i < NQK; ++i) buf.k[i] = buf_ld16_aux<AUX>(rk, k_off + i * 64);
 #pragma unroll
