@@ -401,8 +401,6 @@ struct ValuCore {
   static constexpr int kBalancedWgPerCu = PA_VALU_WG_PER_CU;
   static_assert(DPL * 4 == D, "layout");
   static_assert(kTblWin * BS % kTile == 0, "window");
-  // bytes a tile's buffer resource spans: its 16 rows (8 per block at block_size 8)
-  static constexpr uint32_t kTileBytes = (BS >= 16 ? kTile : BS) * ROWB;
 
   // q heads h0 .. h0+H-1 of sequence s over tokens [tok0, tok1), run by one
   // wave; tbl is the wave's LDS window.
@@ -633,7 +631,6 @@ struct MfmaCore {
   static constexpr int kBalancedWgPerCu = PA_MFMA_WG_PER_CU;
   static_assert(16 % G == 0 && G >= 2, "group");
   static_assert(kTblWin * BS % kTile == 0, "window");
-  static constexpr uint32_t kTileBytes = (BS >= 16 ? kTile : BS) * ROWB;
 
   // the G q heads h0 .. h0+G-1 (KV head h0 / G) of sequence s over tokens
   // [tok0, tok1), run by one wave; tbl is the wave's LDS window.
@@ -861,7 +858,6 @@ struct MfmaPvCore {
   static constexpr int kBalancedWgPerCu = PA_MFMA_WG_PER_CU;
   static_assert(16 % G == 0 && G >= 2, "group");
   static_assert(kTblWin * BS % kTile == 0, "window");
-  static constexpr uint32_t kTileBytes = (BS >= 16 ? kTile : BS) * ROWB;
 
   template <bool SPLIT, bool PARTS = false, bool BUF = PARTS>
   __device__ static void run(const DecodeArgs& a, int32_t* tbl_lds, TblCache& tc, int s, int h0, int tok0,
