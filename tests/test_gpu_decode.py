@@ -186,3 +186,29 @@ def test_resident_partitions_match_unit_kernel_bit_for_bit(dtype, G, bs):
     got = gpu_out_f64(whole, dtype)
     sel = sorted(set(seqs))
     check_close(got[sel], ref[sel], dtype, "resident vs unit")
+
+
+@pytest.mark.parametrize("dtype,G", [("bf16", 4), ("f16", 1)])
+def test_balanced_split_at_its_sequence_limit(dtype, G):
+    """4096 sequences, the most one balanced launch takes: every workgroup's
+    prefix scan covers 16 sequences per thread, empty and one-token sequences
+    are mixed in, and wave ranges cross many sequences.  Sampled sequences
+    (first, last, empty neighbours, the middle) against the oracle, every
+    output finite, and empty sequences exactly zero."""
+    rng = np.random.default_rng(4096)
+    lens = rng.integers(0, 300, size=4096)
+    lens[:4] = [0, 1, 0, 17]
+    lens[-3:] = [0, 299, 1]
+    b = W.make_decode_batch(40, num_seqs=len(lens), num_q_heads=2 * G, num_kv_heads=2, head_dim=128,
+                            dtype=dtype, block_size=16, context_lens=lens.tolist())
+    d = torch_io.to_device(b)
+    note(f"balanced split at 4096 sequences {dtype} G={G}")
+    whole = P.decode_attention(d.query, d.k_pool, d.v_pool, d.block_tables, d.context_lens, b.scale,
+                               b.max_context_len, -1)
+    torch.cuda.synchronize()
+    got = gpu_out_f64(whole, dtype)
+    assert np.isfinite(got).all()
+    sel = sorted(set([0, 1, 2, 3, 2047, 2048, 4093, 4094, 4095] + rng.choice(4096, 12, replace=False).tolist()))
+    check_close(got[sel], oracle_out(b, seqs=sel)[sel], dtype, "4096 sequences")
+    for s in np.flatnonzero(lens == 0):
+        assert (got[s] == 0).all()
