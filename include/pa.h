@@ -75,7 +75,7 @@ typedef enum {
   PA_ERR_SEQUENCE = 10,   /* block manager: a sequence id that is not live     */
   PA_ERR_CAPACITY = 11,   /* block manager: a caller's output buffer is too small */
   PA_ERR_HOST_MEMORY = 12, /* swap: the host buffer is not pinned, GPU-mapped memory */
-  PA_ERR_UNSUPPORTED = 13 /* this build does not provide the call (pa_debug_violations) */
+  PA_ERR_UNSUPPORTED = 13 /* the library was compiled without the call (pa_debug_violations needs PA_DEBUG_CHECKS) */
 } pa_status;
 
 /* In C++ the enum has a fixed 32-bit underlying type, so that any int32 a C

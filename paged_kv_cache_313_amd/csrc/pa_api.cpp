@@ -105,7 +105,7 @@ PA_EXPORT const char* pa_status_string(pa_status s) {
     case PA_ERR_HOST_MEMORY:
       return "PA_ERR_HOST_MEMORY: the host buffer is not pinned memory mapped for the GPU";
     case PA_ERR_UNSUPPORTED:
-      return "PA_ERR_UNSUPPORTED: this build of the library does not provide the call";
+      return "PA_ERR_UNSUPPORTED: the library was compiled without this call (PA_DEBUG_CHECKS)";
   }
   return "unknown pa_status";
 }
