@@ -99,7 +99,13 @@ __device__ __forceinline__ int vt_pair(int x) {
 template <int D, int NW>
 struct PfLayout {
   static constexpr int kThreads = NW * kWave;
-  static constexpr int kRowB = D * 2 + 16;           // K row pitch in LDS (bytes), padded
+  // K row pitch: D + 16 elements.  With 8 elements of padding rocprofv3
+  // counted 31.7 M LDS bank-conflict cycles per chunked-prefill call (D 128;
+  // 15.9 M at D 64), none of them from V (changing V's pitch or its read
+  // left that count alone); with 16 it counts none, and the call is about
+  // 1 % faster.  24 or 32 elements gave the same conflicts as 8; 80 gave
+  // none but ran slower at D 64.
+  static constexpr int kRowB = D * 2 + 32;
   static constexpr int kVtB = kPfKeys * 2 + 16;      // V^T row pitch in LDS (bytes), padded, 16-byte aligned
   // V row pitch: D + 16 elements, so that the 4 rows one transposing read
   // touches (32 bytes each) start 8 dwords apart in the 64 banks
