@@ -8,8 +8,8 @@
 // to the tokens t <= p of the sequence's paged context.  This is a dense
 // contraction on both sides of the softmax, so both run on the matrix cores.
 //
-// Work unit: one workgroup of 4 or 8 waves per (sequence, KV head, block of
-// query tokens).  The 128 or 256 query rows of a workgroup are (token, head)
+// Work unit: one workgroup of 8 waves per (sequence, KV head, block of
+// query tokens).  The 256 query rows of a workgroup are (token, head)
 // pairs of the G heads sharing the KV head, heads fastest: each wave owns two
 // groups of 16.  Keys advance 64 at a time through double-buffered LDS tiles:
 // K and V row-major (V's operand comes from gfx950's transposing LDS read),
@@ -39,14 +39,19 @@
 namespace pa {
 
 // Workgroups of 8 waves (256 query rows) stage each K/V tile once for twice
-// the rows of a 4-wave one; measured, they were 8-14 % faster when every
-// sequence brings at most 2048 new tokens (chunked prefill over a cached
-// prefix, short prompts) and 5-11 % slower on fresh prompts of 4K-8K tokens,
-// whose causal diagonals leave the waves of one workgroup unequal work at
-// each barrier with no second workgroup on the CU to fill the wait.
-#ifndef PA_PREFILL_WIDE_MAX_QUERY
-#define PA_PREFILL_WIDE_MAX_QUERY 2048
+// the rows of a 4-wave one.  With the query blocks handed out longest band
+// first (below) they were faster on every workload measured: 8-14 % on
+// chunked prefill, and on fresh prompts 578 against 606 us (4 x 4K), 1,046
+// against 1,114 us (2 x 8K), 2,029 against 2,187 us (16K), 7,977 against
+// 8,656 us (32K), 3,550 against 4,034 us for 4 x 4K new tokens on 16K
+// contexts (bit-identical results).  Before that order, fresh 4K-8K prompts
+// had run 5-11 % faster in 4-wave workgroups.  PA_PREFILL_WAVES=4 builds the
+// 4-wave form.
+#ifndef PA_PREFILL_WAVES
+#define PA_PREFILL_WAVES 8
 #endif
+constexpr int kPfWaves = PA_PREFILL_WAVES;
+static_assert(kPfWaves == 4 || kPfWaves == 8, "prefill workgroup");
 #ifndef PA_PREFILL_KEYS
 #define PA_PREFILL_KEYS 64
 #endif
@@ -144,12 +149,26 @@ __global__ __launch_bounds__(NW * kWave) void prefill_kernel(PrefillArgs a, int 
   constexpr int NDT = D / 16;              // 16-row d tiles of the output
   __shared__ __align__(16) char lds[2 * Lay::kBufBytes];
 
-  // unit: (sequence, KV head, query block), query block fastest, dealt to
-  // XCDs in runs so that one sequence's blocks share an L2; the last query
-  // block of a sequence (the most keys under the causal mask) goes first
+  // unit: (sequence, KV head, query block).  Query blocks go in bands of 8,
+  // the last band (the most keys under the causal mask) first for every
+  // (sequence, KV head), so that the longest units start first over the
+  // whole grid; within a band a (sequence, KV head)'s blocks are consecutive,
+  // last first, and the 8 of a band form one of xcd_unit's runs, so they
+  // share an L2.  Against the order with each (sequence, KV head)'s blocks
+  // all together, whose last pairs' long blocks started near the end: fresh
+  // 4K prompts 797 -> 590 us, fresh 8K 1,328 -> 1,100 us, 16 x 2,048 new
+  // tokens on 8K contexts 3,979 -> 3,573 us (bit-identical; the same order
+  // when a sequence has at most 8 blocks).  Bands of 4 or no bands at all
+  // (longest first, (sequence, KV head) fastest) were slower on the 2,048-
+  // token chunks: their blocks meet less often in an L2.
+  constexpr uint32_t kBand = 8;
   const uint32_t u = xcd_unit(blockIdx.x, gridDim.x);
-  const int qb = a.qblocks - 1 - (int)(u % (uint32_t)a.qblocks);
-  const int sg = (int)(u / (uint32_t)a.qblocks);
+  const uint32_t SG = (uint32_t)a.num_seqs * (uint32_t)a.num_kv_heads;
+  const uint32_t band = (uint32_t)(u / ((uint64_t)SG * kBand));
+  const uint32_t bw = min(kBand, (uint32_t)a.qblocks - band * kBand);   // blocks in this band
+  const uint32_t rest = (uint32_t)(u - (uint64_t)band * SG * kBand);
+  const int qb = a.qblocks - 1 - (int)(band * kBand + rest % bw);
+  const int sg = (int)(rest / bw);
   const int g = sg % a.num_kv_heads;
   const int s = sg / a.num_kv_heads;
   if (s >= a.num_seqs) return;
@@ -495,8 +514,7 @@ static hipError_t prefill_waves(const PrefillArgs& a, int bs, int group, hipStre
 
 template <class T, int D>
 static hipError_t prefill_group(const PrefillArgs& a, int bs, int group, hipStream_t st) {
-  return a.max_query_len <= PA_PREFILL_WIDE_MAX_QUERY ? prefill_waves<T, D, 8>(a, bs, group, st)
-                                                      : prefill_waves<T, D, 4>(a, bs, group, st);
+  return prefill_waves<T, D, kPfWaves>(a, bs, group, st);
 }
 
 PA_VIOLATIONS_GETTER(debug_violations_prefill)

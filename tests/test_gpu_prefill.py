@@ -63,13 +63,13 @@ CASES = [(dt, D, bs, G) for dt in ("f16", "bf16") for D in (64, 128) for bs in (
 CASES += [("bf16", 128, 16, 2), ("bf16", 128, 16, 8), ("bf16", 128, 16, 16), ("f16", 64, 8, 16)]
 
 
-# The library runs 8-wave workgroups when max_query_len <= 2048 and 4-wave
-# ones above; a host bound above the real n selects the 4-wave kernel (the
-# extra query blocks have no rows and exit).
-NARROW_MAX_QUERY = 4096
+# A host bound far above the real n: the grid holds 8 bands of query blocks,
+# handed out from the band nearest the context's end, and the blocks past a
+# sequence's new tokens have no rows and exit.
+LOOSE_MAX_QUERY = 4096
 
 
-@pytest.mark.parametrize("max_query_len", [None, NARROW_MAX_QUERY], ids=["8waves", "4waves"])
+@pytest.mark.parametrize("max_query_len", [None, LOOSE_MAX_QUERY], ids=["tight", "loose"])
 @pytest.mark.parametrize("dtype,D,bs,G", CASES)
 def test_prefill_matches_oracle(dtype, D, bs, G, max_query_len):
     b, q, starts = case(dtype, D, bs, G, LENS, NEWS, seed=D + bs + G)
@@ -81,7 +81,7 @@ def test_prefill_matches_oracle(dtype, D, bs, G, max_query_len):
                 extra=p_rounding(q, b, starts))
 
 
-@pytest.mark.parametrize("max_query_len", [None, NARROW_MAX_QUERY], ids=["8waves", "4waves"])
+@pytest.mark.parametrize("max_query_len", [None, LOOSE_MAX_QUERY], ids=["tight", "loose"])
 def test_fresh_prompts_and_whole_context(max_query_len):
     """n = L for every sequence: plain causal prefill through the pages."""
     lens = [5, 31, 32, 33, 129]
@@ -123,10 +123,11 @@ def test_rows_not_to_write_are_left_alone():
                 extra=ex[starts[2]:starts[2] + 64])
 
 
-def test_long_fresh_prompt_four_wave_path():
-    """A 2500-token fresh prompt (above the 8-wave bound by itself), GQA 8/2,
-    D 128, bf16: every output vs the oracle."""
-    lens = [2500]
+def test_long_fresh_prompts_several_bands():
+    """Fresh prompts of 2,600 and 700 tokens, GQA 8/2, D 128, bf16: 41 query
+    blocks of 64 tokens for the long one, so 5 full bands of 8 and a band of
+    1, and fewer bands for the short one; every output vs the oracle."""
+    lens = [2600, 700]
     b, q, starts = case("bf16", 128, 16, 4, lens, lens, seed=13)
     note("prefill long fresh prompt")
     out = run(b, q, starts)
