@@ -394,7 +394,7 @@ def unique_kv_bytes(b):
 
 def decode_kernel_name(b, part):
     G = b.num_q_heads // b.num_kv_heads
-    core = "ValuCore" if G == 1 or b.dtype == "f32" else ("MfmaPvCore" if G >= 8 and b.head_dim == 128 else "MfmaCore")
+    core = "ValuCore" if G == 1 or b.dtype == "f32" else ("MfmaPvCore" if G >= 4 and b.head_dim == 128 else "MfmaCore")
     if part == -1:
         return f"pa_decode_attention: decode_balanced_kernel<{core}> + decode_merge_balanced_kernel"
     if part and part > 0:

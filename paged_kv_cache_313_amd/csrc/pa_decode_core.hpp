@@ -845,7 +845,7 @@ struct MfmaCore {
 // MfmaCore's P.V needs G x 36 (2,300 at G = 16).
 // ============================================================================
 #ifndef PA_PV_MFMA_MIN_GROUP
-#define PA_PV_MFMA_MIN_GROUP 8
+#define PA_PV_MFMA_MIN_GROUP 4
 #endif
 template <class T, int D, int BS, int G>
 struct MfmaPvCore {
@@ -1560,9 +1560,13 @@ static hipError_t run_core(const DecodeArgs& a, int bs, hipStream_t st) {
 }
 
 // Grouped queries: P.V on the matrix cores for head_dim 128 and groups of at
-// least PA_PV_MFMA_MIN_GROUP (there the vector P.V of MfmaCore, G x 36
-// instructions per V chunk, bounds the call: 65 % of the HBM peak at G = 8,
-// 32 % at G = 16 on the Llama-3-8B-shaped batch), MfmaCore otherwise.
+// least PA_PV_MFMA_MIN_GROUP, MfmaCore otherwise.  The vector P.V of MfmaCore,
+// G x 36 instructions per V chunk, bounds the call at larger groups (65 % of
+// the HBM peak at G = 8, 32 % at G = 16 on the Llama-3-8B-shaped batch); at
+// G = 4 the HBM-bound batches time the same either way (Llama-3-8B 670.4
+// against 672.5 us, long context 831.4 against 830.9 us), and where shared
+// blocks come from the caches the matrix-core form is 4 % faster
+// (prefix-shared decode 237.3 against 247.7 us).
 template <class T, int D, int BS, int G>
 static hipError_t run_gqa(const DecodeArgs& a, hipStream_t st) {
   if constexpr (D == 128 && G >= PA_PV_MFMA_MIN_GROUP)

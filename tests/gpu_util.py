@@ -55,12 +55,30 @@ def oracle_out(b, k_pool=None, v_pool=None, seqs=None):
                               b.block_size, b.dtype, seqs=seqs)
 
 
-PV_MFMA_MIN_GROUP = 8   # decode groups from this size (head_dim 128) run P.V on the matrix cores
+PV_MFMA_MIN_GROUP = 4   # decode groups from this size (head_dim 128) run P.V on the matrix cores
+
+
+def pv_bound(q, k_pool, v_pool, tables, lens, scale, block_size, dtype, seqs=None, hier=None):
+    """pv_extra for a decode call given by its arrays (hier = (large, num_large,
+    small, pages) for two-level tables): 2^-m times the oracle over |V| when
+    the call's P.V runs on the matrix cores, else None."""
+    G = q.shape[1] // k_pool.shape[1]
+    if dtype == "f32" or q.shape[2] != 128 or G < PV_MFMA_MIN_GROUP:
+        return None
+    from workloads import synth as W
+    vabs = W.to_storage(np.abs(O.upcast(v_pool, dtype)).astype(np.float32), dtype)
+    if hier is not None:
+        large, num_large, small, pages = hier
+        mean = O.decode_attention_hier(q, k_pool, vabs, large, num_large, small, pages, lens, scale, block_size,
+                                       dtype)
+    else:
+        mean = O.decode_attention(q, k_pool, vabs, tables, lens, scale, block_size, dtype, seqs=seqs)
+    return 2.0 ** -MANT_BITS[dtype] * mean
 
 
 def pv_extra(b, k_pool=None, v_pool=None, seqs=None):
     """Allowance for decode batches whose P.V runs on the matrix cores (f16 /
-    bf16, head_dim 128, group >= 8): the probabilities are rounded to the
+    bf16, head_dim 128, group >= 4): the probabilities are rounded to the
     input type (relative error <= u = 2^-(m+1) each) and normalised by the sum
     of the same rounded weights, so each normalised weight is off by at most
     2u / (1 - u) relatively and an output by at most that times

@@ -15,7 +15,7 @@ from oracle.block_manager import BlockManager as RefBM
 from workloads import synth as W
 from workloads import torch_io
 
-from gpu_util import check_close, gpu_out_f64, note
+from gpu_util import check_close, gpu_out_f64, note, pv_bound
 
 pytestmark = pytest.mark.gpu
 
@@ -62,7 +62,8 @@ def test_manager_driven_decode_steps(bs, partition):
                                  int(lens.max()), partition)
         torch.cuda.synchronize()
         want = O.decode_attention(q, k_host, v_host, tables, lens, scale, bs, DT)
-        check_close(gpu_out_f64(out, DT), want, DT, label)
+        check_close(gpu_out_f64(out, DT), want, DT, label,
+                    extra=pv_bound(q, k_host, v_host, tables, lens, scale, bs, DT))
 
     prompts = []
     for plen in (37, 40, 13):                   # partly filled last blocks, and one full
@@ -171,5 +172,6 @@ def test_manager_large_pages_drive_hier_calls():
                                       int(lens.max()), -1)
         torch.cuda.synchronize()
         want = O.decode_attention_hier(q, k_host, v_host, large, nl, small, H, lens, scale, bs, DT)
-        check_close(gpu_out_f64(out, DT), want, DT, f"decode step {t}")
+        check_close(gpu_out_f64(out, DT), want, DT, f"decode step {t}",
+                    extra=pv_bound(q, k_host, v_host, None, lens, scale, bs, DT, hier=(large, nl, small, H)))
     assert torch_io.torch_to_storage(k_dev, DT).tobytes() == k_host.tobytes()

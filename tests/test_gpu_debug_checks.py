@@ -17,7 +17,7 @@ from paged_kv_cache_313_amd import _lib
 from workloads import synth as W
 from workloads import torch_io
 
-from gpu_util import check_close, gpu_out_f64, note, oracle_out
+from gpu_util import check_close, gpu_out_f64, note, oracle_out, pv_extra
 
 pytestmark = pytest.mark.gpu
 
@@ -56,7 +56,7 @@ def test_clean_step_reports_nothing_and_matches_normal_build(checked, partition)
     d = torch_io.to_device(b)
     out = step(b, d, partition)
     assert P.debug_violations() == 0
-    check_close(gpu_out_f64(out, "bf16"), oracle_out(b), "bf16", "checked build")
+    check_close(gpu_out_f64(out, "bf16"), oracle_out(b), "bf16", "checked build", extra=pv_extra(b))
     lib, normal = checked
     _lib._LIB = normal   # the normal build on the same inputs gives the same bits
     d2 = torch_io.to_device(b)

@@ -110,7 +110,7 @@ def test_poisoned_slots_never_leak():
     note("poison")
     out = gpu_out_f64(run(b, 32), "bf16")
     assert np.isfinite(out).all()
-    check_close(out, oracle_out(b), "bf16", "poison")
+    check_close(out, oracle_out(b), "bf16", "poison", extra=pv_extra(b))
 
 
 def test_lengths_clamped_to_max_context_len():
@@ -123,7 +123,7 @@ def test_lengths_clamped_to_max_context_len():
                              64, partition_size=32)
     torch.cuda.synchronize()
     b.context_lens = np.minimum(b.context_lens, 64).astype(np.int32)
-    check_close(gpu_out_f64(out, "bf16"), oracle_out(b), "bf16", "clamp")
+    check_close(gpu_out_f64(out, "bf16"), oracle_out(b), "bf16", "clamp", extra=pv_extra(b))
 
 
 def test_explicit_workspace_and_stream():
@@ -140,7 +140,7 @@ def test_explicit_workspace_and_stream():
         P.decode_attention(d.query, d.k_pool, d.v_pool, d.block_tables, d.context_lens, b.scale,
                            b.max_context_len, 512, out=out, workspace=ws, stream=s)
     s.synchronize()
-    check_close(gpu_out_f64(out, "bf16"), oracle_out(b), "bf16", "workspace")
+    check_close(gpu_out_f64(out, "bf16"), oracle_out(b), "bf16", "workspace", extra=pv_extra(b))
 
 
 @pytest.mark.parametrize("partition", [64, -1])
@@ -158,7 +158,7 @@ def test_split_ignores_stale_workspace(dtype, G, partition):
     out = P.decode_attention(d.query, d.k_pool, d.v_pool, d.block_tables, d.context_lens, b.scale,
                              b.max_context_len, partition, workspace=ws)
     torch.cuda.synchronize()
-    check_close(gpu_out_f64(out, dtype), oracle_out(b), dtype, "stale workspace")
+    check_close(gpu_out_f64(out, dtype), oracle_out(b), dtype, "stale workspace", extra=pv_extra(b))
 
 
 @pytest.mark.parametrize("dtype,G,bs", [("bf16", 4, 16), ("f16", 1, 8), ("f32", 2, 32)])
@@ -185,7 +185,8 @@ def test_resident_partitions_match_unit_kernel_bit_for_bit(dtype, G, bs):
     ref = oracle_out(b, seqs=sorted(set(seqs)))
     got = gpu_out_f64(whole, dtype)
     sel = sorted(set(seqs))
-    check_close(got[sel], ref[sel], dtype, "resident vs unit")
+    ex = pv_extra(b, seqs=sel)
+    check_close(got[sel], ref[sel], dtype, "resident vs unit", extra=None if ex is None else ex[sel])
 
 
 @pytest.mark.parametrize("dtype,G", [("bf16", 4), ("f16", 1)])
@@ -209,6 +210,7 @@ def test_balanced_split_at_its_sequence_limit(dtype, G):
     got = gpu_out_f64(whole, dtype)
     assert np.isfinite(got).all()
     sel = sorted(set([0, 1, 2, 3, 2047, 2048, 4093, 4094, 4095] + rng.choice(4096, 12, replace=False).tolist()))
-    check_close(got[sel], oracle_out(b, seqs=sel)[sel], dtype, "4096 sequences")
+    ex = pv_extra(b, seqs=sel)
+    check_close(got[sel], oracle_out(b, seqs=sel)[sel], dtype, "4096 sequences", extra=None if ex is None else ex[sel])
     for s in np.flatnonzero(lens == 0):
         assert (got[s] == 0).all()

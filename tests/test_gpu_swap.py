@@ -16,7 +16,7 @@ from oracle.block_manager import BlockManager as RefBM
 from workloads import synth as W
 from workloads import torch_io
 
-from gpu_util import check_close, gpu_out_f64, note
+from gpu_util import check_close, gpu_out_f64, note, pv_bound
 
 pytestmark = pytest.mark.gpu
 
@@ -124,7 +124,7 @@ def test_preemption_round_trip_in_decode_steps():
                                  int(lens.max()), -1)
         torch.cuda.synchronize()
         check_close(gpu_out_f64(out, dtype), O.decode_attention(q, k_host, v_host, tables, lens, scale, bs, dtype),
-                    dtype, label)
+                    dtype, label, extra=pv_bound(q, k_host, v_host, tables, lens, scale, bs, dtype))
 
     seqs = [nat.add_sequence() for _ in range(5)]
     assert [ref.add_sequence() for _ in range(5)] == seqs
