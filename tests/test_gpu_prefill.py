@@ -153,3 +153,18 @@ def test_chunked_prefill_at_serving_size():
     for s in seqs:
         sl = slice(starts[s], starts[s + 1])
         check_close(got[sl], ref[sl], "bf16", f"seq {s}", ulps=ULPS, extra=ex[sl])
+
+
+def test_ragged_long_chunks_across_bands():
+    """Sequences bringing 1,500, 700, 2,100, 64 and 1 new tokens on contexts
+    of 4,000, 700 (fresh), 3,000, 5,000 and 900 tokens, GQA 16/4, D 128,
+    bf16: 33 query blocks of 64 tokens for the longest, so the grid has 5
+    bands and in most of them the shorter sequences' blocks have no rows and
+    exit; every output of every sequence vs the oracle."""
+    lens, news = [4000, 700, 3000, 5000, 900], [1500, 700, 2100, 64, 1]
+    b, q, starts = case("bf16", 128, 16, 4, lens, news, Hkv=4, seed=21)
+    note("prefill ragged long chunks")
+    out = run(b, q, starts)
+    ref = O.prefill_attention(q, b.k_pool, b.v_pool, b.block_tables, b.context_lens, starts, b.scale, 16, "bf16")
+    check_close(gpu_out_f64(out, "bf16"), ref, "bf16", "ragged long chunks", ulps=ULPS,
+                extra=p_rounding(q, b, starts))
