@@ -149,25 +149,30 @@ __global__ __launch_bounds__(NW * kWave) void prefill_kernel(PrefillArgs a, int 
   constexpr int NDT = D / 16;              // 16-row d tiles of the output
   __shared__ __align__(16) char lds[2 * Lay::kBufBytes];
 
-  // unit: (sequence, KV head, query block).  Query blocks go in bands of 8,
-  // the last band (the most keys under the causal mask) first for every
-  // (sequence, KV head), so that the longest units start first over the
-  // whole grid; within a band a (sequence, KV head)'s blocks are consecutive,
-  // last first, and the 8 of a band form one of xcd_unit's runs, so they
-  // share an L2.  Against the order with each (sequence, KV head)'s blocks
+  // unit: (sequence, KV head, query block).  Query blocks go in bands of 8
+  // counted from each sequence's last block (the most keys under the causal
+  // mask), the first band first for every (sequence, KV head), so that the
+  // longest units start first over the whole grid, also when sequences bring
+  // different numbers of new tokens; within a band a (sequence, KV head)'s
+  // blocks are consecutive, last first, and the 8 of a band form one of
+  // xcd_unit's runs, so they share an L2.  A unit with no block of its
+  // sequence left exits.  Against the order with each (sequence, KV head)'s blocks
   // all together, whose last pairs' long blocks started near the end: fresh
   // 4K prompts 797 -> 590 us, fresh 8K 1,328 -> 1,100 us, 16 x 2,048 new
   // tokens on 8K contexts 3,979 -> 3,573 us (bit-identical; the same order
   // when a sequence has at most 8 blocks).  Bands of 4 or no bands at all
   // (longest first, (sequence, KV head) fastest) were slower on the 2,048-
-  // token chunks: their blocks meet less often in an L2.
+  // token chunks: their blocks meet less often in an L2.  Counting the bands
+  // from each sequence's own last block rather than from the batch's longest
+  // took a mixed batch (16 sequences, 8 to 2,048 new tokens on 2K-8K
+  // contexts) from 1,115 to 1,095 us.
   constexpr uint32_t kBand = 8;
   const uint32_t u = xcd_unit(blockIdx.x, gridDim.x);
   const uint32_t SG = (uint32_t)a.num_seqs * (uint32_t)a.num_kv_heads;
   const uint32_t band = (uint32_t)(u / ((uint64_t)SG * kBand));
   const uint32_t bw = min(kBand, (uint32_t)a.qblocks - band * kBand);   // blocks in this band
   const uint32_t rest = (uint32_t)(u - (uint64_t)band * SG * kBand);
-  const int qb = a.qblocks - 1 - (int)(band * kBand + rest % bw);
+  const int r = (int)(band * kBand + rest % bw);   // blocks after this one in its sequence
   const int sg = (int)(rest / bw);
   const int g = sg % a.num_kv_heads;
   const int s = sg / a.num_kv_heads;
@@ -179,11 +184,15 @@ __global__ __launch_bounds__(NW * kWave) void prefill_kernel(PrefillArgs a, int 
   const int n = a.query_start[s + 1] - q0;
   const TableView trow = table_view(a, s);
   const int L = min(a.context_lens[s], trow.capacity * block_size);
-  PA_FLAG_IF(threadIdx.x == 0 && qb == 0 &&
+  PA_FLAG_IF(threadIdx.x == 0 && r == 0 &&
                  (a.context_lens[s] > trow.capacity * block_size || q0 < 0 || n < 0 || n > a.num_tokens - q0 ||
                   n > L || n > a.max_query_len),
              kViolationLength);
-  if (q0 < 0 || n <= 0 || n > a.num_tokens - q0 || qb * QB >= n || n > L) return;
+  if (q0 < 0 || n <= 0 || n > a.num_tokens - q0 || n > L) return;
+  // blocks of this sequence (never more than the grid's: past max_query_len
+  // its later tokens stay unwritten), this unit's block counted from its start
+  const int qb = min((n + QB - 1) / QB, a.qblocks) - 1 - r;
+  if (qb < 0) return;
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);

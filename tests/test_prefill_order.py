@@ -1,10 +1,13 @@
 """The prefill grid's unit order, checked on the CPU: the index arithmetic of
-prefill_kernel (pa_prefill_kernels.hip) maps the workgroups one to one onto
-(sequence x KV head, query block) pairs, hands out the query blocks in bands
-of 8 with the band nearest the context's end first, keeps each (sequence, KV
-head)'s blocks of a band together (one run of 8 units on an XCD), and reduces
-to the plain order (blocks of one pair together, last first) when a sequence
-has at most 8 query blocks.  xcd_unit is mirrored from pa_common.hpp."""
+prefill_kernel (pa_prefill_kernels.hip) maps the workgroups onto
+(sequence x KV head, query block) pairs so that every block of every
+sequence is taken exactly once and the other units exit, hands out the
+query blocks in bands of 8 counted from each sequence's last block (so every
+sequence's last blocks come first, whatever its number of new tokens), keeps
+each (sequence, KV head)'s blocks of a band together (one run of 8 units on
+an XCD), and reduces to the plain order (blocks of one pair together, last
+first) when no sequence has more than 8 query blocks.  xcd_unit is mirrored
+from pa_common.hpp."""
 
 import pytest
 
@@ -20,10 +23,31 @@ def xcd_unit(b, n):
 
 
 def unit(u, SG, qblocks):
+    """(blocks after this one in its sequence, sequence x KV head)"""
     band = u // (SG * BAND)
     bw = min(BAND, qblocks - band * BAND)
     rest = u - band * SG * BAND
-    return qblocks - 1 - (band * BAND + rest % bw), rest // bw
+    return band * BAND + rest % bw, rest // bw
+
+
+def block(r, nblocks, qblocks):
+    """The unit's query block, or None when its sequence has no block left."""
+    qb = min(nblocks, qblocks) - 1 - r
+    return qb if qb >= 0 else None
+
+
+def run_grid(nblocks, Hkv, qblocks):
+    """Walk the grid in dispatch order (u); nblocks[s] = ceil(n_s / QB)."""
+    SG = len(nblocks) * Hkv
+    n = SG * qblocks
+    order = []
+    for b in range(n):
+        u = xcd_unit(b, n)
+        r, sg = unit(u, SG, qblocks)
+        qb = block(r, nblocks[sg // Hkv], qblocks)
+        order.append((u, r, sg, qb))
+    order.sort()
+    return order
 
 
 @pytest.mark.parametrize("SG", [1, 3, 8, 32, 128, 129])
@@ -35,7 +59,8 @@ def test_prefill_units_cover_each_block_once(SG, qblocks):
     for b in range(n):
         u = xcd_unit(b, n)
         assert 0 <= u < n
-        qb, sg = unit(u, SG, qblocks)
+        r, sg = unit(u, SG, qblocks)
+        qb = block(r, qblocks, qblocks)
         assert 0 <= qb < qblocks and 0 <= sg < SG
         assert (qb, sg) not in seen
         seen[(qb, sg)] = b
@@ -65,3 +90,32 @@ def test_full_band_is_one_xcd_run():
         us = [xcd_unit(b0 // 8 % 8 + 8 * (8 * (b0 // 64) + j), n) for j in range(8)]
         pairs = {unit(u, SG, qblocks)[1] for u in us}
         assert len(pairs) == 1
+
+
+@pytest.mark.parametrize("nblocks", [[33, 11, 1, 2, 8], [1, 1, 40], [9, 0, 16], [5, 5, 5]])
+def test_ragged_sequences_last_blocks_first(nblocks):
+    Hkv = 2
+    qblocks = max(nblocks)
+    order = run_grid(nblocks, Hkv, qblocks)
+    got = [(sg, qb) for _, _, sg, qb in order if qb is not None]
+    want = {(s * Hkv + g, q) for s, nb in enumerate(nblocks) for g in range(Hkv) for q in range(nb)}
+    assert len(got) == len(set(got)) and set(got) == want
+    # every sequence's last block is in the first band, and a pair's blocks
+    # come last first
+    pos = {key: i for i, key in enumerate(got)}
+    first_band = {(sg, qb) for _, r, sg, qb in order if qb is not None and r < BAND}
+    for s, nb in enumerate(nblocks):
+        for g in range(Hkv):
+            if nb:
+                assert (s * Hkv + g, nb - 1) in first_band
+            for q in range(1, nb):
+                assert pos[(s * Hkv + g, q)] < pos[(s * Hkv + g, q - 1)]
+
+
+def test_blocks_past_the_grid_stay_unwritten():
+    """A sequence with more blocks than the grid (more new tokens than
+    max_query_len) gets its first qblocks blocks, as the rows past
+    max_query_len are left alone."""
+    order = run_grid([12, 3], 1, 8)
+    got = {(sg, qb) for _, _, sg, qb in order if qb is not None}
+    assert got == {(0, q) for q in range(8)} | {(1, q) for q in range(3)}
