@@ -4,8 +4,10 @@ block size, group size, number of KV heads, batch size, a length mix (empty
 and one-token sequences, short ragged ones, ones crossing table windows),
 the split mode and whether the step appends a token; prefill cases draw a
 mix of cached prefixes and new tokens (fresh prompts, single tokens, chunks
-spanning several query-block bands).  The hand-picked cases of the other
-files stay; these reach combinations that no one picked."""
+spanning several query-block bands); two-level-table cases lay a random
+decode step out with large pages of a random size and compare bit for bit
+with the flat layout.  The hand-picked cases of the other files stay; these
+reach combinations that no one picked."""
 
 import numpy as np
 import pytest
@@ -90,3 +92,28 @@ def test_random_prefill(seed):
     vabs = W.to_storage(np.abs(O.upcast(b.v_pool, dtype)).astype(np.float32), dtype)
     mean = O.prefill_attention(q, b.k_pool, vabs, b.block_tables, b.context_lens, starts, b.scale, bs, dtype)
     check_close(gpu_out_f64(out, dtype), ref, dtype, f"random prefill {seed}", extra=2.0 ** -MANT_BITS[dtype] * mean)
+
+
+@pytest.mark.parametrize("seed", range(3000, 3024))
+def test_random_decode_two_level_tables_bit_identical_to_flat(seed):
+    """A random decode case (with an appended token) laid out flat and with
+    large pages of a random size holding a random share of each prompt: the
+    two calls give the same bits, in the case's split mode."""
+    c = decode_case(seed)
+    rng = np.random.default_rng(seed + 7)
+    lens = [max(L, 1) for L in c["lens"]]
+    H = int(rng.choice([1, 2, 4, 16, 64]))
+    prompts = [int(rng.integers(0, L + 1)) for L in lens]
+    b = W.make_decode_batch(seed, num_seqs=len(lens), num_q_heads=c["G"] * c["Hkv"], num_kv_heads=c["Hkv"],
+                            head_dim=c["D"], dtype=c["dtype"], block_size=c["bs"], context_lens=lens, append=True)
+    hb, large, nl = W.to_hierarchical(b, H, prompts, seed=seed + 1)
+    note(f"random two-level decode seed={seed} H={H} {c}")
+    flat = gpu_step(b, torch_io.to_device(b), partition_size=c["part"])
+    d = torch_io.to_device(hb)
+    P.kv_append(d.new_key, d.new_value, d.k_pool, d.v_pool, d.slot_mapping)
+    hier = P.decode_attention_hier(d.query, d.k_pool, d.v_pool, d.block_tables, torch.from_numpy(large).cuda(),
+                                   torch.from_numpy(nl).cuda(), H, d.context_lens, hb.scale, hb.max_context_len,
+                                   c["part"])
+    torch.cuda.synchronize()
+    dt = c["dtype"]
+    assert torch_io.torch_to_storage(flat, dt).tobytes() == torch_io.torch_to_storage(hier, dt).tobytes()
