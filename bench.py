@@ -630,6 +630,68 @@ def swap_leg(d, b, reps: int = 5, target_bytes: int = 1 << 30) -> dict:
                     "plain = one contiguous torch copy of the same bytes"}
 
 
+def grouped_decode_leg(b, d, stream, alg_unique: int, step_decode_ms: float, K: int = 20,
+                       partition_size: int = 1024) -> dict:
+    """The prefix-shared batch through pa_decode_attention_grouped: the
+    samples of a prompt read each shared K/V tile once per 16 / G of them
+    instead of once each.  Groups come from the tables on the host (outside
+    the timed region, as a block manager that forked the samples would hand
+    them over).  Time per call over a HIP graph of K calls after the clock
+    has settled, the distinct-bytes roofline, and the bit-for-bit check
+    against pa_decode_attention with the same partitions."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_313_amd as P
+
+    gs, gsh = P.prefix_groups(b.block_tables, b.context_lens, b.block_size)
+    max_group, max_shared = int(np.diff(gs).max(initial=1)), int(gsh.max(initial=0))
+    gsd, gshd = torch.from_numpy(gs).cuda(), torch.from_numpy(gsh).cuda()
+    ws = torch.empty(max(16, P.decode_workspace_bytes(b.num_seqs, b.num_q_heads, b.num_kv_heads, b.head_dim,
+                                                      b.max_context_len, partition_size)),
+                     dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(d.query)
+
+    def call(st):
+        P.decode_attention_grouped(d.query, d.k_pool, d.v_pool, d.block_tables, d.context_lens, gsd, gshd,
+                                   max_group, max_shared, b.scale, b.max_context_len, partition_size, out=out,
+                                   workspace=ws, stream=st)
+
+    call(stream)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    cs = torch.cuda.Stream()
+    cs.wait_stream(stream)
+    with torch.cuda.graph(g, stream=cs):
+        for _ in range(K):
+            call(cs)
+    stream.wait_stream(cs)
+    t_end = time.perf_counter() + SETTLE_S
+    while True:
+        g.replay()
+        torch.cuda.synchronize()
+        if time.perf_counter() >= t_end:
+            break
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    g.replay()
+    e1.record(stream)
+    e1.synchronize()
+    ms = e0.elapsed_time(e1) / K
+    plain = P.decode_attention(d.query, d.k_pool, d.v_pool, d.block_tables, d.context_lens, b.scale,
+                               b.max_context_len, partition_size, workspace=ws)
+    call(stream)
+    torch.cuda.synchronize()
+    same = bool(torch.equal(out.view(torch.int16), plain.view(torch.int16)))
+    achieved = alg_unique / (ms * 1e-3) / 1e9
+    return {"ms": ms, "partition_size": partition_size, "groups": len(gsh), "max_group_size": max_group,
+            "shared_tokens": max_shared, "achieved_gbps": achieved, "frac_of_hbm_peak": achieved / HBM_PEAK_GBPS,
+            "speedup_vs_step_decode": step_decode_ms / ms, "bit_identical_to_partitions": same,
+            "what": "pa_decode_attention_grouped over the step's pools (prompt groups from the tables), "
+                    "HIP graph of K calls; bytes as roofline.algorithmic_bytes_per_launch"}
+
+
 def cold_decode_leg(decode_call, stream, reps: int = 10, evict_bytes: int = 1 << 30) -> dict:
     """Decode time with nothing of the batch left in the caches: before each
     timed call a 1 GiB scratch buffer is read through (it evicts the 256 MB
@@ -897,6 +959,9 @@ def main():
         stream_leg["decode_frac_of_achievable"] = achieved / stream_leg["gbps"]
         bm_leg = block_manager_leg(b, max(args.steps, 10))
     swap = None if args.no_swap else swap_leg(d, b)
+    grouped = None
+    if "samples" in b.meta and not args.no_aux:   # the prefix-shared batch
+        grouped = grouped_decode_leg(b, d, stream, alg_unique, dec_ms, K)
     prefill = None if args.no_prefill else prefill_leg(parity_seqs=() if args.no_cpu_baseline else (0, 9))
 
     step_fn(stream)          # one whole step last: the output the parity check reads
@@ -967,6 +1032,7 @@ def main():
         "block_manager": bm_leg,
         "swap": swap,
         "prefill": prefill,
+        "grouped_decode": grouped,
     }
     print(json.dumps(line), flush=True)
 

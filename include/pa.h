@@ -194,6 +194,51 @@ pa_status pa_decode_attention(void* out, const void* query, const void* k_pool, 
                               size_t workspace_bytes, void* stream);
 
 /*
+ * pa_decode_attention_grouped -- pa_decode_attention for a batch in which
+ * consecutive sequences share the physical blocks of a common prefix: the
+ * samples of parallel sampling or the beams of beam search, which the
+ * pages give refcounted shared blocks (vLLM entity page, "what it is";
+ * paged-KV analysis page, section 3.2).  The same operation and results as
+ * pa_decode_attention with the same fixed partition_size; only the reads of
+ * the shared blocks change.
+ *
+ *   group_start    DEVICE int32 [num_groups + 1], non-decreasing from 0:
+ *                  group i is sequences group_start[i] .. group_start[i+1]-1
+ *                  (sequences outside every group run alone).
+ *   group_shared   DEVICE int32 [num_groups]: the first group_shared[i]
+ *                  tokens of every member of group i map to the same
+ *                  physical blocks (the caller's contract, like the table
+ *                  entries themselves).  The call uses the largest multiple
+ *                  of partition_size that is at most this, at most
+ *                  max_shared_len rounded up to a partition, and shorter than
+ *                  every member's context.
+ *   num_groups     >= 0;  max_group_size >= 1 when num_groups > 0: a host
+ *                  bound of the group sizes (members past it read their
+ *                  shared blocks alone);  max_shared_len >= 0: a host bound
+ *                  of group_shared.
+ *   partition_size > 0, a multiple of 16 and of block_size (else
+ *                  PA_ERR_PARTITION); workspace as for pa_decode_attention
+ *                  with this partition_size.
+ *
+ * Each shared partition is computed once per group of 16 / G members
+ * (G = Hq / Hkv): their query rows fill the 16 columns of the matrix-core
+ * products that one sequence's G rows pad, so each shared K/V tile is read
+ * and multiplied once for all of them.  Their partial results (max, sum,
+ * un-normalised output per partition) are the ones the plain partition pass
+ * writes, bit for bit, and the same merge combines them.  On the other cores
+ * (group size below 4, head_dim 64, f32) the call runs the plain partition
+ * pass.
+ */
+pa_status pa_decode_attention_grouped(void* out, const void* query, const void* k_pool, const void* v_pool,
+                                      const int32_t* block_tables, const int32_t* context_lens,
+                                      const int32_t* group_start, const int32_t* group_shared, int32_t num_groups,
+                                      int32_t max_group_size, int32_t max_shared_len, int32_t num_seqs,
+                                      int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                      int32_t block_size, int32_t max_blocks_per_seq, int32_t num_blocks,
+                                      int32_t max_context_len, float scale, int32_t partition_size,
+                                      pa_dtype dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * pa_decode_attention_noalloc -- pa_decode_attention without a workspace
  * argument, for callers that cannot allocate device memory (code under HIP
  * graph capture, tight serving loops, harnesses that forbid hipMalloc).

@@ -22,7 +22,8 @@ __all__ = ["kv_append", "block_copy", "decode_attention", "decode_attention_noal
            "decode_attention_hier",
            "prefill_attention_hier", "decode_workspace_bytes",
            "choose_partition", "swap_out", "swap_in", "swap_buffer", "stream_read", "PagedKVError", "load",
-           "PA_PARTITION_BALANCED", "BlockManager", "debug_violations"]
+           "PA_PARTITION_BALANCED", "BlockManager", "debug_violations",
+           "decode_attention_grouped", "prefix_groups"]
 
 _DTYPES = {torch.float32: _lib.PA_F32, torch.float16: _lib.PA_F16, torch.bfloat16: _lib.PA_BF16}
 
@@ -227,6 +228,90 @@ def decode_attention(query: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Te
                                  _stream(query, stream))
     _lib.check("pa_decode_attention", st)
     return out
+
+
+def decode_attention_grouped(query: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+                             block_tables: torch.Tensor, context_lens: torch.Tensor, group_start: torch.Tensor,
+                             group_shared: torch.Tensor, max_group_size: int, max_shared_len: int, scale: float,
+                             max_context_len: int, partition_size: int = 512, out: Optional[torch.Tensor] = None,
+                             workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """decode_attention with fixed ``partition_size``-token partitions for a
+    batch whose consecutive sequences share a prefix's blocks: group i is
+    sequences group_start[i] .. group_start[i+1] - 1 (int32 [G + 1] on the
+    GPU), whose first group_shared[i] tokens (int32 [G]) map to the same
+    blocks.  ``max_group_size`` and ``max_shared_len`` are host bounds of the
+    group sizes and of group_shared.  Same results as decode_attention with
+    that partition size; see prefix_groups for deriving the groups."""
+    lib = load()
+    S, Hq, D = query.shape
+    NB, Hkv, bs, D2 = k_pool.shape
+    if D2 != D or v_pool.shape != k_pool.shape:
+        raise ValueError("head_dim mismatch between query and pools")
+    for t, name in ((block_tables, "block_tables"), (context_lens, "context_lens"), (group_start, "group_start"),
+                    (group_shared, "group_shared")):
+        if t.dtype != torch.int32:
+            raise TypeError(f"{name} must be int32")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or context_lens.numel() != S:
+        raise ValueError("block_tables must be [S, max_blocks_per_seq] and context_lens [S]")
+    G = group_shared.numel()
+    if group_start.numel() != G + 1:
+        raise ValueError("group_start must have one entry more than group_shared")
+    if not (query.dtype == k_pool.dtype == v_pool.dtype):
+        raise TypeError("query and pools must share a dtype")
+    if out is None:
+        out = torch.empty_like(query)
+    else:
+        _check_out(out, query)
+    need = decode_workspace_bytes(S, Hq, Hkv, D, max_context_len, partition_size)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=query.device)
+    ws_ptr = _dev(workspace, "workspace") if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib.pa_decode_attention_grouped(_dev(out, "out"), _dev(query, "query"), _dev(k_pool, "k_pool"),
+                                         _dev(v_pool, "v_pool"), _dev(block_tables, "block_tables"),
+                                         _dev(context_lens, "context_lens"), _dev(group_start, "group_start"),
+                                         _dev(group_shared, "group_shared"), G, int(max_group_size),
+                                         int(max_shared_len), S, Hq, Hkv, D, bs, block_tables.shape[1], NB,
+                                         int(max_context_len), float(scale), int(partition_size),
+                                         _dtype_code(query), ws_ptr, ws_bytes, _stream(query, stream))
+    _lib.check("pa_decode_attention_grouped", st)
+    return out
+
+
+def prefix_groups(block_tables, context_lens, block_size: int, min_shared_blocks: int = 1):
+    """Host helper: runs of consecutive sequences whose tables start with the
+    same physical blocks (numpy int32 [S, MB] and [S]).  Returns
+    (group_start int32 [G + 1], group_shared int32 [G] in tokens): a run
+    holds the sequences that share at least ``min_shared_blocks`` leading
+    blocks of their valid entries with the run's first sequence, and its
+    shared length is the longest such common block prefix of all of them;
+    a sequence that shares nothing with its neighbour is a group of one with
+    no shared tokens."""
+    import numpy as np
+    tables = np.asarray(block_tables, dtype=np.int32)
+    lens = np.asarray(context_lens, dtype=np.int64)
+    S = tables.shape[0]
+    nblk = (lens + block_size - 1) // block_size
+
+    def common(a, b):   # leading valid blocks that sequences a and b both map to the same ids
+        n = int(min(nblk[a], nblk[b]))
+        diff = np.flatnonzero(tables[a, :n] != tables[b, :n])
+        return int(diff[0]) if diff.size else n
+
+    starts, shared = [0], []
+    run = int(nblk[0]) if S else 0
+    for s in range(1, S):
+        c = min(common(starts[-1], s), run)
+        if c >= min_shared_blocks:
+            run = c
+            continue
+        shared.append(run * block_size if s - starts[-1] > 1 else 0)
+        starts.append(s)
+        run = int(nblk[s])
+    if S:
+        shared.append(run * block_size if S - starts[-1] > 1 else 0)
+        starts.append(S)
+    return np.asarray(starts, dtype=np.int32), np.asarray(shared, dtype=np.int32)
 
 
 def decode_attention_noalloc(query: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,

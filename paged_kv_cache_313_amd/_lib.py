@@ -34,6 +34,7 @@ SIGNATURES = {
     "pa_decode_attention": (_c_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _c_i32, _c_i32, _c_i32, _c_i32,
                                      _c_i32, _c_i32, _c_i32, _c_i32, _c_f32, _c_i32, _c_i32, _vp,
                                      _c_size, _vp]),
+    "pa_decode_attention_grouped": (_c_i32, [_vp] * 8 + [_c_i32] * 11 + [_c_f32, _c_i32, _c_i32, _vp, _c_size, _vp]),
     "pa_decode_attention_noalloc": (_c_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _c_i32, _c_i32, _c_i32, _c_i32,
                                              _c_i32, _c_i32, _c_i32, _c_i32, _c_f32, _c_i32, _c_i32, _vp]),
     "pa_prefill_attention": (_c_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_i32, _c_i32, _c_i32, _c_i32,

@@ -321,13 +321,21 @@ PA_EXPORT int32_t pa_decode_choose_partition(int32_t num_seqs, int32_t num_kv_he
   return PA_PARTITION_BALANCED;
 }
 
+// Prefix groups of pa_decode_attention_grouped.
+struct PrefixGroups {
+  const int32_t* group_start;
+  const int32_t* group_shared;
+  int32_t num_groups, max_group_size, max_shared_len;
+};
+
 static pa_status decode_impl(void* out, const void* query, const void* k_pool, const void* v_pool,
                              const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
                              int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                              int32_t block_size, int32_t max_blocks_per_seq, int32_t num_blocks,
                              int32_t max_context_len, float scale, int32_t partition_size, pa_dtype dtype,
                              void* workspace, size_t workspace_bytes, void* stream,
-                             const HierTables& hier, bool use_scratch = false) {
+                             const HierTables& hier, bool use_scratch = false,
+                             const PrefixGroups* groups = nullptr) {
   if (!dtype_ok(dtype)) return PA_ERR_DTYPE;
   if (!block_size_ok(block_size)) return PA_ERR_BLOCK_SIZE;
   if (num_seqs < 0 || num_q_heads < 1 || num_kv_heads < 1 || !head_dim_ok(head_dim) ||
@@ -404,8 +412,21 @@ static pa_status decode_impl(void* out, const void* query, const void* k_pool, c
   a.num_large = hier.num_large;
   a.max_large_per_seq = hier.max_large_per_seq;
   a.large_shift = hier.shift;
+  pa::GroupArgs ga{};
+  const bool grouped = groups && groups->num_groups > 0 && np > 1;
+  if (grouped) {
+    ga.group_start = groups->group_start;
+    ga.group_shared = groups->group_shared;
+    ga.num_groups = groups->num_groups;
+    ga.max_group_size = groups->max_group_size;
+    const int64_t sp = ((int64_t)groups->max_shared_len + partition_size - 1) / partition_size;
+    ga.shared_parts = (int32_t)(sp < np ? sp : np);
+    // shared units (at most max_group_size member chunks) plus the partition units
+    if ((int64_t)groups->max_group_size * groups->num_groups * chunks * ga.shared_parts + units > INT32_MAX)
+      return PA_ERR_SHAPE;
+  }
   return hip_status(pa::launch_decode(a, elem_of(dtype), head_dim, block_size, group,
-                                      reinterpret_cast<hipStream_t>(stream)));
+                                      reinterpret_cast<hipStream_t>(stream), grouped ? &ga : nullptr));
 }
 
 PA_EXPORT pa_status pa_decode_attention(void* out, const void* query, const void* k_pool,
@@ -420,6 +441,28 @@ PA_EXPORT pa_status pa_decode_attention(void* out, const void* query, const void
   return decode_impl(out, query, k_pool, v_pool, block_tables, context_lens, num_seqs, num_q_heads,
                      num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks, max_context_len,
                      scale, partition_size, dtype, workspace, workspace_bytes, stream, HierTables{});
+}
+
+PA_EXPORT pa_status pa_decode_attention_grouped(void* out, const void* query, const void* k_pool,
+                                                const void* v_pool, const int32_t* block_tables,
+                                                const int32_t* context_lens, const int32_t* group_start,
+                                                const int32_t* group_shared, int32_t num_groups,
+                                                int32_t max_group_size, int32_t max_shared_len, int32_t num_seqs,
+                                                int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                                int32_t block_size, int32_t max_blocks_per_seq, int32_t num_blocks,
+                                                int32_t max_context_len, float scale, int32_t partition_size,
+                                                pa_dtype dtype, void* workspace, size_t workspace_bytes,
+                                                void* stream) {
+  if (!dtype_ok(dtype)) return PA_ERR_DTYPE;
+  if (!block_size_ok(block_size)) return PA_ERR_BLOCK_SIZE;
+  if (partition_size <= 0 || partition_size % 16 != 0 || partition_size % block_size != 0)
+    return PA_ERR_PARTITION;
+  if (num_groups < 0 || max_shared_len < 0 || (num_groups > 0 && max_group_size < 1)) return PA_ERR_SHAPE;
+  if (num_groups > 0 && num_seqs > 0 && (!group_start || !group_shared)) return PA_ERR_NULL;
+  const PrefixGroups g{group_start, group_shared, num_groups, max_group_size, max_shared_len};
+  return decode_impl(out, query, k_pool, v_pool, block_tables, context_lens, num_seqs, num_q_heads,
+                     num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks, max_context_len,
+                     scale, partition_size, dtype, workspace, workspace_bytes, stream, HierTables{}, false, &g);
 }
 
 PA_EXPORT pa_status pa_decode_attention_hier(void* out, const void* query, const void* k_pool,

@@ -390,6 +390,18 @@ struct DecodeArgs {
   int32_t large_shift;          // log2(blocks per large page)
 };
 
+// Prefix groups of the grouped decode: sequences group_start[i] ..
+// group_start[i+1] - 1 hold the same blocks for their first group_shared[i]
+// tokens.  A kernel argument of its own, so that DecodeArgs (and with it
+// every other decode kernel) stays as it is.
+struct GroupArgs {
+  const int32_t* group_start;   // [num_groups + 1]
+  const int32_t* group_shared;  // [num_groups]
+  int32_t num_groups;
+  int32_t max_group_size;       // host bound of group_start[i+1] - group_start[i]
+  int32_t shared_parts;         // partitions of the longest shared prefix in the grid
+};
+
 // Arguments of the prefill kernel.
 struct PrefillArgs {
   void* out;                    // [T, Hq, D] dtype

@@ -847,7 +847,12 @@ struct MfmaCore {
 #ifndef PA_PV_MFMA_MIN_GROUP
 #define PA_PV_MFMA_MIN_GROUP 4
 #endif
-template <class T, int D, int BS, int G>
+// KM > 1 (grouped decode): the 16 query columns hold the G heads of KM
+// consecutive sequences, which read the same K/V tiles (a shared prefix);
+// column w is sequence s + (w % (G KM)) / G, head h0 + w % G, so one tile
+// load and one set of products serve all of them.  Each column's
+// arithmetic is the same as with KM = 1.
+template <class T, int D, int BS, int G, int KM = 1>
 struct MfmaPvCore {
   static_assert(D == 128, "lane layout of the V chunks");
   static constexpr int ROWB = D * 2;
@@ -855,21 +860,28 @@ struct MfmaPvCore {
   static constexpr int NVI = 4;        // V chunks per lane per tile: tokens 4 gr .. 4 gr + 3
   static constexpr int NDT = 8;        // P.V products per tile (elements of a chunk)
   static constexpr int HEADS = G;
+  static constexpr int MEMBERS = KM;
   static constexpr int kBalancedWgPerCu = PA_MFMA_WG_PER_CU;
-  static_assert(16 % G == 0 && G >= 2, "group");
+  static_assert(16 % (G * KM) == 0 && G >= 2, "group");
   static_assert(kTblWin * BS % kTile == 0, "window");
 
+  // km (KM > 1): sequences s .. s + km - 1 take part (km <= KM); the other
+  // columns repeat sequence s and write nothing.
   template <bool SPLIT, bool PARTS = false, bool BUF = PARTS>
   __device__ static void run(const DecodeArgs& a, int32_t* tbl_lds, TblCache& tc, int s, int h0, int tok0,
-                             int tok1, const Dest& dst, PartBuf<G, D>* pb = nullptr) {
+                             int tok1, const Dest& dst, PartBuf<G, D>* pb = nullptr, int km = 1) {
+    static_assert(KM == 1 || !BUF, "grouped units write their partial rows directly");
     const int lane = threadIdx.x & (kWave - 1);
     const int gr = lane >> 4, w = lane & 15;
     const int g = h0 / G;
+    const int mi = (w % (G * KM)) / G;   // column w's sequence s + mi
+    const bool col_on = KM == 1 || (w < G * KM && mi < km);
 
     u32x4 qop[NQK];  // B operand of the scores: query row of head w % G, chunk 4 i + gr
     {
+      const int qs = KM == 1 ? s : s + (mi < km ? mi : 0);
       const char* qrow = reinterpret_cast<const char*>(a.query) +
-                         ((size_t)s * a.num_q_heads + h0 + (w % G)) * ROWB;
+                         ((size_t)qs * a.num_q_heads + h0 + (w % G)) * ROWB;
 #pragma unroll
       for (int i = 0; i < NQK; ++i) qop[i] = ld16(qrow + (4 * i + gr) * 16);
     }
@@ -896,7 +908,7 @@ struct MfmaPvCore {
       for (int r = 0; r < 4; ++r)
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) v[8 * r + dt] = oacc[dt][r];
-      if (w < G) {
+      if (KM == 1 && w < G) {
         const size_t orow = (size_t)s * a.num_q_heads + h0 + w;
         if constexpr (BUF) {
           pb->template chunk<32>(slot, w, 32 * gr, v);
@@ -905,6 +917,11 @@ struct MfmaPvCore {
           emit_chunk<T, 32>(a, d, orow, w, 32 * gr, D, v, l);
           if (gr == 0) emit_ml(a, d, w, m_run, l);
         }
+      } else if (KM > 1 && col_on) {   // row (s + mi, h0 + w % G), partial row prow0 + hh pstride
+        const int hh = mi * a.num_q_heads + w % G;
+        const size_t orow = ((size_t)s + mi) * a.num_q_heads + h0 + w % G;
+        emit_chunk<T, 32>(a, d, orow, hh, 32 * gr, D, v, l);
+        if (gr == 0) emit_ml(a, d, hh, m_run, l);
       }
       if constexpr (BUF) {
         if (lane == 0)
@@ -1052,6 +1069,104 @@ __global__ __launch_bounds__(NW * kWave) void decode_unit_kernel(DecodeArgs a, i
   const Dest dst{!a.split || L <= P, ((size_t)s * a.num_q_heads + h0) * a.num_parts + p,
                  (size_t)a.num_parts, 0};
   TblCache tc;
+  Core::template run<false>(a, s_tbl[wave], tc, s, h0, t0, t1, dst);
+}
+
+// ============================================================================
+// Grouped decode: the partition units of decode_unit_kernel, except that the
+// partitions of a prefix group's shared tokens run once per KM of its
+// sequences (CoreK), which read each shared K/V tile once for all of them.
+// The grid holds the shared units first -- (group, member chunk, head
+// group, partition), member chunk fastest, so the units that read one tile
+// are neighbours on one XCD -- then the private units in decode_unit_kernel's
+// order, which skip the partitions their group's shared units cover.  Every
+// partial row is the one the plain partition pass would write, so
+// decode_merge_parts_kernel merges them unchanged.
+// ============================================================================
+
+// Shared tokens of group grp: group_shared[grp] rounded down to whole
+// partitions, within the grid's shared partitions, and short of every
+// member's length (each member keeps a private partition, so its merge has
+// at least two parts, the shared units never write its output, and the
+// unit's first member, whose table it reads, holds every shared block; a
+// group with an empty member shares nothing).
+__device__ __forceinline__ int group_shared_tokens(const DecodeArgs& a, const GroupArgs& ga, int grp, int first,
+                                                   int end, int block_size) {
+  const int P = a.partition_size;
+  int sh = ga.group_shared[grp];
+  sh = sh < 0 ? 0 : sh - sh % P;
+  sh = min(sh, ga.shared_parts * P);
+  for (int s = max(first, 0); s < end; ++s) sh = min(sh, (clamp_len(a, s, block_size) - 1) / P * P);
+  return sh < 0 ? 0 : sh;
+}
+
+// Group of sequence s (its members first .. end - 1), or false when no group
+// holds it.  group_start is non-decreasing from 0 (caller's contract).
+__device__ __forceinline__ bool find_group(const GroupArgs& ga, int s, int& grp, int& first, int& end) {
+  int lo = 0, hi = ga.num_groups;   // group_start[lo] <= s < group_start[hi] when s is in a group
+  if (ga.num_groups <= 0 || s < ga.group_start[0] || s >= ga.group_start[ga.num_groups]) return false;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) / 2;
+    if (ga.group_start[mid] <= s) lo = mid; else hi = mid;
+  }
+  grp = lo;
+  first = ga.group_start[lo];
+  end = ga.group_start[lo + 1];
+  return true;
+}
+
+template <class Core, class CoreK, class T, int D, int NW>
+__global__ __launch_bounds__(NW * kWave) void decode_group_kernel(DecodeArgs a, GroupArgs ga, int block_size) {
+  constexpr int H = Core::HEADS;
+  constexpr int KM = CoreK::MEMBERS;
+  __shared__ int32_t s_tbl[NW][kTblWin];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const uint32_t u = xcd_unit(blockIdx.x, gridDim.x) * NW + wave;
+  const int S = a.num_seqs, C = a.head_chunks, P = a.partition_size;
+  const uint32_t MC = (uint32_t)((ga.max_group_size + KM - 1) / KM);
+  const uint32_t nsh = MC * (uint32_t)ga.num_groups * (uint32_t)C * (uint32_t)ga.shared_parts;
+  TblCache tc;
+  if (u < nsh) {
+    const int mc = (int)(u % MC);
+    uint32_t rest = u / MC;
+    const int grp = (int)(rest % (uint32_t)ga.num_groups);
+    rest /= (uint32_t)ga.num_groups;
+    const int c = (int)(rest % (uint32_t)C);
+    const int p = (int)(rest / (uint32_t)C);
+    const int first = ga.group_start[grp], end = min(ga.group_start[grp + 1], S);
+    const int s0 = first + mc * KM;
+    const int km = min(KM, end - s0);
+    if (first < 0 || km <= 0) return;
+    const int t0 = p * P;
+    if (t0 >= group_shared_tokens(a, ga, grp, first, end, block_size)) return;
+    const int h0 = c * H;
+    // rows (s0 + i, h0 + j, p) -> ((s0 + i) Hq + h0 + j) NP + p = prow0 + (i Hq + j) NP
+    const Dest dst{false, ((size_t)s0 * a.num_q_heads + h0) * a.num_parts + p, (size_t)a.num_parts, 0};
+    CoreK::template run<false>(a, s_tbl[wave], tc, s0, h0, t0, t0 + P, dst, nullptr, km);
+    return;
+  }
+  const uint32_t v = u - nsh;
+  if (v >= (uint32_t)S * C * a.num_parts) return;
+  const int s = (int)(v % (uint32_t)S);
+  const uint32_t rest = v / (uint32_t)S;
+  const int c = (int)(rest % (uint32_t)C);
+  const int p = (int)(rest / (uint32_t)C);
+  const int h0 = c * H;
+  const int L = clamp_len(a, s, block_size);
+  if (L == 0) {
+    if (p == 0) store_zero_rows<T, D, H>(a, s, h0, lane);
+    return;
+  }
+  const int t0 = p * P;
+  if (t0 >= L) return;
+  int grp, first, end;
+  // members past the grid's member chunks keep their shared tokens to themselves
+  if (find_group(ga, s, grp, first, end) && s - first < (int)MC * KM &&
+      t0 < group_shared_tokens(a, ga, grp, first, min(end, S), block_size))
+    return;   // a shared unit's partition
+  const int t1 = min(t0 + P, L);
+  const Dest dst{L <= P, ((size_t)s * a.num_q_heads + h0) * a.num_parts + p, (size_t)a.num_parts, 0};
   Core::template run<false>(a, s_tbl[wave], tc, s, h0, t0, t1, dst);
 }
 
@@ -1406,6 +1521,80 @@ __global__ __launch_bounds__(kPartMergeWaves * kWave) void decode_merge_parts_ke
   }
 }
 
+// The same merge for calls of at most 8 partitions per sequence at head_dim
+// 128 (short contexts, prefix-shared samples), where a workgroup per row
+// spends its launch on two or three partial rows: here a wave merges two
+// rows, 32 lanes per row and one 16-byte chunk per lane.  It forms the same
+// sums in the same order as decode_merge_parts_kernel, where partition p
+// falls to wave p / 2 and lane half p % 2 (each wave adds its two products,
+// then the four wave sums are added in wave order, absent partitions adding
+// +0), so the two kernels give the same bits.
+constexpr int kFewParts = 8;
+template <class T, int D>
+__global__ __launch_bounds__(4 * kWave) void decode_merge_few_kernel(DecodeArgs a, int block_size) {
+  static_assert(D == 128, "32 lanes of 4 floats per row");
+  const int lane = threadIdx.x & (kWave - 1);
+  const size_t row = ((size_t)blockIdx.x * 4 + threadIdx.x / kWave) * 2 + (lane >> 5);   // s * Hq + h
+  if (row >= (size_t)a.num_seqs * a.num_q_heads) return;
+  const int s = (int)(row / (size_t)a.num_q_heads);
+  const int L = clamp_len(a, s, block_size);
+  const int P = a.partition_size;
+  const int np = min((L + P - 1) / P, kFewParts);
+  if (np <= 1) return;                      // written directly by the partition pass
+  const size_t base = row * a.num_parts;
+  const int ch = lane & 31;
+  float m[kFewParts];
+  float M = kNegInf;
+#pragma unroll
+  for (int p = 0; p < kFewParts; ++p) {
+    m[p] = p < np ? a.ws_m[base + p] : kNegInf;
+    M = fmaxf(M, m[p]);
+  }
+  f32x4 t = {0.f, 0.f, 0.f, 0.f};
+  float dt = 0.f;
+#pragma unroll
+  for (int k = 0; k < kFewParts / 2; ++k) {
+    f32x4 half[2];
+    float dh[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int p = 2 * k + j;
+      half[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      dh[j] = 0.f;
+      if (p < np) {
+        const float w = fast_exp2(m[p] - M);
+        const f32x4 o = *reinterpret_cast<const f32x4*>(a.ws_o + (base + p) * D + 4 * ch);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) half[j][e] = fmaf(w, o[e], 0.f);
+        dh[j] = fmaf(w, a.ws_l[base + p], 0.f);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float n = half[0][e] + half[1][e];
+      t[e] = k == 0 ? n : t[e] + n;
+    }
+    const float dn = dh[0] + dh[1];
+    dt = k == 0 ? dn : dt + dn;
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) store_elem<T>(a.out, row * D + 4 * ch + e, t[e] / dt);
+}
+
+// Merge launch of the fixed-partition passes.
+template <class T, int D>
+static hipError_t launch_merge_parts(const DecodeArgs& a, int bs, hipStream_t st) {
+  const uint32_t rows = (uint32_t)a.num_seqs * a.num_q_heads;
+  if constexpr (D == 128) {
+    if (a.num_parts <= kFewParts) {
+      hipLaunchKernelGGL((decode_merge_few_kernel<T, D>), dim3((rows + 7) / 8), dim3(4 * kWave), 0, st, a, bs);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((decode_merge_parts_kernel<T, D>), dim3(rows), dim3(kPartMergeWaves * kWave), 0, st, a, bs);
+  return hipGetLastError();
+}
+
 // Balanced mode: the head groups whose tiles were split between waves are
 // found from the wave boundaries.  Boundary w (1 <= w < W, at position
 // b = range_start(w) of the flattened space) merges the head group whose
@@ -1545,18 +1734,14 @@ static hipError_t run_core(const DecodeArgs& a, int bs, hipStream_t st) {
     hipLaunchKernelGGL(kern, dim3(nwg), dim3(NW * kWave), 0, st, a, bs);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((decode_merge_parts_kernel<T, D>), dim3((uint32_t)a.num_seqs * a.num_q_heads),
-                       dim3(kPartMergeWaves * kWave), 0, st, a, bs);
-    return hipGetLastError();
+    return launch_merge_parts<T, D>(a, bs, st);
   }
   const uint64_t units = (uint64_t)a.num_seqs * a.head_chunks * a.num_parts;
   const uint32_t groups = (uint32_t)((units + NW - 1) / NW);
   hipLaunchKernelGGL((decode_unit_kernel<Core, T, D, NW>), dim3(groups), dim3(NW * kWave), 0, st, a, bs);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !a.split) return e;
-  hipLaunchKernelGGL((decode_merge_parts_kernel<T, D>), dim3((uint32_t)a.num_seqs * a.num_q_heads),
-                     dim3(kPartMergeWaves * kWave), 0, st, a, bs);
-  return hipGetLastError();
+  return launch_merge_parts<T, D>(a, bs, st);
 }
 
 // Grouped queries: P.V on the matrix cores for head_dim 128 and groups of at
@@ -1567,22 +1752,45 @@ static hipError_t run_core(const DecodeArgs& a, int bs, hipStream_t st) {
 // against 672.5 us, long context 831.4 against 830.9 us), and where shared
 // blocks come from the caches the matrix-core form is 4 % faster
 // (prefix-shared decode 237.3 against 247.7 us).
+// Grouped decode (prefix groups given, fixed partitions): the group kernel,
+// then the partition merge.
 template <class T, int D, int BS, int G>
-static hipError_t run_gqa(const DecodeArgs& a, hipStream_t st) {
-  if constexpr (D == 128 && G >= PA_PV_MFMA_MIN_GROUP)
+static hipError_t run_grouped(const DecodeArgs& a, const GroupArgs& ga, hipStream_t st) {
+  constexpr int NW = kWavesPerGroup;
+  using Core = MfmaPvCore<T, D, BS, G>;
+  using CoreK = MfmaPvCore<T, D, BS, G, 16 / G>;
+  constexpr int KM = CoreK::MEMBERS;
+  const uint64_t mc = ((uint64_t)ga.max_group_size + KM - 1) / KM;
+  const uint64_t units = mc * (uint64_t)ga.num_groups * a.head_chunks * ga.shared_parts +
+                         (uint64_t)a.num_seqs * a.head_chunks * a.num_parts;
+  if (units > 0x7fffffffull) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((decode_group_kernel<Core, CoreK, T, D, NW>), dim3((uint32_t)((units + NW - 1) / NW)),
+                     dim3(NW * kWave), 0, st, a, ga, BS);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_merge_parts<T, D>(a, BS, st);
+}
+
+// With prefix groups on other cores the plain partition pass runs: the
+// same results, without the shared reads.
+template <class T, int D, int BS, int G>
+static hipError_t run_gqa(const DecodeArgs& a, const GroupArgs* ga, hipStream_t st) {
+  if constexpr (D == 128 && G >= PA_PV_MFMA_MIN_GROUP) {
+    if (ga && a.split && a.mode == kModeUnit) return run_grouped<T, D, BS, G>(a, *ga, st);
     return run_core<MfmaPvCore<T, D, BS, G>, T, D>(a, BS, st);
-  else
+  } else {
     return run_core<MfmaCore<T, D, BS, G>, T, D>(a, BS, st);
+  }
 }
 
 template <class T, int D, int BS>
-static hipError_t dispatch_bs(const DecodeArgs& a, int group, hipStream_t st) {
+static hipError_t dispatch_bs(const DecodeArgs& a, int group, hipStream_t st, const GroupArgs* ga) {
   if constexpr (!std::is_same<T, F32>::value) {
     switch (group) {
-      case 2: return run_gqa<T, D, BS, 2>(a, st);
-      case 4: return run_gqa<T, D, BS, 4>(a, st);
-      case 8: return run_gqa<T, D, BS, 8>(a, st);
-      case 16: return run_gqa<T, D, BS, 16>(a, st);
+      case 2: return run_gqa<T, D, BS, 2>(a, ga, st);
+      case 4: return run_gqa<T, D, BS, 4>(a, ga, st);
+      case 8: return run_gqa<T, D, BS, 8>(a, ga, st);
+      case 16: return run_gqa<T, D, BS, 16>(a, ga, st);
       default: break;   // group 1: VALU
     }
   }
@@ -1601,20 +1809,21 @@ static hipError_t dispatch_bs(const DecodeArgs& a, int group, hipStream_t st) {
 }
 
 template <class T, int D>
-static hipError_t dispatch_d(const DecodeArgs& a, int bs, int group, hipStream_t st) {
+static hipError_t dispatch_d(const DecodeArgs& a, int bs, int group, hipStream_t st, const GroupArgs* ga) {
   switch (bs) {
-    case 8: return dispatch_bs<T, D, 8>(a, group, st);
-    case 16: return dispatch_bs<T, D, 16>(a, group, st);
-    case 32: return dispatch_bs<T, D, 32>(a, group, st);
+    case 8: return dispatch_bs<T, D, 8>(a, group, st, ga);
+    case 16: return dispatch_bs<T, D, 16>(a, group, st, ga);
+    case 32: return dispatch_bs<T, D, 32>(a, group, st, ga);
     default: return hipErrorInvalidValue;
   }
 }
 
 template <class T>
-static hipError_t dispatch_t(const DecodeArgs& a, int head_dim, int bs, int group, hipStream_t st) {
+static hipError_t dispatch_t(const DecodeArgs& a, int head_dim, int bs, int group, hipStream_t st,
+                             const GroupArgs* ga) {
   switch (head_dim) {
-    case 64: return dispatch_d<T, 64>(a, bs, group, st);
-    case 128: return dispatch_d<T, 128>(a, bs, group, st);
+    case 64: return dispatch_d<T, 64>(a, bs, group, st, ga);
+    case 128: return dispatch_d<T, 128>(a, bs, group, st, ga);
     default: return hipErrorInvalidValue;
   }
 }

@@ -36,11 +36,11 @@ hipError_t decode_scratch(void** ptr) {
 }
 
 hipError_t launch_decode(const DecodeArgs& a, Elem elem, int head_dim, int block_size, int group,
-                         hipStream_t st) {
+                         hipStream_t st, const GroupArgs* groups) {
   switch (elem) {
-    case Elem::F32: return launch_decode_f32(a, head_dim, block_size, group, st);
-    case Elem::F16: return launch_decode_f16(a, head_dim, block_size, group, st);
-    case Elem::BF16: return launch_decode_bf16(a, head_dim, block_size, group, st);
+    case Elem::F32: return launch_decode_f32(a, head_dim, block_size, group, st, groups);
+    case Elem::F16: return launch_decode_f16(a, head_dim, block_size, group, st, groups);
+    case Elem::BF16: return launch_decode_bf16(a, head_dim, block_size, group, st, groups);
   }
   return hipErrorInvalidValue;
 }

@@ -7,6 +7,7 @@
 namespace pa {
 
 struct DecodeArgs;
+struct GroupArgs;
 
 enum class Elem { F32 = 0, F16 = 1, BF16 = 2 };
 
@@ -36,13 +37,17 @@ hipError_t launch_stream_read(const void* buf, uint64_t bytes, uint32_t* partial
 
 // Decode: the segment kernel of the chosen mode plus, when results are split,
 // its merge kernel.  f16/bf16 with group size 2..16 run the MFMA core, all
-// other cases the VALU core.
+// other cases the VALU core.  With prefix groups (fixed partitions) the
+// matrix-core P.V path runs the grouped kernel instead.
 hipError_t launch_decode(const DecodeArgs& args, Elem elem, int head_dim, int block_size,
-                         int group, hipStream_t stream);
+                         int group, hipStream_t stream, const GroupArgs* groups = nullptr);
 // the same, one per storage type (separate translation units)
-hipError_t launch_decode_f32(const DecodeArgs& args, int head_dim, int block_size, int group, hipStream_t stream);
-hipError_t launch_decode_f16(const DecodeArgs& args, int head_dim, int block_size, int group, hipStream_t stream);
-hipError_t launch_decode_bf16(const DecodeArgs& args, int head_dim, int block_size, int group, hipStream_t stream);
+hipError_t launch_decode_f32(const DecodeArgs& args, int head_dim, int block_size, int group, hipStream_t stream,
+                             const GroupArgs* groups);
+hipError_t launch_decode_f16(const DecodeArgs& args, int head_dim, int block_size, int group, hipStream_t stream,
+                             const GroupArgs* groups);
+hipError_t launch_decode_bf16(const DecodeArgs& args, int head_dim, int block_size, int group, hipStream_t stream,
+                              const GroupArgs* groups);
 
 // Contract-violation flags of each translation unit (zero unless built with
 // PA_DEBUG_CHECKS=1); read, and cleared when asked, synchronously.

@@ -8,6 +8,7 @@ import os
 import re
 import subprocess
 
+import numpy as np
 import pytest
 
 import paged_kv_cache_313_amd as P
@@ -128,6 +129,49 @@ def decode(lib, **kw):
 ])
 def test_decode_argument_checks(lib, kw, status):
     assert decode(lib, **kw) == status
+
+
+def decode_grouped(lib, **kw):
+    a = dict(DEC_OK, gs=A, gsh=A, ng=2, mg=8, ms=1024, P=512, maxL=2048, ws=B, wsb=1 << 30)
+    a.update(kw)
+    return lib.pa_decode_attention_grouped(a["out"], a["q"], a["k"], a["v"], a["tbl"], a["lens"], a["gs"], a["gsh"],
+                                           a["ng"], a["mg"], a["ms"], a["S"], a["Hq"], a["Hkv"], a["D"], a["bs"],
+                                           a["MB"], a["NB"], a["maxL"], a["scale"], a["P"], a["dtype"], a["ws"],
+                                           a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=9), 4), (dict(bs=4), 3),
+    (dict(P=0), 5), (dict(P=-1), 5), (dict(P=24), 5), (dict(P=16, bs=32), 5),   # fixed partitions only
+    (dict(ng=-1), 2), (dict(ms=-1), 2), (dict(mg=0), 2),
+    (dict(gs=None), 1), (dict(gsh=None), 1),
+    (dict(ng=0, gs=None, gsh=None, mg=0, ws=None, wsb=0), 6),   # no groups: the partition pass, which needs a workspace
+    (dict(D=80), 2), (dict(Hq=24, Hkv=8), 2), (dict(out=None), 1), (dict(k=B + 4), 8),
+    (dict(wsb=100), 6),
+    (dict(ng=1 << 20, mg=1 << 12, S=4096, MB=128), 2),   # shared units past the grid's limit
+    (dict(S=0, out=None, q=None, gs=None, gsh=None), 0),
+])
+def test_decode_grouped_argument_checks(lib, kw, status):
+    assert decode_grouped(lib, **kw) == status
+
+
+def test_prefix_groups_from_tables():
+    """Runs of consecutive sequences with common leading blocks; a sequence
+    that shares nothing with its neighbour is a group of one with no shared
+    tokens; the shared length is the common prefix of the whole run, in
+    tokens, over valid entries only."""
+    from paged_kv_cache_313_amd import prefix_groups
+    t = np.array([[5, 6, 7, 8], [5, 6, 7, 9], [5, 6, 3, 1],     # share 2 blocks (the third narrows the run)
+                  [2, 4, 0, 0],                                 # alone
+                  [10, 11, 12, 0], [10, 11, 12, 0]], np.int32)  # share 3 blocks, 4th entry past the lengths
+    lens = np.array([64, 64, 64, 20, 40, 48], np.int32)         # block size 16
+    gs, gsh = prefix_groups(t, lens, 16)
+    assert gs.tolist() == [0, 3, 4, 6]
+    assert gsh.tolist() == [32, 0, 48]
+    gs, gsh = prefix_groups(t, lens, 16, min_shared_blocks=3)
+    assert gs.tolist() == [0, 2, 3, 4, 6] and gsh.tolist() == [48, 0, 0, 48]
+    gs, gsh = prefix_groups(np.zeros((0, 4), np.int32), np.zeros(0, np.int32), 16)
+    assert gs.tolist() == [0] and gsh.tolist() == []
 
 
 def decode_noalloc(lib, **kw):
