@@ -1,4 +1,4 @@
-"""The library's calls captured in a HIP graph (append + decode, and prefill)
+"""The library's calls captured in a HIP graph (append + decode, grouped decode, and prefill)
 give, on every replay, exactly what eager calls give -- with eager work and
 synchronisations between the replays.  The calls allocate, clear and
 synchronise nothing, so capture needs no special path."""
@@ -82,3 +82,43 @@ def test_prefill_graph_replays_match_eager():
         assert torch.equal(out_g.view(torch.int16), want.view(torch.int16)), f"replay {r}"
         P.prefill_attention(q, d.k_pool, d.v_pool, d.block_tables, d.context_lens, starts, b.scale, 200, out=out_e)
         torch.cuda.synchronize()
+
+
+def test_grouped_decode_graph_replays_match_eager():
+    b = W.make_prefix_shared_batch(33, num_prompts=3, samples=5, prefix_len=600, suffix_len=90, num_q_heads=8,
+                                   num_kv_heads=2, head_dim=128, dtype="bf16", block_size=16, threads=4)
+    d = torch_io.to_device(b)
+    P.block_copy(d.k_pool, d.v_pool, d.block_mapping)
+    P.kv_append(d.new_key, d.new_value, d.k_pool, d.v_pool, d.slot_mapping)
+    gs, gsh = P.prefix_groups(b.block_tables, b.context_lens, 16)
+    gsd, gshd = torch.from_numpy(gs).cuda(), torch.from_numpy(gsh).cuda()
+    ws = torch.empty(P.decode_workspace_bytes(b.num_seqs, 8, 2, 128, b.max_context_len, 256), dtype=torch.uint8,
+                     device="cuda")
+
+    def call(out, st):
+        P.decode_attention_grouped(d.query, d.k_pool, d.v_pool, d.block_tables, d.context_lens, gsd, gshd, 5,
+                                   int(gsh.max()), b.scale, b.max_context_len, 256, out=out, workspace=ws, stream=st)
+
+    out_e = torch.empty_like(d.query)
+    out_g = torch.empty_like(d.query)
+    note("graph grouped decode: eager reference")
+    call(out_e, torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    want = out_e.clone()
+    g = torch.cuda.CUDAGraph()
+    cs = torch.cuda.Stream()
+    cs.wait_stream(torch.cuda.current_stream())
+    note("graph grouped decode: capture")
+    with torch.cuda.graph(g, stream=cs):
+        call(out_g, cs)
+    torch.cuda.current_stream().wait_stream(cs)
+    torch.cuda.synchronize()
+    for r in range(3):
+        out_g.fill_(float("nan"))
+        note(f"graph grouped decode: replay {r}")
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out_g.view(torch.int16), want.view(torch.int16)), f"replay {r}"
+        call(out_e, torch.cuda.current_stream())   # eager work on the same workspace between replays
+        torch.cuda.synchronize()
+        assert torch.equal(out_e.view(torch.int16), want.view(torch.int16))
