@@ -211,7 +211,8 @@ pa_status pa_decode_attention(void* out, const void* query, const void* k_pool, 
  *                  entries themselves).  The call uses the largest multiple
  *                  of partition_size that is at most this, at most
  *                  max_shared_len rounded up to a partition, and shorter than
- *                  every member's context.
+ *                  every member's context (a group with an empty member
+ *                  shares nothing).
  *   num_groups     >= 0;  max_group_size >= 1 when num_groups > 0: a host
  *                  bound of the group sizes (members past it read their
  *                  shared blocks alone);  max_shared_len >= 0: a host bound
