@@ -142,7 +142,8 @@ def ingest_counters(root, config=3, partition=-1, out_path=None, block_size=16, 
     elif partition > 0:   # fixed partitions: the resident-grid kernel (the unit kernel above 4096 sequences)
         resident = [k for k in fetch if "decode_parts_resident_kernel" in k]
         dk = pick(fetch, "decode_parts_resident_kernel" if resident else "decode_unit_kernel")
-        mk = pick(fetch, "decode_merge_parts_kernel")
+        few = any("decode_merge_few_kernel" in k for k in fetch)   # at most 8 partitions
+        mk = pick(fetch, "decode_merge_few_kernel" if few else "decode_merge_parts_kernel")
     else:
         dk, mk = pick(fetch, "decode_unit_kernel"), None
     dec_f, dec_w = fetch[dk] * 1024 * ff, write[dk] * 1024 * wf
@@ -398,8 +399,11 @@ def decode_kernel_name(b, part):
     if part == -1:
         return f"pa_decode_attention: decode_balanced_kernel<{core}> + decode_merge_balanced_kernel"
     if part and part > 0:
+        if b.max_context_len <= part:   # one partition: no split, no merge
+            return f"pa_decode_attention: decode_unit_kernel<{core}>"
         kern = "decode_parts_resident_kernel" if b.num_seqs <= 4096 else "decode_unit_kernel"
-        return f"pa_decode_attention: {kern}<{core}> + decode_merge_parts_kernel"
+        few = b.head_dim == 128 and -(-b.max_context_len // part) <= 8   # at most 8 partitions
+        return f"pa_decode_attention: {kern}<{core}> + {'decode_merge_few_kernel' if few else 'decode_merge_parts_kernel'}"
     return f"pa_decode_attention: decode_unit_kernel<{core}>"
 
 
