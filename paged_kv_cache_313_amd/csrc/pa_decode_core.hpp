@@ -1080,8 +1080,8 @@ __global__ __launch_bounds__(NW * kWave) void decode_unit_kernel(DecodeArgs a, i
 // group, partition), member chunk fastest, so the units that read one tile
 // are neighbours on one XCD -- then the private units in decode_unit_kernel's
 // order, which skip the partitions their group's shared units cover.  Every
-// partial row is the one the plain partition pass would write, so
-// decode_merge_parts_kernel merges them unchanged.
+// partial row is the one the plain partition pass would write, so the
+// partition merge (launch_merge_parts) combines them unchanged.
 // ============================================================================
 
 // Shared tokens of group grp: group_shared[grp] rounded down to whole
@@ -1744,14 +1744,6 @@ static hipError_t run_core(const DecodeArgs& a, int bs, hipStream_t st) {
   return launch_merge_parts<T, D>(a, bs, st);
 }
 
-// Grouped queries: P.V on the matrix cores for head_dim 128 and groups of at
-// least PA_PV_MFMA_MIN_GROUP, MfmaCore otherwise.  The vector P.V of MfmaCore,
-// G x 36 instructions per V chunk, bounds the call at larger groups (65 % of
-// the HBM peak at G = 8, 32 % at G = 16 on the Llama-3-8B-shaped batch); at
-// G = 4 the HBM-bound batches time the same either way (Llama-3-8B 670.4
-// against 672.5 us, long context 831.4 against 830.9 us), and where shared
-// blocks come from the caches the matrix-core form is 4 % faster
-// (prefix-shared decode 237.3 against 247.7 us).
 // Grouped decode (prefix groups given, fixed partitions): the group kernel,
 // then the partition merge.
 template <class T, int D, int BS, int G>
@@ -1771,6 +1763,14 @@ static hipError_t run_grouped(const DecodeArgs& a, const GroupArgs& ga, hipStrea
   return launch_merge_parts<T, D>(a, BS, st);
 }
 
+// Grouped queries: P.V on the matrix cores for head_dim 128 and groups of at
+// least PA_PV_MFMA_MIN_GROUP, MfmaCore otherwise.  The vector P.V of MfmaCore,
+// G x 36 instructions per V chunk, bounds the call at larger groups (65 % of
+// the HBM peak at G = 8, 32 % at G = 16 on the Llama-3-8B-shaped batch); at
+// G = 4 the HBM-bound batches time the same either way (Llama-3-8B 670.4
+// against 672.5 us, long context 831.4 against 830.9 us), and where shared
+// blocks come from the caches the matrix-core form is 4 % faster
+// (prefix-shared decode 237.3 against 247.7 us).
 // With prefix groups on other cores the plain partition pass runs: the
 // same results, without the shared reads.
 template <class T, int D, int BS, int G>
