@@ -175,3 +175,65 @@ def test_manager_large_pages_drive_hier_calls():
         check_close(gpu_out_f64(out, DT), want, DT, f"decode step {t}",
                     extra=pv_bound(q, k_host, v_host, None, lens, scale, bs, DT, hier=(large, nl, small, H)))
     assert torch_io.torch_to_storage(k_dev, DT).tobytes() == k_host.tobytes()
+
+
+@pytest.mark.parametrize("bs", [16, 32])
+def test_manager_forks_drive_grouped_decode(bs):
+    """Two prompts, each forked into 8 samples that then decode a token per
+    step: the manager's tables give the prompt groups (prefix_groups), and
+    the grouped decode of every step equals the plain decode at the same
+    partitions bit for bit and the oracle within the bf16 bound.  A sample
+    that finishes leaves its group one smaller; the groups are derived anew
+    each step."""
+    rng = np.random.default_rng(3140 + bs)
+    NB, Hkv, G, D, part = 200, 2, 4, 128, 64
+    Hq = Hkv * G
+    scale = W.default_scale(D)
+    nat = P.BlockManager(NB, bs)
+    k_host = W.poison_array((NB, Hkv, bs, D), DT)
+    v_host = W.poison_array((NB, Hkv, bs, D), DT)
+    k_dev = torch_io.storage_to_torch(k_host, DT, "cuda")
+    v_dev = torch_io.storage_to_torch(v_host, DT, "cuda")
+
+    def step(seqs, counts):
+        slots, pairs = nat.append_slots(seqs, counts)
+        n = len(slots)
+        key, val = draw(rng, (n, Hkv, D)), draw(rng, (n, Hkv, D))
+        if len(pairs):
+            P.block_copy(k_dev, v_dev, torch.from_numpy(pairs).cuda())
+            O.block_copy(k_host, v_host, pairs)
+        P.kv_append(torch_io.storage_to_torch(key, DT, "cuda"), torch_io.storage_to_torch(val, DT, "cuda"),
+                    k_dev, v_dev, torch.from_numpy(slots).cuda())
+        O.kv_append(k_host, v_host, key, val, slots, bs)
+
+    prompts = []
+    for plen in (300, 257):
+        s = nat.add_sequence()
+        prompts.append(s)
+        step([s], [plen])
+    live = []
+    for s in prompts:
+        live.append(s)
+        live.extend(nat.fork(s) for _ in range(7))
+    for t in range(6):
+        step(live, [1] * len(live))
+        mb = max(nat.length(s) for s in live) // bs + 1
+        tables, lens = nat.block_tables(live, mb)
+        gs, gsh = P.prefix_groups(tables, lens, bs)
+        assert (gsh > 0).sum() == 2, (gs, gsh)
+        q = draw(rng, (len(live), Hq, D))
+        qd = torch_io.storage_to_torch(q, DT, "cuda")
+        td, ld = torch.from_numpy(tables).cuda(), torch.from_numpy(lens).cuda()
+        note(f"block manager grouped decode bs={bs} step {t}")
+        plain = P.decode_attention(qd, k_dev, v_dev, td, ld, scale, int(lens.max()), part)
+        got = P.decode_attention_grouped(qd, k_dev, v_dev, td, ld, torch.from_numpy(gs).cuda(),
+                                         torch.from_numpy(gsh).cuda(), int(np.diff(gs).max()), int(gsh.max()),
+                                         scale, int(lens.max()), part)
+        torch.cuda.synchronize()
+        assert torch.equal(got.view(torch.int16), plain.view(torch.int16)), f"step {t}"
+        want = O.decode_attention(q, k_host, v_host, tables, lens, scale, bs, DT)
+        check_close(gpu_out_f64(got, DT), want, DT, f"grouped step {t}",
+                    extra=pv_bound(q, k_host, v_host, tables, lens, scale, bs, DT))
+        if t == 2:   # a sample of the first prompt finishes
+            nat.free_sequence(live[3])
+            live = live[:3] + live[4:]
