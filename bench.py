@@ -79,6 +79,10 @@ def parse_args():
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB (5 times), the "
                          "reference kernel for scaling HBM byte counters, and exit")
+    ap.add_argument("--ingest-grouped-counters", metavar="DIR", default=None,
+                    help="only read FETCH_SIZE / WRITE_SIZE passes (and the copy calibration) under DIR of a "
+                         "--config 4 run with its grouped leg, write the grouped decode's HBM bytes per call to "
+                         "the profiles counters file, and exit (no GPU)")
     ap.add_argument("--ingest-counters", metavar="DIR", default=None,
                     help="only read rocprofv3 --pmc csv output under DIR/{fetch,write,calf,calw} (FETCH_SIZE and "
                          "WRITE_SIZE passes of the default decode bench and of --calibrate-copy-mib 1024), write "
@@ -117,26 +121,59 @@ def _pmc_per_dispatch(root, counter):
     return {k: sums[k] / counts[k] for k in sums}
 
 
-def ingest_counters(root, config=3, partition=-1, out_path=None, block_size=16, explicit_partition=False):
-    """Turn FETCH_SIZE / WRITE_SIZE passes (KiB per dispatch) into bytes per
-    decode call, each scaled by what the same counter reads for a plain copy of
-    known size, and store them keyed by the kernel sources' hash.  `partition`
-    names the decode kernels: -1 the balanced kernel + its merge, P > 0 the
-    unit kernel + the partition merge, 0 the unit kernel alone."""
+def _counter_passes(root):
+    """FETCH_SIZE / WRITE_SIZE per dispatch (KiB) under root/{fetch,write},
+    the scale factors from the plain 1 GiB copy under root/{calf,calw}, and a
+    picker of the one kernel whose name holds a tag."""
     calib = 1 << 30
     fetch, write = _pmc_per_dispatch(os.path.join(root, "fetch"), "FETCH_SIZE"), \
         _pmc_per_dispatch(os.path.join(root, "write"), "WRITE_SIZE")
     calf, calw = _pmc_per_dispatch(os.path.join(root, "calf"), "FETCH_SIZE"), \
         _pmc_per_dispatch(os.path.join(root, "calw"), "WRITE_SIZE")
     copy_k = max(calf, key=calf.get)
-    ff = (calib / 1024) / calf[copy_k]
-    wf = (calib / 1024) / calw[copy_k]
+    cal = {"copy_bytes": calib, "copy_kernel": copy_k, "fetch_kib": calf[copy_k], "write_kib": calw[copy_k],
+           "fetch_factor": (calib / 1024) / calf[copy_k], "write_factor": (calib / 1024) / calw[copy_k]}
 
     def pick(d, tag):
         ks = [k for k in d if tag in k]
         if len(ks) != 1:
             raise SystemExit(f"expected one kernel named like {tag!r}, found {ks}")
         return ks[0]
+    return fetch, write, cal, pick
+
+
+GROUPED_COUNTERS = os.path.join(ROOT, "profiles", "decode_prefix_shared_sampling_grouped_counters.json")
+
+
+def ingest_grouped_counters(root, out_path=GROUPED_COUNTERS):
+    """The grouped decode's HBM bytes per call (its group kernel and its
+    merge), from FETCH_SIZE / WRITE_SIZE passes over a prefix-shared run
+    that includes bench's grouped leg, keyed by the kernel sources' hash."""
+    fetch, write, cal, pick = _counter_passes(root)
+    ff, wf = cal["fetch_factor"], cal["write_factor"]
+    gk = pick(fetch, "decode_group_kernel")
+    mk = pick(fetch, "decode_merge_few_kernel" if any("decode_merge_few_kernel" in k for k in fetch)
+              else "decode_merge_parts_kernel")
+    out = {"source_sha": source_sha(), "kernel": gk, "merge_kernel": mk, "calibration": cal,
+           "fetch_bytes_per_call": (fetch[gk] + fetch[mk]) * 1024 * ff,
+           "write_bytes_per_call": (write[gk] + write[mk]) * 1024 * wf,
+           "group_kernel_fetch_bytes": fetch[gk] * 1024 * ff, "group_kernel_write_bytes": write[gk] * 1024 * wf}
+    out["hbm_bytes_per_call"] = out["fetch_bytes_per_call"] + out["write_bytes_per_call"]
+    with open(out_path, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out, indent=1))
+    return out
+
+
+def ingest_counters(root, config=3, partition=-1, out_path=None, block_size=16, explicit_partition=False):
+    """Turn FETCH_SIZE / WRITE_SIZE passes (KiB per dispatch) into bytes per
+    decode call, each scaled by what the same counter reads for a plain copy of
+    known size, and store them keyed by the kernel sources' hash.  `partition`
+    names the decode kernels: -1 the balanced kernel + its merge, P > 0 the
+    unit kernel + the partition merge, 0 the unit kernel alone."""
+    fetch, write, calib, pick = _counter_passes(root)
+    ff, wf = calib["fetch_factor"], calib["write_factor"]
     if partition == -1:
         dk, mk = pick(fetch, "decode_balanced_kernel"), pick(fetch, "decode_merge_balanced_kernel")
     elif partition > 0:   # fixed partitions: the resident-grid kernel (the unit kernel above 4096 sequences)
@@ -150,8 +187,7 @@ def ingest_counters(root, config=3, partition=-1, out_path=None, block_size=16, 
     mrg_f, mrg_w = (fetch[mk] * 1024 * ff, write[mk] * 1024 * wf) if mk else (0.0, 0.0)
     out = {"config": config, "partition": partition, "block_size": block_size, "source_sha": source_sha(),
            "kernel": dk, "fetch_kib_per_dispatch": fetch[dk], "write_kib_per_dispatch": write[dk],
-           "calibration": {"copy_bytes": calib, "copy_kernel": copy_k, "fetch_kib": calf[copy_k],
-                           "write_kib": calw[copy_k], "fetch_factor": ff, "write_factor": wf},
+           "calibration": calib,
            "merge_kernel": None if mk is None else {
                "name": mk, "fetch_kib_per_dispatch": fetch[mk], "write_kib_per_dispatch": write[mk],
                "fetch_bytes": mrg_f, "write_bytes": mrg_w},
@@ -689,9 +725,18 @@ def grouped_decode_leg(b, d, stream, alg_unique: int, step_decode_ms: float, K: 
     torch.cuda.synchronize()
     same = bool(torch.equal(out.view(torch.int16), plain.view(torch.int16)))
     achieved = alg_unique / (ms * 1e-3) / 1e9
+    traffic = None   # HBM bytes per call from rocprofv3 passes, while the kernel sources are unchanged
+    try:
+        with open(GROUPED_COUNTERS) as f:
+            ctr = json.load(f)
+        if ctr.get("source_sha") == source_sha():
+            traffic = ctr["hbm_bytes_per_call"]
+    except (OSError, ValueError):
+        pass
     return {"ms": ms, "partition_size": partition_size, "groups": len(gsh), "max_group_size": max_group,
             "shared_tokens": max_shared, "achieved_gbps": achieved, "frac_of_hbm_peak": achieved / HBM_PEAK_GBPS,
             "speedup_vs_step_decode": step_decode_ms / ms, "bit_identical_to_partitions": same,
+            "traffic": traffic, "traffic_over_algorithmic": None if traffic is None else traffic / alg_unique,
             "what": "pa_decode_attention_grouped over the step's pools (prompt groups from the tables), "
                     "HIP graph of K calls; bytes as roofline.algorithmic_bytes_per_launch"}
 
@@ -792,6 +837,9 @@ def main():
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}): "
               "the decode path here is a single-GPU kernel; sharding across GPUs is not implemented", file=sys.stderr)
         sys.exit(2)
+    if args.ingest_grouped_counters:
+        ingest_grouped_counters(args.ingest_grouped_counters)
+        return
     if args.ingest_counters:
         part = args.partition if args.partition is not None else -1
         ingest_counters(args.ingest_counters, config=args.config, partition=part, block_size=args.block_size,

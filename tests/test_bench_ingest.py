@@ -83,6 +83,25 @@ def test_ingest_partition_modes_name_the_unit_kernels(tmp_path):
     assert out2["kernel"] == RES and out2["hbm_bytes_per_launch"] == pytest.approx(((50.0 + 6.0) * 2 + 3.0) * 1024)
 
 
+GROUP = ("void pa::decode_group_kernel<pa::MfmaPvCore<pa::BF16, 128, 16, 4, 1>, pa::MfmaPvCore<pa::BF16, 128, 16, 4, "
+         "4>, pa::BF16, 128, 4>(pa::DecodeArgs, pa::GroupArgs, int)")
+FEW = "void pa::decode_merge_few_kernel<pa::BF16, 128>(pa::DecodeArgs, int)"
+
+
+def test_ingest_grouped_counters_adds_the_group_kernel_and_its_merge(tmp_path):
+    gib_kib = (1 << 30) / 1024
+    # a run that also holds the step's balanced decode: only the grouped call counts
+    write_pass(tmp_path / "fetch", "FETCH_SIZE", [(DEC, 999.0), (GROUP, 400.0), (FEW, 8.0), (GROUP, 402.0)])
+    write_pass(tmp_path / "write", "WRITE_SIZE", [(DEC, 5.0), (GROUP, 17.0), (FEW, 4.0), (GROUP, 17.0)])
+    write_pass(tmp_path / "calf", "FETCH_SIZE", [(COPY, gib_kib / 2)])
+    write_pass(tmp_path / "calw", "WRITE_SIZE", [(COPY, gib_kib)])
+    out = bench.ingest_grouped_counters(str(tmp_path), out_path=str(tmp_path / "g.json"))
+    assert out["kernel"] == GROUP and out["merge_kernel"] == FEW
+    assert out["fetch_bytes_per_call"] == pytest.approx((401.0 + 8.0) * 2 * 1024)
+    assert out["hbm_bytes_per_call"] == pytest.approx(((401.0 + 8.0) * 2 + 17.0 + 4.0) * 1024)
+    assert out["source_sha"] == bench.source_sha()
+
+
 def test_counter_files_are_named_by_workload():
     assert bench.counters_file(3).endswith("profiles/decode_gqa_llama3_8b_counters.json")
     assert bench.counters_file(5, 8).endswith("profiles/decode_long_context_bs8_counters.json")
